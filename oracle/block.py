@@ -1,0 +1,225 @@
+"""One joint text + video + audio Flash DiT block, plain fp64 numpy.
+
+Sources:
+  * tokendh.com article, backbone section: one shared denoiser over text,
+    video and audio tokens; block width 5376, 56 heads of 128, feed-forward
+    width 14336; tokens carry 3D rotary positions.
+  * tokendh.com article, training section and PaperDaily review, section 2:
+    the compressed layers compute attention and the feed-forward update on the
+    kept video tokens (plus all text and audio tokens), and every video
+    position adds the update of its nearest kept position of the same frame to
+    its own full-resolution features.
+
+Readings of the points the pages leave open (each one a choice, listed with
+the reasons in the design notes):
+  * block form: pre-RMSNorm, no biases, no modulation, one weight set shared by
+    all modalities: h = X + Attn(RMSNorm(X) g1) Wo^T,
+    y = h + (silu(n2 Wg^T) * (n2 Wu^T)) Wd^T with n2 = RMSNorm(h) g2;
+  * RMSNorm: x / sqrt(mean(x^2) + eps) * g over the hidden axis;
+  * attention: softmax(q k^T / sqrt(head_dim)) v per head over the whole joint
+    sequence, no mask;
+  * rotary embedding: each head splits into bands (t, h, w) in that order;
+    inside a band of width d, pair (2i, 2i+1) turns by pos * base**(-2i/d)
+    as (a, b) -> (a cos - b sin, a sin + b cos); q and k rotate, v does not.
+    Video tokens use (t, h, w) (compressed tokens keep their original
+    coordinates), audio token j rotates only its t band by position j, text
+    does not rotate;
+  * "the update" of a kept token is y - X (attention plus feed-forward);
+  * sequence order [text | video (t, h, w raster) | audio].
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import compress as cmp
+from .fp8 import quantize_act_fp8
+
+KIND_TEXT, KIND_VIDEO, KIND_AUDIO = 0, 1, 2
+
+
+@dataclass
+class BlockWeights:
+    """fp64 weights, [out, in]. With lowbit=True the projection weights are
+    already the dequantised fp8 values (codes * scale) and every projection
+    input is quantised per tensor before the product."""
+    g1: np.ndarray
+    wqkv: np.ndarray
+    wo: np.ndarray
+    g2: np.ndarray
+    wgate: np.ndarray
+    wup: np.ndarray
+    wdown: np.ndarray
+    lowbit: bool = False
+
+    @classmethod
+    def from_arrays(cls, w: dict, lowbit: bool = False) -> "BlockWeights":
+        f = lambda a: np.asarray(a, dtype=np.float64)  # noqa: E731
+        return cls(f(w["g1"]), f(w["wqkv"]), f(w["wo"]), f(w["g2"]), f(w["wgate"]), f(w["wup"]),
+                   f(w["wdown"]), lowbit)
+
+
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * g
+
+
+def linear(a: np.ndarray, w: np.ndarray, lowbit: bool) -> np.ndarray:
+    """a @ w^T; with lowbit the input is first quantised to e4m3 with a
+    per-tensor dynamic scale (the weights are already dequantised fp8)."""
+    if lowbit:
+        a, s = quantize_act_fp8(a)
+        return (a @ w.T) * s
+    return a @ w.T
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu(n2: np.ndarray, wgate: np.ndarray, wup: np.ndarray, lowbit: bool = False) -> np.ndarray:
+    if lowbit:  # one quantised input feeds both projections
+        a, s = quantize_act_fp8(n2)
+        return silu((a @ wgate.T) * s) * ((a @ wup.T) * s)
+    return silu(n2 @ wgate.T) * (n2 @ wup.T)
+
+
+def token_coords(d, compressed: bool, stride: int = None):
+    """Per token of the joint sequence: coordinates [S, 3] and kind [S]."""
+    s = d.stride if stride is None else stride
+    text = np.zeros((d.n_text, 3), dtype=np.int64)
+    if compressed:
+        video = cmp.kept_coords(d.T, d.H, d.W, s)
+    else:
+        t, h, w = np.meshgrid(np.arange(d.T), np.arange(d.H), np.arange(d.W), indexing="ij")
+        video = np.stack([t.ravel(), h.ravel(), w.ravel()], axis=1).astype(np.int64)
+    audio = np.zeros((d.n_audio, 3), dtype=np.int64)
+    audio[:, 0] = np.arange(d.n_audio)
+    coords = np.concatenate([text, video, audio], axis=0)
+    kinds = np.concatenate([np.full(d.n_text, KIND_TEXT), np.full(len(video), KIND_VIDEO),
+                            np.full(d.n_audio, KIND_AUDIO)]).astype(np.int64)
+    return coords, kinds
+
+
+def rope_rotate(x: np.ndarray, coords: np.ndarray, kinds: np.ndarray, bands, base: float) -> np.ndarray:
+    """x [S, heads, head_dim] -> rotated copy (see the module docstring)."""
+    x = np.asarray(x, dtype=np.float64)
+    out = x.copy()
+    off = 0
+    for axis, width in enumerate(bands):
+        if width % 2:
+            raise ValueError("rotary band widths must be even")
+        theta = base ** (-np.arange(0, width, 2, dtype=np.float64) / width)      # [width/2]
+        applies = (kinds == KIND_VIDEO) | ((kinds == KIND_AUDIO) & (axis == 0))
+        ang = coords[:, axis:axis + 1].astype(np.float64) * theta[None, :]        # [S, width/2]
+        c = np.where(applies[:, None], np.cos(ang), 1.0)[:, None, :]
+        s = np.where(applies[:, None], np.sin(ang), 0.0)[:, None, :]
+        a = x[:, :, off:off + width:2]
+        b = x[:, :, off + 1:off + width:2]
+        out[:, :, off:off + width:2] = a * c - b * s
+        out[:, :, off + 1:off + width:2] = a * s + b * c
+        off += width
+    if off != x.shape[-1]:
+        raise ValueError("rotary bands must sum to head_dim")
+    return out
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, chunk: int = 1024) -> np.ndarray:
+    """q [Sq, heads, dh], k and v [Sk, heads, dh] -> [Sq, heads, dh]:
+    softmax(q k^T / sqrt(dh)) v per head, max-subtracted, unmasked."""
+    sq, nh, dh = q.shape
+    out = np.empty((sq, nh, v.shape[-1]), dtype=np.float64)
+    scale = 1.0 / np.sqrt(dh)
+    for h in range(nh):
+        kh = k[:, h, :]
+        vh = v[:, h, :]
+        for r0 in range(0, sq, chunk):
+            logits = (q[r0:r0 + chunk, h, :] @ kh.T) * scale
+            logits -= logits.max(axis=1, keepdims=True)
+            p = np.exp(logits)
+            p /= p.sum(axis=1, keepdims=True)
+            out[r0:r0 + chunk, h, :] = p @ vh
+    return out
+
+
+def block_core(X: np.ndarray, coords: np.ndarray, kinds: np.ndarray, w: BlockWeights, d,
+               rows: np.ndarray = None) -> np.ndarray:
+    """The block on an already assembled joint sequence X [S, D] -> y.
+    With `rows`, only those output rows are evaluated (keys and values still
+    come from every token); not available for the low-bit form, whose
+    per-tensor activation scales need every row."""
+    X = np.asarray(X, dtype=np.float64)
+    S, D = X.shape
+    nh, dh, I = d.n_heads, d.head_dim, d.n_heads * d.head_dim
+    if rows is not None and w.lowbit:
+        raise ValueError("row sampling needs the full tensor for low-bit scales")
+    n1 = rmsnorm(X, w.g1, d.eps)
+    if w.lowbit:
+        qkv = linear(n1, w.wqkv, True)
+        q, k, v = qkv[:, :I], qkv[:, I:2 * I], qkv[:, 2 * I:]
+    else:
+        n1q = n1 if rows is None else n1[rows]
+        q = n1q @ w.wqkv[:I].T
+        k = n1 @ w.wqkv[I:2 * I].T
+        v = n1 @ w.wqkv[2 * I:].T
+    qrows = np.arange(S) if rows is None or w.lowbit else np.asarray(rows)
+    q = rope_rotate(q.reshape(len(qrows), nh, dh), coords[qrows], kinds[qrows], d.rope, d.rope_base)
+    k = rope_rotate(k.reshape(S, nh, dh), coords, kinds, d.rope, d.rope_base)
+    o = attention(q, k, v.reshape(S, nh, dh)).reshape(len(qrows), I)
+    Xr = X[qrows]
+    h = Xr + linear(o, w.wo, w.lowbit)
+    n2 = rmsnorm(h, w.g2, d.eps)
+    u = swiglu(n2, w.wgate, w.wup, w.lowbit)
+    return h + linear(u, w.wdown, w.lowbit)
+
+
+def block_forward(x_text, x_video, x_audio, w: BlockWeights, d, compress: bool, stride: int = None,
+                  sample: dict = None):
+    """The full block on the three inputs (x_video [T, H, W, D]).
+
+    Returns (y_text [Nt, D], y_video [T, H, W, D], y_audio [Na, D]).
+    With compress=True the joint sequence holds only the kept video tokens;
+    text and audio outputs come from the block, and every video position gets
+    x + (update of its nearest kept slot).
+
+    sample = {"text": idx, "video": flat positions, "audio": idx} evaluates only
+    those outputs (returned flat, in the same three-tuple form)."""
+    s = d.stride if stride is None else stride
+    D = d.d_model
+    xt = np.asarray(x_text, dtype=np.float64).reshape(d.n_text, D)
+    xv = np.asarray(x_video, dtype=np.float64).reshape(d.n_video, D)
+    xa = np.asarray(x_audio, dtype=np.float64).reshape(d.n_audio, D)
+    coords, kinds = token_coords(d, compress, s)
+    if compress:
+        keep = cmp.keep_index(d.T, d.H, d.W, s)
+        nk = cmp.nearest_kept_map(d.T, d.H, d.W, s)
+        xv_seq = xv[keep]
+    else:
+        xv_seq = xv
+    nvs = len(xv_seq)
+    X = np.concatenate([xt, xv_seq, xa], axis=0)
+
+    if sample is None:
+        y = block_core(X, coords, kinds, w, d)
+        yt, yv_seq, ya = y[:d.n_text], y[d.n_text:d.n_text + nvs], y[d.n_text + nvs:]
+        if compress:
+            delta = yv_seq - xv_seq
+            yv = xv + delta[nk]
+        else:
+            yv = yv_seq
+        return yt, yv.reshape(d.T, d.H, d.W, D), ya
+
+    st = np.asarray(sample.get("text", []), dtype=np.int64)
+    sv = np.asarray(sample.get("video", []), dtype=np.int64)
+    sa = np.asarray(sample.get("audio", []), dtype=np.int64)
+    vslots = nk[sv] if compress else sv
+    rows = np.concatenate([st, d.n_text + vslots, d.n_text + nvs + sa]).astype(np.int64)
+    y = block_core(X, coords, kinds, w, d, rows=rows)
+    yt, yv_rows, ya = y[:len(st)], y[len(st):len(st) + len(sv)], y[len(st) + len(sv):]
+    if compress:
+        yv = xv[sv] + (yv_rows - xv_seq[vslots])
+    else:
+        yv = yv_rows
+    return yt, yv, ya

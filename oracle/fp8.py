@@ -1,0 +1,84 @@
+"""fp8 e4m3 encoding for the low-bit projections.
+
+Source: PaperDaily review, section 2 (Flash): suitable projections use low-bit
+weights and activations, with quantisation fused into the normalisation. The
+pages give no format or scale rule. Readings:
+  * format: OCP e4m3 "fn" (1 sign, 4 exponent bits with bias 7, 3 mantissa
+    bits, no infinities, largest finite 448, subnormal step 2**-9);
+  * rounding: to the nearest representable value, ties to the even code;
+    magnitudes above 448 saturate to 448;
+  * scales: one per tensor. Weights: static s_W = amax(W) / 448, codes of
+    W * (448 / amax(W)), both evaluated in IEEE fp32 (the precision the GPU
+    quantiser uses, so that both sides produce the same bytes). Activations:
+    dynamic s_A = amax(A) / 448 per GEMM input (amax 0 -> scale 1).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+
+
+def _positive_table() -> np.ndarray:
+    """Values of codes 0..126 (sign bit clear), ascending with the code."""
+    vals = []
+    for code in range(127):
+        e, m = code >> 3, code & 7
+        if e == 0:
+            vals.append(m / 8.0 * 2.0 ** -6)
+        else:
+            vals.append((1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return np.asarray(vals, dtype=np.float64)
+
+
+_POS = _positive_table()
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """uint8 codes -> float64 values (0x7F / 0xFF are NaN)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, _POS[np.minimum(c & 0x7F, 126)])
+    return np.where(c & 0x80, -mag, mag)
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """Finite float array -> uint8 e4m3fn codes: nearest value, ties to even
+    code, saturating at +-448, sign kept (so -0.0 and tiny negatives -> 0x80)."""
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("e4m3_encode expects finite input")
+    neg = np.signbit(x)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.searchsorted(_POS, a, side="left")          # first table value >= a
+    hi = np.minimum(hi, 126)
+    lo = np.maximum(hi - 1, 0)
+    dlo = a - _POS[lo]
+    dhi = _POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(_POS[hi] == a, hi, code)              # exact hit
+    return (code.astype(np.uint8) | np.where(neg, 0x80, 0).astype(np.uint8)).astype(np.uint8)
+
+
+def quantize_weight_fp8(w: np.ndarray):
+    """Per-tensor static weight quantisation in fp32: returns (codes uint8,
+    scale float32) with W ~= decode(codes) * scale."""
+    w32 = np.ascontiguousarray(w, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(w32))) if w32.size else np.float32(0)
+    if amax == 0:
+        inv, scale = np.float32(1), np.float32(1)
+    else:
+        inv = np.float32(E4M3_MAX) / amax
+        scale = amax / np.float32(E4M3_MAX)
+    q = (w32 * inv).astype(np.float32)
+    return e4m3_encode(q), np.float32(scale)
+
+
+def quantize_act_fp8(a: np.ndarray):
+    """Per-tensor dynamic activation quantisation in fp64: returns
+    (decoded e4m3 values, scale s) with a ~= values * s. This is what the
+    low-bit GEMM consumes: (values @ W_codes^T) * s * s_W."""
+    a = np.asarray(a, dtype=np.float64)
+    amax = float(np.max(np.abs(a))) if a.size else 0.0
+    s = amax / E4M3_MAX if amax > 0 else 1.0
+    return e4m3_decode(e4m3_encode(a / s)), s
