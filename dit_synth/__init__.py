@@ -10,14 +10,19 @@ Value recipe (the workload description of the five block configurations):
   * projection weights W[out, in]          ~ N(0, 1/fan_in)   (second argument
     read as the variance, so std = 1/sqrt(fan_in))
   * RMSNorm gains                          ~ 1 + N(0, 0.1)    (variance 0.1)
-Every tensor has its own stream: numpy PCG64 seeded by SeedSequence([seed,
-tensor_id]), so any tensor can be regenerated on its own.
+Every tensor has its own streams: the flattened tensor is cut into chunks of
+2**22 values and chunk c is drawn from numpy PCG64 seeded by
+SeedSequence([seed, tensor_id, c]), so any tensor (or chunk) can be
+regenerated on its own, and chunks are drawn in parallel threads.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
-from .configs import BlockDims, CONFIGS, get_config  # noqa: F401
+from .configs import BlockDims, CONFIGS, FLASH_EVALS, FLASH_LAYERS, SWEEP_FRAMES, get_config  # noqa: F401
 
 # tensor ids inside one seed
 TID_X_TEXT, TID_X_VIDEO, TID_X_AUDIO = 0, 1, 2
@@ -29,12 +34,25 @@ def rng(seed: int, tensor_id: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), int(tensor_id)])))
 
 
-def round_bf16(a: np.ndarray) -> np.ndarray:
-    """fp32 -> nearest bf16 value (ties to even), returned as fp32 (storage format)."""
-    a = np.ascontiguousarray(a, dtype=np.float32)
-    b = a.view(np.uint32).astype(np.uint64)
-    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
-    return b.astype(np.uint32).view(np.float32)
+CHUNK = 1 << 22
+_POOL = ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1))
+
+
+def round_bf16(a: np.ndarray, inplace: bool = False) -> np.ndarray:
+    """fp32 -> nearest bf16 value (ties to even), returned as fp32 (storage
+    format). Finite inputs only."""
+    a = np.array(a, dtype=np.float32, copy=not inplace, order="C")
+    u = a.reshape(-1).view(np.uint32)
+
+    def work(lo):
+        b = u[lo:lo + CHUNK]
+        lsb = (b >> 16) & 1
+        b += np.uint32(0x7FFF)
+        b += lsb
+        b &= np.uint32(0xFFFF0000)
+
+    list(_POOL.map(work, range(0, u.size, CHUNK)))
+    return a
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -44,17 +62,24 @@ def bf16_bits(a: np.ndarray) -> np.ndarray:
 
 
 def _normal(seed, tid, shape, std=1.0, mean=0.0):
-    g = rng(seed, tid)
-    x = g.standard_normal(size=shape, dtype=np.float32)
-    if std != 1.0:
-        x *= np.float32(std)
-    if mean != 0.0:
-        x += np.float32(mean)
-    return x
+    n = int(np.prod(shape))
+    x = np.empty(n, dtype=np.float32)
+
+    def work(c):
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), int(tid), c])))
+        part = x[c * CHUNK:(c + 1) * CHUNK]
+        g.standard_normal(out=part, dtype=np.float32)
+        if std != 1.0:
+            part *= np.float32(std)
+        if mean != 0.0:
+            part += np.float32(mean)
+
+    list(_POOL.map(work, range((n + CHUNK - 1) // CHUNK)))
+    return x.reshape(shape)
 
 
 def _fmt(x, dtype):
-    return round_bf16(x) if dtype in ("bf16", "fp8") else x.astype(np.float32)
+    return round_bf16(x, inplace=True) if dtype in ("bf16", "fp8") else x
 
 
 def activations(d: BlockDims, seed: int, dtype: str = None) -> dict:

@@ -1,0 +1,206 @@
+/*
+ * vdtflash.h - C ABI of the MI355X (gfx950) Flash DiT block library.
+ *
+ * One joint text + video + audio diffusion-transformer block of the Flash
+ * model, with spatial token compression and its full-resolution residual,
+ * and the few-step flow-matching sampler over a stack of such blocks.
+ *
+ * Sources (the pages this follows):
+ *   [TDH-backbone] tokendh.com article on LynnReal-Omni, backbone section:
+ *       one shared denoiser over text, video and audio tokens; width 5376,
+ *       56 heads of 128, feed-forward width 14336; 3D rotary positions.
+ *   [TDH-training] same article, training section: flow matching, separate
+ *       video and audio noise clocks, Flash keeps 42 layers (2 full, 26 with
+ *       2x spatial token subsampling that keeps boundary rows and columns,
+ *       14 full) and 3 evaluations; dropped tokens take the update of the
+ *       nearest kept token of the same frame.
+ *   [PD-2] PaperDaily review (longzhangge.com), section 2 (Flash): per-frame
+ *       subsampling of rows and columns keeping about a quarter of the
+ *       positions plus the edge rows and columns, no temporal subsampling,
+ *       text and audio never compressed; compressed layers compute updates
+ *       for the kept positions and every missing position adds the update of
+ *       the nearest kept position of its frame to the full features; low-bit
+ *       projections with fused norm, quantisation, rotary embedding and
+ *       residual update.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless the name ends in _host. The caller
+ *     owns every buffer; the library allocates nothing, keeps no pointer
+ *     after returning and never synchronises the stream. `stream` is a
+ *     hipStream_t (NULL = the default stream).
+ *   - Row-major layouts. Token activations are [rows][d_model]; x_video is
+ *     [T][H][W][d_model] (raster order of t, h, w). Weights are [out][in].
+ *   - Every argument is validated on the host before any launch; on error
+ *     nothing is enqueued and a negative dit_status is returned.
+ *   - Device pointers must be 16-byte aligned.
+ *   - Outputs may alias the corresponding inputs (y_video == x_video etc.).
+ *   - Calls are stateless; two calls may run concurrently on different
+ *     streams only if each has its own workspace.
+ */
+#ifndef VDTFLASH_H
+#define VDTFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DIT_OK = 0,
+    DIT_EINVAL = -1,        /* bad pointer, size or dimension */
+    DIT_EUNSUPPORTED = -2,  /* valid but not implemented (dtype combination, head_dim, ...) */
+    DIT_EWORKSPACE = -3,    /* workspace smaller than the *_workspace_size query */
+    DIT_EHIP = -4           /* a HIP launch failed; see dit_last_hip_error() */
+} dit_status;
+
+typedef enum {
+    DIT_F32 = 0,            /* IEEE binary32 */
+    DIT_BF16 = 1,           /* bfloat16 */
+    DIT_FP8_E4M3 = 2        /* OCP e4m3 (finite max 448), weights only, per-tensor fp32 scale */
+} dit_dtype;
+
+/* Block and grid sizes. Supported combinations (act_dtype, w_dtype):
+ * (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
+ * Constraints: d_model % 64 == 0; d_ffn % 64 == 0; head_dim in {64, 128};
+ * rope_t + rope_h + rope_w == head_dim, each even; T, H, W >= 1;
+ * n_text, n_audio >= 0; stride >= 1. The bf16 / fp8 paths also need
+ * d_model, n_heads * head_dim and d_ffn multiples of 128. */
+typedef struct {
+    int32_t T, H, W;              /* latent video grid */
+    int32_t n_text, n_audio;      /* text / audio tokens (never compressed) */
+    int32_t d_model;              /* hidden width D */
+    int32_t n_heads, head_dim;    /* attention inner width I = n_heads * head_dim */
+    int32_t d_ffn;                /* SwiGLU width F */
+    int32_t rope_t, rope_h, rope_w; /* rotary band widths inside a head, in this order */
+    float rope_base;              /* rotary base (10000) */
+    float eps;                    /* RMSNorm epsilon (1e-6) */
+    int32_t stride;               /* compression stride (2 in the Flash layers; 1 keeps every token) */
+    int32_t act_dtype;            /* dit_dtype of activations and gains */
+    int32_t w_dtype;              /* dit_dtype of the projection weights */
+} dit_dims;
+
+/* One block's parameters (device pointers). Gains g1, g2 [D] have act_dtype;
+ * wqkv [3I][D] (rows: q, then k, then v), wo [D][I], wgate [F][D], wup [F][D],
+ * wdown [D][F] have w_dtype. For FP8_E4M3 weights each s_* points to the
+ * tensor's fp32 dequantisation scale on the device (W ~= code * scale, as
+ * written by dit_quantize_fp8); otherwise the s_* are ignored. */
+typedef struct {
+    const void *g1, *wqkv, *wo, *g2, *wgate, *wup, *wdown;
+    const float *s_wqkv, *s_wo, *s_wgate, *s_wup, *s_wdown;
+} dit_block_weights;
+
+/* Kept rows and columns of one frame for a compression stride [PD-2],
+ * [TDH-training]: K(n) = {r : r mod stride == 0} U {n - 1}, so
+ * |K(n)| = ceil(n / stride) + ((n - 1) mod stride != 0). Host only.
+ * Returns DIT_OK and writes *Hk, *Wk, or DIT_EINVAL for H, W, stride < 1. */
+int32_t dit_keep_dims(int32_t H, int32_t W, int32_t stride, int32_t* Hk, int32_t* Wk);
+
+/* keep[j] = flat video position t*H*W + h*W + w of kept slot j, for the kept
+ * set K(H) x K(W) of every frame in raster order of (t, h, w) [PD-2].
+ * keep: int32 [T * Hk * Wk], device. Time is never subsampled. */
+int32_t dit_keep_index(int32_t T, int32_t H, int32_t W, int32_t stride, int32_t* keep, void* stream);
+
+/* nk[p] = kept slot (index into keep) of (t, near_H(h), near_W(w)) for every
+ * video position p = (t, h, w), where near_n(r) is the kept index nearest to r,
+ * ties to the lower index [TDH-training], [PD-2]. nk: int32 [T * H * W], device. */
+int32_t dit_nearest_kept_map(int32_t T, int32_t H, int32_t W, int32_t stride, int32_t* nk, void* stream);
+
+/* Workspace bytes for dit_block_forward with these dims (compress_on 0 / 1). */
+int32_t dit_block_workspace_size(const dit_dims* dims, int32_t compress_on, size_t* bytes);
+
+/* One Flash DiT block [TDH-backbone], [TDH-training], [PD-2].
+ * Joint sequence X = [x_text | video tokens | x_audio]; with compress_on the
+ * video tokens are x_video[keep[j]] (original coordinates kept for the rotary
+ * embedding), otherwise all of x_video in raster order.
+ *   n1 = RMSNorm(X) g1; q, k, v = n1 Wqkv^T; rotary embedding on q, k
+ *   (video: bands t, h, w; audio: t band at its index; text: none);
+ *   o = softmax(q k^T / sqrt(head_dim)) v per head over the whole sequence;
+ *   h = X + o Wo^T; y = h + (silu(n2 Wg^T) * (n2 Wu^T)) Wd^T, n2 = RMSNorm(h) g2.
+ * Outputs: y_text, y_audio = the text and audio rows of y. Uncompressed:
+ * y_video = video rows of y. Compressed: y_video[p] = x_video[p] + (y - X)
+ * at slot nk[p], for all T*H*W positions.
+ * x_text [n_text][D], x_video [T][H][W][D], x_audio [n_audio][D] and the
+ * outputs have act_dtype; keep and nk (from the two calls above, same stride)
+ * are required iff compress_on. ws: device workspace of at least the queried
+ * size, 256-byte aligned. With FP8 weights, each projection input is
+ * quantised to e4m3 with a per-tensor dynamic scale amax / 448 before the
+ * product; attention and the residual stream stay bf16 / fp32. */
+int32_t dit_block_forward(const dit_dims* dims,
+                          const void* x_text, const void* x_video, const void* x_audio,
+                          const dit_block_weights* weights, int32_t compress_on,
+                          const int32_t* keep, const int32_t* nk,
+                          void* y_text, void* y_video, void* y_audio,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for dit_stack_sample with these dims and layer flags. */
+int32_t dit_stack_workspace_size(const dit_dims* dims, const uint8_t* compressed_host, int32_t n_layers,
+                                 size_t* bytes);
+
+/* Few-step flow-matching sampler over n_layers blocks [TDH-training], [PD-2].
+ * For k = 0 .. n_evals-1: run the layers on [x_text | x_video | x_audio]
+ * (layer l compressed iff compressed_host[l]; text re-fed unchanged each
+ * evaluation), take the video and audio outputs as the velocity v and update
+ *   x_video += (t_video[k+1] - t_video[k]) v_video,
+ *   x_audio += (t_audio[k+1] - t_audio[k]) v_audio   (t_audio NULL: t_video).
+ * x_video and x_audio are updated in place. A run of consecutive compressed
+ * layers gathers the kept tokens once and broadcasts the summed update once,
+ * which equals per-layer broadcasting (kept positions are their own nearest).
+ * layers_host: host array of n_layers weight sets (device pointers inside).
+ * t_video_host / t_audio_host: host arrays of n_evals + 1 clean times. */
+int32_t dit_stack_sample(const dit_dims* dims, const dit_block_weights* layers_host, int32_t n_layers,
+                         const uint8_t* compressed_host, int32_t n_evals,
+                         const float* t_video_host, const float* t_audio_host,
+                         const void* x_text, void* x_video, void* x_audio,
+                         const int32_t* keep, const int32_t* nk,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Per-tensor e4m3 quantisation of a weight tensor [PD-2] (low-bit
+ * projections): amax = max |src|, dst = e4m3(saturate(src * (448 / amax))) with
+ * round-to-nearest-even, *scale = amax / 448 (fp32, device); amax 0 gives
+ * scale 1 and zero codes. src has src_dtype (F32 or BF16), n elements; dst
+ * uint8 [n]. Runs on the stream; *scale is valid when the stream reaches it. */
+int32_t dit_quantize_fp8(const void* src, int32_t src_dtype, int64_t n, uint8_t* dst, float* scale, void* stream);
+
+/* Row gather of the kept video tokens [PD-2]: out[j] = x_video[keep[j]],
+ * rows of D elements of dtype (F32 or BF16). Coalesced, bandwidth bound. */
+int32_t dit_gather_kept(int32_t n_kept, int32_t D, int32_t dtype, const void* x_video, const int32_t* keep,
+                        void* out, void* stream);
+
+/* Nearest-kept update broadcast with the full-resolution residual [PD-2],
+ * [TDH-training]: out[p] = x_video[p] + delta[nk[p]] for p < n_video, rows of
+ * D elements; x_video / out have dtype (F32 or BF16), delta is fp32
+ * [n_kept][D]. out may alias x_video. Bandwidth bound. */
+int32_t dit_broadcast_residual(int32_t n_video, int32_t n_kept, int32_t D, int32_t dtype, const void* x_video,
+                               const float* delta, const int32_t* nk, void* out, void* stream);
+
+/* Multi-head attention over a joint sequence, the block's attention step on
+ * its own [TDH-backbone]: o = softmax(q k^T * scale) v per head, unmasked.
+ * q, k, v, o are [S][n_heads * head_dim] of dtype (F32 or BF16); no rotary
+ * embedding is applied here. ws: workspace of dit_attention_workspace_size. */
+int32_t dit_attention_workspace_size(int32_t S, int32_t n_heads, int32_t head_dim, int32_t dtype, size_t* bytes);
+int32_t dit_attention(int32_t S, int32_t n_heads, int32_t head_dim, int32_t dtype, float scale,
+                      const void* q, const void* k, const void* v, void* o, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/* Profiling trace (process-global, not thread-safe). With capacity > 0 the
+ * library records a hipEvent on the call's stream before each kernel group of
+ * every later call (names: rope_tables, rmsnorm1, gemm_qkv, attention,
+ * gemm_o, rmsnorm2, gemm_gate_up, gemm_down, broadcast_residual, euler,
+ * quant_o, quant_u) and one named "end" after each call's last launch, up to
+ * `capacity` records; capacity 0 turns tracing off. dit_trace_read(i) waits
+ * for record i + 1 and returns the name of record i and the milliseconds from
+ * record i to record i + 1. */
+int32_t dit_trace_enable(int32_t capacity);
+int32_t dit_trace_count(void);
+int32_t dit_trace_read(int32_t index, const char** name, float* ms);
+
+const char* dit_status_str(int32_t status);
+/* HIP error code of the last failed launch in this process (0 if none). */
+int32_t dit_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VDTFLASH_H */

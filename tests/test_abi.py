@@ -1,0 +1,112 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol declared in
+include/vdtflash.h, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vdtflash.h")
+
+V = pytest.importorskip("video_diffusion_transformer_flash_amd")
+from video_diffusion_transformer_flash_amd import _lib  # noqa: E402
+from dit_synth import CONFIGS  # noqa: E402
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dit_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = V.lib()
+    names = declared_symbols()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, n
+
+
+def test_keep_dims_matches_oracle():
+    for s in (1, 2, 3, 4):
+        for H in range(1, 40):
+            for W in (1, 2, 7, 60):
+                assert V.keep_dims(H, W, s) == O.keep_dims(H, W, s)
+
+
+def _dims(**kw):
+    d = V.make_dims(CONFIGS["540p_on"])
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(head_dim=96), _lib.DIT_EUNSUPPORTED),
+    (dict(rope_t=30), _lib.DIT_EINVAL),
+    (dict(rope_t=31, rope_h=49), _lib.DIT_EINVAL),
+    (dict(d_model=5377), _lib.DIT_EINVAL),
+    (dict(T=0), _lib.DIT_EINVAL),
+    (dict(stride=0), _lib.DIT_EINVAL),
+    (dict(act_dtype=_lib.DIT_F32), _lib.DIT_EUNSUPPORTED),       # f32 activations with bf16 weights
+    (dict(w_dtype=7), _lib.DIT_EUNSUPPORTED),
+    (dict(d_model=5376 + 64), _lib.DIT_EUNSUPPORTED),          # bf16 path wants multiples of 128
+])
+def test_dims_rejected(bad, code):
+    n = ctypes.c_size_t()
+    assert V.lib().dit_block_workspace_size(ctypes.byref(_dims(**bad)), 1, ctypes.byref(n)) == code
+
+
+def test_block_forward_rejects_before_launch():
+    lib = V.lib()
+    d = _dims()
+    w = _lib.BlockWeights()
+    # null weights / inputs: EINVAL, nothing launched (no GPU needed)
+    st = lib.dit_block_forward(ctypes.byref(d), None, None, None, ctypes.byref(w), 1, None, None, None, None, None,
+                               None, 0, None)
+    assert st == _lib.DIT_EINVAL
+    fake = ctypes.c_void_p(1 << 20)
+    ws = ctypes.c_void_p(1 << 24)
+    wf = _lib.BlockWeights(*([fake] * 7))
+    # compressed without keep / nk
+    st = lib.dit_block_forward(ctypes.byref(d), fake, fake, fake, ctypes.byref(wf), 1, None, None, fake, fake, fake,
+                               ws, 1 << 40, None)
+    assert st == _lib.DIT_EINVAL
+    # workspace too small
+    st = lib.dit_block_forward(ctypes.byref(d), fake, fake, fake, ctypes.byref(wf), 1, fake, fake, fake, fake, fake,
+                               ws, 1024, None)
+    assert st == _lib.DIT_EWORKSPACE
+    # misaligned input pointer
+    st = lib.dit_block_forward(ctypes.byref(d), ctypes.c_void_p((1 << 20) + 8), fake, fake, ctypes.byref(wf), 0,
+                               None, None, fake, fake, fake, ws, 1 << 40, None)
+    assert st == _lib.DIT_EINVAL
+
+
+def test_other_entry_points_reject():
+    lib = V.lib()
+    assert lib.dit_keep_index(0, 4, 4, 2, ctypes.c_void_p(1 << 20), None) == _lib.DIT_EINVAL
+    assert lib.dit_nearest_kept_map(1, 4, 4, 0, ctypes.c_void_p(1 << 20), None) == _lib.DIT_EINVAL
+    assert lib.dit_keep_index(1, 4, 4, 2, None, None) == _lib.DIT_EINVAL
+    assert lib.dit_quantize_fp8(None, 0, 16, None, None, None) == _lib.DIT_EINVAL
+    assert lib.dit_quantize_fp8(ctypes.c_void_p(1 << 20), 2, 16, ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 20),
+                                None) == _lib.DIT_EUNSUPPORTED
+    assert lib.dit_broadcast_residual(4, 0, 64, 1, ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 20),
+                                      ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 20), None) == _lib.DIT_EINVAL
+    n = ctypes.c_size_t()
+    assert lib.dit_attention_workspace_size(10, 2, 96, 1, ctypes.byref(n)) == _lib.DIT_EUNSUPPORTED
+    d = _dims()
+    assert lib.dit_stack_sample(ctypes.byref(d), None, 3, None, 1, None, None, None, None, None, None, None, None, 0,
+                                None) == _lib.DIT_EINVAL
+    assert lib.dit_status_str(_lib.DIT_EWORKSPACE) == b"workspace too small"
+
+
+def test_workspace_grows_with_sequence():
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    d = _dims()
+    V.lib().dit_block_workspace_size(ctypes.byref(d), 1, ctypes.byref(a))
+    V.lib().dit_block_workspace_size(ctypes.byref(d), 0, ctypes.byref(b))
+    assert 0 < a.value < b.value

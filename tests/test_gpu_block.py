@@ -1,0 +1,129 @@
+"""GPU parity of dit_block_forward against the fp64 oracle.
+
+Metric: max |gpu - oracle| over every output element / RMS of the oracle
+outputs. Bars: 1e-4 for the fp32 block, 2e-2 for bf16, 6e-2 for fp8
+projections. Small configurations compare every element; the full
+540p / 768p configurations compare sampled rows that the oracle evaluates one
+by one (keys and values still come from the whole sequence)."""
+import numpy as np
+import pytest
+
+import oracle as O
+from dit_synth import CONFIGS, BlockDims
+from helpers import gpu_weights, inputs, oracle_weights, rel_err, to_numpy, torch_act
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+V = pytest.importorskip("video_diffusion_transformer_flash_amd")
+
+TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 6e-2}
+
+# small bf16 / fp8 blocks: several GEMM and attention tiles and a ragged tail
+SMALL_BF16 = BlockDims("small_bf16", d_model=512, n_heads=4, head_dim=128, d_ffn=1024, T=2, H=9, W=15, n_text=16,
+                       n_audio=8, rope=(32, 48, 48), dtype="bf16", seed=5)
+SMALL_FP8 = SMALL_BF16.with_(name="small_fp8", dtype="fp8", seed=6)
+
+
+def run_gpu(d, x, w, compress, stride=None):
+    dims = V.make_dims(d, stride)
+    s = d.stride if stride is None else stride
+    xt, xv, xa = (torch_act(x[k], d.dtype) for k in ("x_text", "x_video", "x_audio"))
+    gw, codes = gpu_weights(w, d.dtype)
+    keep = V.keep_index(d.T, d.H, d.W, s) if compress else None
+    nk = V.nearest_kept_map(d.T, d.H, d.W, s) if compress else None
+    yt, yv, ya = V.block_forward(dims, xt, xv, xa, gw, compress, keep, nk)
+    torch.cuda.synchronize()
+    return [to_numpy(yt), to_numpy(yv), to_numpy(ya)], codes
+
+
+def check_full(d, compress, stride=None):
+    print(f"block {d.name} compress={compress} stride={stride}", flush=True)
+    x, w = inputs(d)
+    got, codes = run_gpu(d, x, w, compress, stride)
+    if codes:
+        for k, (c, s) in codes.items():
+            rc, rs = O.quantize_weight_fp8(w[k])
+            assert np.array_equal(c.cpu().numpy().reshape(-1), rc.reshape(-1)) and np.float32(s.item()) == rs
+    ow = oracle_weights(w, d.dtype)
+    ref = O.block_forward(x["x_text"], x["x_video"], x["x_audio"], ow, d, compress, stride)
+    err = rel_err(got, ref)
+    print(f"  max|err|/rms = {err:.3e} (bar {TOL[d.dtype]})")
+    assert np.all(np.isfinite(np.concatenate([g.ravel() for g in got])))
+    assert err <= TOL[d.dtype]
+    return got, ref
+
+
+@pytest.mark.parametrize("compress", [False, True])
+def test_tiny_fp32(compress):
+    check_full(CONFIGS["tiny"], compress)
+
+
+@pytest.mark.parametrize("compress", [False, True])
+def test_small_bf16(compress):
+    check_full(SMALL_BF16, compress)
+
+
+@pytest.mark.parametrize("compress", [False, True])
+def test_small_fp8(compress):
+    check_full(SMALL_FP8, compress)
+
+
+@pytest.mark.parametrize("name", ["tiny", "small_bf16"])
+def test_stride1_equals_uncompressed(name):
+    d = CONFIGS["tiny"] if name == "tiny" else SMALL_BF16
+    x, w = inputs(d)
+    a, _ = run_gpu(d, x, w, False)
+    b, _ = run_gpu(d, x, w, True, stride=1)
+    # kept rows are every row; the output is x + (y - x) instead of y
+    assert rel_err(b, a) <= (1e-6 if d.dtype == "f32" else 1e-2)
+
+
+def test_degenerate_grids_bf16():
+    for T, H, W, nt, na in [(1, 1, 1, 0, 0), (1, 2, 2, 3, 0), (2, 3, 1, 0, 5), (1, 2, 97, 1, 1)]:
+        d = SMALL_BF16.with_(name=f"deg{T}x{H}x{W}", T=T, H=H, W=W, n_text=nt, n_audio=na)
+        for compress in (False, True):
+            check_full(d, compress)
+
+
+def test_deterministic_and_in_place():
+    d = SMALL_BF16
+    x, w = inputs(d)
+    a, _ = run_gpu(d, x, w, True)
+    b, _ = run_gpu(d, x, w, True)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+    # in place: outputs alias the inputs
+    dims = V.make_dims(d)
+    xt, xv, xa = (torch_act(x[k], d.dtype) for k in ("x_text", "x_video", "x_audio"))
+    gw, _ = gpu_weights(w, d.dtype)
+    V.block_forward(dims, xt, xv, xa, gw, True, V.keep_index(d.T, d.H, d.W), V.nearest_kept_map(d.T, d.H, d.W),
+                    out=(xt, xv, xa))
+    for u, v in zip(a, (to_numpy(xt), to_numpy(xv), to_numpy(xa))):
+        assert np.array_equal(u, v)
+
+
+def sampled(d, compress, n_video=96, seed=0):
+    g = np.random.default_rng(seed)
+    sv = np.unique(np.concatenate([g.integers(0, d.n_video, n_video), [0, d.n_video - 1, d.W - 1]]))
+    st = np.unique(np.concatenate([g.integers(0, d.n_text, 8), [d.n_text - 1]]))
+    sa = np.unique(np.concatenate([g.integers(0, d.n_audio, 8), [d.n_audio - 1]]))
+    return {"text": st, "video": sv, "audio": sa}
+
+
+@pytest.mark.parametrize("name,compress", [("540p_on", True), ("540p_off", False), ("768p", True)])
+def test_full_size_sampled(name, compress):
+    d = CONFIGS[name]
+    print(f"block {name} compress={compress} (sampled rows)", flush=True)
+    x, w = inputs(d)
+    got, _ = run_gpu(d, x, w, compress)
+    smp = sampled(d, compress)
+    ow = oracle_weights(w, d.dtype)
+    ref = O.block_forward(x["x_text"], x["x_video"], x["x_audio"], ow, d, compress, sample=smp)
+    D = d.d_model
+    gs = [got[0][smp["text"]], got[1].reshape(-1, D)[smp["video"]], got[2][smp["audio"]]]
+    err = rel_err(gs, ref)
+    print(f"  max|err|/rms = {err:.3e} over {sum(len(v) for v in smp.values())} rows")
+    assert err <= TOL[d.dtype]
+    # every output finite
+    assert all(np.all(np.isfinite(a)) for a in got)

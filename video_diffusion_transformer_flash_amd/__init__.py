@@ -1,0 +1,188 @@
+"""MI355X (gfx950) Flash DiT block: thin Python binding of libvdtflash.so.
+
+Every call marshals torch tensors (device memory) and the current HIP stream
+into the C ABI of include/vdtflash.h; all arithmetic runs in the library's
+HIP kernels. Outputs and workspaces are allocated with torch (plumbing).
+The binding refuses to run without the built library.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import DIT_BF16, DIT_F32, DIT_FP8_E4M3, BlockWeights, Dims, DitError, check  # noqa: F401
+
+__all__ = ["Dims", "make_dims", "keep_dims", "keep_index", "nearest_kept_map", "block_workspace_size",
+           "block_forward", "stack_workspace_size", "stack_sample", "quantize_fp8", "gather_kept",
+           "broadcast_residual", "attention", "trace_enable", "trace_records", "DitError"]
+
+_ACT = {"f32": DIT_F32, "bf16": DIT_BF16, "fp8": DIT_BF16}
+_WT = {"f32": DIT_F32, "bf16": DIT_BF16, "fp8": DIT_FP8_E4M3}
+_TORCH = {DIT_F32: torch.float32, DIT_BF16: torch.bfloat16}
+
+
+def lib():
+    return _lib.load()
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def make_dims(cfg, stride: int = None) -> Dims:
+    """Dims from a dit_synth.BlockDims-like object."""
+    return Dims(T=cfg.T, H=cfg.H, W=cfg.W, n_text=cfg.n_text, n_audio=cfg.n_audio, d_model=cfg.d_model,
+                n_heads=cfg.n_heads, head_dim=cfg.head_dim, d_ffn=cfg.d_ffn, rope_t=cfg.rope[0], rope_h=cfg.rope[1],
+                rope_w=cfg.rope[2], rope_base=cfg.rope_base, eps=cfg.eps,
+                stride=cfg.stride if stride is None else stride, act_dtype=_ACT[cfg.dtype], w_dtype=_WT[cfg.dtype])
+
+
+def keep_dims(H: int, W: int, stride: int = 2):
+    hk, wk = ctypes.c_int32(), ctypes.c_int32()
+    check(lib().dit_keep_dims(H, W, stride, ctypes.byref(hk), ctypes.byref(wk)), "dit_keep_dims")
+    return hk.value, wk.value
+
+
+def keep_index(T: int, H: int, W: int, stride: int = 2, out=None):
+    hk, wk = keep_dims(H, W, stride)
+    if out is None:
+        out = torch.empty(T * hk * wk, dtype=torch.int32, device="cuda")
+    check(lib().dit_keep_index(T, H, W, stride, _ptr(out), _stream()), "dit_keep_index")
+    return out
+
+
+def nearest_kept_map(T: int, H: int, W: int, stride: int = 2, out=None):
+    if out is None:
+        out = torch.empty(T * H * W, dtype=torch.int32, device="cuda")
+    check(lib().dit_nearest_kept_map(T, H, W, stride, _ptr(out), _stream()), "dit_nearest_kept_map")
+    return out
+
+
+def block_workspace_size(dims: Dims, compress: bool) -> int:
+    n = ctypes.c_size_t()
+    check(lib().dit_block_workspace_size(ctypes.byref(dims), int(compress), ctypes.byref(n)),
+          "dit_block_workspace_size")
+    return n.value
+
+
+def _weights_struct(w: dict) -> BlockWeights:
+    g = lambda k: _ptr(w.get(k))  # noqa: E731
+    return BlockWeights(g("g1"), g("wqkv"), g("wo"), g("g2"), g("wgate"), g("wup"), g("wdown"), g("s_wqkv"),
+                        g("s_wo"), g("s_wgate"), g("s_wup"), g("s_wdown"))
+
+
+def workspace(nbytes: int):
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+
+
+def block_forward(dims: Dims, x_text, x_video, x_audio, weights: dict, compress: bool, keep=None, nk=None,
+                  out=None, ws=None):
+    """One block; returns (y_text, y_video, y_audio). `out` may be the inputs
+    themselves (in place)."""
+    if out is None:
+        out = (torch.empty_like(x_text), torch.empty_like(x_video), torch.empty_like(x_audio))
+    need = block_workspace_size(dims, compress)
+    if ws is None:
+        ws = workspace(need)
+    w = _weights_struct(weights)
+    st = lib().dit_block_forward(ctypes.byref(dims), _ptr(x_text), _ptr(x_video), _ptr(x_audio), ctypes.byref(w),
+                                 int(compress), _ptr(keep), _ptr(nk), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]),
+                                 _ptr(ws), ws.numel(), _stream())
+    check(st, "dit_block_forward")
+    return out
+
+
+def stack_workspace_size(dims: Dims, flags) -> int:
+    fl = (ctypes.c_uint8 * len(flags))(*[int(f) for f in flags])
+    n = ctypes.c_size_t()
+    check(lib().dit_stack_workspace_size(ctypes.byref(dims), ctypes.cast(fl, ctypes.c_void_p), len(flags),
+                                         ctypes.byref(n)), "dit_stack_workspace_size")
+    return n.value
+
+
+def stack_sample(dims: Dims, layers: list, flags, t_video, t_audio, x_text, x_video, x_audio, keep=None, nk=None,
+                 ws=None):
+    """Flow-matching sampler; x_video and x_audio are updated in place."""
+    n = len(layers)
+    arr = (BlockWeights * max(n, 1))(*[_weights_struct(w) for w in layers])
+    fl = (ctypes.c_uint8 * max(n, 1))(*[int(f) for f in flags])
+    tv = (ctypes.c_float * len(t_video))(*[float(t) for t in t_video])
+    ta = None if t_audio is None else (ctypes.c_float * len(t_audio))(*[float(t) for t in t_audio])
+    if ws is None:
+        ws = workspace(stack_workspace_size(dims, flags))
+    st = lib().dit_stack_sample(ctypes.byref(dims), arr, n, ctypes.cast(fl, ctypes.c_void_p), len(t_video) - 1,
+                                ctypes.cast(tv, ctypes.c_void_p),
+                                None if ta is None else ctypes.cast(ta, ctypes.c_void_p), _ptr(x_text),
+                                _ptr(x_video), _ptr(x_audio), _ptr(keep), _ptr(nk), _ptr(ws), ws.numel(), _stream())
+    check(st, "dit_stack_sample")
+    return x_video, x_audio
+
+
+def quantize_fp8(src, codes=None, scale=None):
+    """Per-tensor e4m3 quantisation; returns (uint8 codes, fp32 scale [1])."""
+    dt = {torch.float32: DIT_F32, torch.bfloat16: DIT_BF16}[src.dtype]
+    if codes is None:
+        codes = torch.empty(src.shape, dtype=torch.uint8, device=src.device)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=src.device)
+    check(lib().dit_quantize_fp8(_ptr(src), dt, src.numel(), _ptr(codes), _ptr(scale), _stream()), "dit_quantize_fp8")
+    return codes, scale
+
+
+def gather_kept(x_video, keep, out=None):
+    D = x_video.shape[-1]
+    dt = {torch.float32: DIT_F32, torch.bfloat16: DIT_BF16}[x_video.dtype]
+    if out is None:
+        out = torch.empty((keep.numel(), D), dtype=x_video.dtype, device=x_video.device)
+    check(lib().dit_gather_kept(keep.numel(), D, dt, _ptr(x_video), _ptr(keep), _ptr(out), _stream()),
+          "dit_gather_kept")
+    return out
+
+
+def broadcast_residual(x_video, delta, nk, out=None):
+    D = x_video.shape[-1]
+    dt = {torch.float32: DIT_F32, torch.bfloat16: DIT_BF16}[x_video.dtype]
+    if out is None:
+        out = torch.empty_like(x_video)
+    check(lib().dit_broadcast_residual(nk.numel(), delta.shape[0], D, dt, _ptr(x_video), _ptr(delta), _ptr(nk),
+                                       _ptr(out), _stream()), "dit_broadcast_residual")
+    return out
+
+
+def attention(q, k, v, n_heads: int, scale: float, out=None, ws=None):
+    """q, k, v [S, n_heads * head_dim] -> softmax(q k^T * scale) v per head."""
+    S, I = q.shape
+    hd = I // n_heads
+    dt = {torch.float32: DIT_F32, torch.bfloat16: DIT_BF16}[q.dtype]
+    n = ctypes.c_size_t()
+    check(lib().dit_attention_workspace_size(S, n_heads, hd, dt, ctypes.byref(n)), "dit_attention_workspace_size")
+    if ws is None:
+        ws = workspace(n.value)
+    if out is None:
+        out = torch.empty_like(q)
+    check(lib().dit_attention(S, n_heads, hd, dt, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ws),
+                              ws.numel(), _stream()), "dit_attention")
+    return out
+
+
+def trace_enable(capacity: int):
+    """Record a HIP event before every kernel group of later calls (0: off)."""
+    check(lib().dit_trace_enable(int(capacity)), "dit_trace_enable")
+
+
+def trace_records():
+    """[(name, ms)] for every traced kernel group so far (waits for them)."""
+    out = []
+    L = lib()
+    name, ms = ctypes.c_char_p(), ctypes.c_float()
+    for i in range(L.dit_trace_count() - 1):
+        check(L.dit_trace_read(i, ctypes.byref(name), ctypes.byref(ms)), "dit_trace_read")
+        if name.value != b"end":
+            out.append((name.value.decode(), ms.value))
+    return out

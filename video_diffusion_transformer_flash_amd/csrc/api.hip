@@ -1,0 +1,539 @@
+// C ABI of the gfx950 Flash DiT block library: validation, workspace plans,
+// launch sequencing of one block and of the flow-matching stack.
+//
+// Block (tokendh.com article, backbone and training sections; PaperDaily
+// review, section 2), one stream, no host synchronisation:
+//   rmsnorm1 (reads the joint sequence through its three segments; with
+//             compression the video rows are gathered through keep on read)
+//   -> QKV GEMM (+ rotary embedding, head-major q/k, transposed v)
+//   -> attention -> O GEMM (+ residual, fp32 h) -> rmsnorm2
+//   -> gate/up GEMM (+ SwiGLU) -> down GEMM (+ residual; text/audio/video
+//      rows to the outputs, or delta = y - X for kept video rows)
+//   -> compressed only: broadcast of delta[nk[p]] onto every x_video[p].
+// With fp8 weights every GEMM input is e4m3 with a per-tensor dynamic scale:
+// the norm kernels quantise in a second pass after an amax pass, the
+// attention and SwiGLU outputs are quantised by a separate pass.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "common.h"
+#include "epilogue.h"
+#include "kernels.h"
+
+using namespace dit;
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+// ------------------------------------------------------------------ tracing
+// Process-global event trace for profiling: when enabled, a hipEvent is
+// recorded on the call's stream before each kernel group and after the last
+// one ("end"); durations are read back after the fact. Not thread-safe.
+struct TraceState {
+    int cap = 0;
+    int n = 0;
+    std::vector<hipEvent_t> ev;
+    std::vector<const char*> name;
+};
+TraceState g_tr;
+
+inline void trace(const char* name, hipStream_t st) {
+    if (g_tr.n < g_tr.cap) {
+        hipEventRecord(g_tr.ev[g_tr.n], st);
+        g_tr.name[g_tr.n] = name;
+        ++g_tr.n;
+    }
+}
+#define TR(name) trace(name, st)
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+int keep_count(int n, int s) { return (n + s - 1) / s + (((n - 1) % s) != 0 ? 1 : 0); }
+
+#define HIPCHK(expr)                           \
+    do {                                       \
+        hipError_t e_ = (expr);                \
+        if (e_ != hipSuccess) {                \
+            g_last_hip = (int)e_;              \
+            return DIT_EHIP;                   \
+        }                                      \
+    } while (0)
+
+int esize(int dt) { return dt == DIT_F32 ? 4 : (dt == DIT_BF16 ? 2 : 1); }
+
+int validate_dims(const dit_dims* d) {
+    if (!d) return DIT_EINVAL;
+    if (d->T < 1 || d->H < 1 || d->W < 1 || d->n_text < 0 || d->n_audio < 0 || d->stride < 1) return DIT_EINVAL;
+    if (d->d_model < 64 || d->d_model % 64 || d->d_ffn < 64 || d->d_ffn % 64 || d->n_heads < 1) return DIT_EINVAL;
+    if (d->head_dim != 64 && d->head_dim != 128) return DIT_EUNSUPPORTED;
+    if (d->rope_t < 0 || d->rope_h < 0 || d->rope_w < 0 || (d->rope_t | d->rope_h | d->rope_w) & 1) return DIT_EINVAL;
+    if (d->rope_t + d->rope_h + d->rope_w != d->head_dim) return DIT_EINVAL;
+    if (!(d->rope_base > 0.f) || !(d->eps >= 0.f)) return DIT_EINVAL;
+    const long long nv = (long long)d->T * d->H * d->W;
+    const long long S = nv + d->n_text + d->n_audio;
+    if (S > (1LL << 30) || nv * d->d_model > (1LL << 40)) return DIT_EINVAL;
+    const int a = d->act_dtype, w = d->w_dtype;
+    const bool f32 = a == DIT_F32 && w == DIT_F32;
+    const bool bf = a == DIT_BF16 && w == DIT_BF16;
+    const bool f8 = a == DIT_BF16 && w == DIT_FP8_E4M3;
+    if (!(f32 || bf || f8)) return DIT_EUNSUPPORTED;
+    if (!f32) {
+        const int I = d->n_heads * d->head_dim;
+        if (d->head_dim != 128) return DIT_EUNSUPPORTED;
+        if (d->d_model % 128 || I % 128 || d->d_ffn % 128) return DIT_EUNSUPPORTED;
+    }
+    return DIT_OK;
+}
+
+// ------------------------------------------------------------------ workspace plan
+struct Plan {
+    int S, Sp, nv_seq;
+    size_t tab, n, rinv, q, k, vt, o, o8, h, u, u8, delta, sc, total;
+    int ntab_t;
+};
+
+Plan make_plan(const dit_dims& d, int nv_seq, bool delta) {
+    Plan p{};
+    const bool fp8 = d.w_dtype == DIT_FP8_E4M3;
+    const size_t es = esize(d.act_dtype);
+    const size_t D = d.d_model, I = (size_t)d.n_heads * d.head_dim, F = d.d_ffn;
+    p.nv_seq = nv_seq;
+    p.S = d.n_text + nv_seq + d.n_audio;
+    p.Sp = (p.S + 127) / 128 * 128;
+    p.ntab_t = std::max(std::max(d.T, d.n_audio), 1);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += align256(bytes);
+        return o;
+    };
+    const size_t ntab = (size_t)p.ntab_t * (d.rope_t / 2) + (size_t)d.H * (d.rope_h / 2) + (size_t)d.W * (d.rope_w / 2);
+    p.tab = take(std::max<size_t>(ntab, 1) * sizeof(float2));
+    p.n = take((size_t)p.S * D * (fp8 ? 1 : es));
+    p.rinv = take((size_t)p.S * 4);
+    p.q = take((size_t)d.n_heads * p.Sp * d.head_dim * es);
+    p.k = take((size_t)d.n_heads * p.Sp * d.head_dim * es);
+    p.vt = take((size_t)d.n_heads * p.Sp * d.head_dim * es);
+    p.o = take((size_t)p.S * I * es);
+    p.o8 = fp8 ? take((size_t)p.S * I) : 0;
+    p.h = take((size_t)p.S * D * 4);
+    p.u = take((size_t)p.S * F * es);
+    p.u8 = fp8 ? take((size_t)p.S * F) : 0;
+    p.delta = delta ? take((size_t)nv_seq * D * 4) : 0;
+    p.sc = take(16 * sizeof(float));
+    p.total = off;
+    return p;
+}
+
+// ------------------------------------------------------------------ one block
+// `in`: the joint sequence; `vpos`: flat positions of its video tokens
+// (nullptr: raster); `out`: output segments (or delta); `refin`: rows the
+// delta is taken against.
+int run_block(const dit_dims& d, const dit_block_weights& w, const SeqIn& in, const int32_t* vpos, const SeqOut& out,
+              const SeqIn& refin, uint8_t* ws, const Plan& P, hipStream_t st) {
+    const bool f32 = d.act_dtype == DIT_F32;
+    const bool fp8 = d.w_dtype == DIT_FP8_E4M3;
+    const int D = d.d_model, nh = d.n_heads, dh = d.head_dim, I = nh * dh, F = d.d_ffn;
+    const int S = P.S, Sp = P.Sp;
+
+    float2* tab = (float2*)(ws + P.tab);
+    const int nt_pos = P.ntab_t;
+    TR("rope_tables");
+    HIPCHK(rope_tables_launch(tab, nt_pos, d.rope_t, d.H, d.rope_h, d.W, d.rope_w, (double)d.rope_base, st));
+    Rope rope{};
+    rope.tab_t = tab;
+    rope.tab_h = tab + (size_t)nt_pos * (d.rope_t / 2);
+    rope.tab_w = rope.tab_h + (size_t)d.H * (d.rope_h / 2);
+    rope.vpos = vpos;
+    rope.rt = d.rope_t; rope.rh = d.rope_h; rope.rw = d.rope_w;
+    rope.H = d.H; rope.W = d.W;
+    rope.nt = in.nt; rope.nv = in.nv;
+
+    void* n = ws + P.n;
+    float* rinv = (float*)(ws + P.rinv);
+    void* q = ws + P.q;
+    void* k = ws + P.k;
+    void* vt = ws + P.vt;
+    void* o = ws + P.o;
+    uint8_t* o8 = fp8 ? ws + P.o8 : nullptr;
+    float* h = (float*)(ws + P.h);
+    void* u = ws + P.u;
+    uint8_t* u8 = fp8 ? ws + P.u8 : nullptr;
+    float* sc = (float*)(ws + P.sc);   // [0] n1 amax, [1] o amax, [2] n2 amax, [3] u amax
+
+    EpiParams ep{};
+    ep.M = S; ep.Mpad = Sp; ep.D = D; ep.I = I; ep.F = F; ep.dh = dh;
+    ep.q = q; ep.k = k; ep.vt = vt; ep.Sp = Sp;
+    ep.qscale = (float)(1.4426950408889634 / sqrt((double)dh));
+    ep.rope = rope;
+    ep.xin = in;
+    ep.h = h;
+    ep.u = u;
+    ep.hres = h;
+    ep.out = out;
+    ep.refin = refin;
+
+    // 1-2. RMSNorm1 + QKV (+ rotary)
+    if (fp8) {
+        TR("rmsnorm1");
+        HIPCHK(rmsnorm_fp8_launch(true, in, nullptr, w.g1, (uint8_t*)n, rinv, sc + 0, S, D, d.eps, st));
+        ep.amax_a = sc + 0; ep.s_w = w.s_wqkv;
+        TR("gemm_qkv");
+        HIPCHK(gemm_mfma(true, EPI_QKV, n, w.wqkv, nullptr, S, 3 * I, D, ep, st));
+    } else {
+        TR("rmsnorm1");
+        HIPCHK(rmsnorm_launch(d.act_dtype, true, in, nullptr, w.g1, n, S, D, d.eps, st));
+        TR("gemm_qkv");
+        if (f32) HIPCHK(gemm_f32(EPI_QKV, n, w.wqkv, nullptr, S, 3 * I, D, ep, st));
+        else HIPCHK(gemm_mfma(false, EPI_QKV, n, w.wqkv, nullptr, S, 3 * I, D, ep, st));
+    }
+    // 3. attention
+    TR("attention");
+    if (f32) {
+        HIPCHK(attention_f32(q, k, vt, o, S, Sp, nh, dh, st));
+    } else {
+        if (fp8) HIPCHK(fill_launch(sc + 1, 1, 0.f, st));
+        HIPCHK(attention_bf16(q, k, vt, o, S, Sp, nh, dh, fp8 ? sc + 1 : nullptr, st));
+    }
+    // 4. O projection + residual -> h (fp32)
+    if (fp8) {
+        TR("quant_o");
+        HIPCHK(quant_launch(true, o, o8, sc + 1, (size_t)S * I, st));
+        ep.amax_a = sc + 1; ep.s_w = w.s_wo;
+        TR("gemm_o");
+        HIPCHK(gemm_mfma(true, EPI_RESID, o8, w.wo, nullptr, S, D, I, ep, st));
+    } else if (f32) {
+        TR("gemm_o");
+        HIPCHK(gemm_f32(EPI_RESID, o, w.wo, nullptr, S, D, I, ep, st));
+    } else {
+        TR("gemm_o");
+        HIPCHK(gemm_mfma(false, EPI_RESID, o, w.wo, nullptr, S, D, I, ep, st));
+    }
+    // 5-6. RMSNorm2 + gate/up (+ SwiGLU)
+    if (fp8) {
+        TR("rmsnorm2");
+        HIPCHK(rmsnorm_fp8_launch(false, in, h, w.g2, (uint8_t*)n, rinv, sc + 2, S, D, d.eps, st));
+        HIPCHK(fill_launch(sc + 3, 1, 0.f, st));
+        ep.amax_a = sc + 2; ep.s_w = w.s_wgate; ep.s_w2 = w.s_wup; ep.u_amax = sc + 3;
+        TR("gemm_gate_up");
+        HIPCHK(gemm_mfma(true, EPI_SWIGLU, n, w.wgate, w.wup, S, 2 * F, D, ep, st));
+        ep.u_amax = nullptr;
+    } else {
+        TR("rmsnorm2");
+        HIPCHK(rmsnorm_launch(d.act_dtype, false, in, h, w.g2, n, S, D, d.eps, st));
+        TR("gemm_gate_up");
+        if (f32) HIPCHK(gemm_f32(EPI_SWIGLU, n, w.wgate, w.wup, S, 2 * F, D, ep, st));
+        else HIPCHK(gemm_mfma(false, EPI_SWIGLU, n, w.wgate, w.wup, S, 2 * F, D, ep, st));
+    }
+    // 7. down projection + residual -> outputs / delta
+    if (fp8) {
+        TR("quant_u");
+        HIPCHK(quant_launch(true, u, u8, sc + 3, (size_t)S * F, st));
+        ep.amax_a = sc + 3; ep.s_w = w.s_wdown; ep.s_w2 = nullptr;
+        TR("gemm_down");
+        HIPCHK(gemm_mfma(true, EPI_DOWN, u8, w.wdown, nullptr, S, D, F, ep, st));
+    } else if (f32) {
+        TR("gemm_down");
+        HIPCHK(gemm_f32(EPI_DOWN, u, w.wdown, nullptr, S, D, F, ep, st));
+    } else {
+        TR("gemm_down");
+        HIPCHK(gemm_mfma(false, EPI_DOWN, u, w.wdown, nullptr, S, D, F, ep, st));
+    }
+    return DIT_OK;
+}
+
+int check_weights(const dit_dims& d, const dit_block_weights* w) {
+    if (!w) return DIT_EINVAL;
+    const void* ps[] = {w->g1, w->wqkv, w->wo, w->g2, w->wgate, w->wup, w->wdown};
+    for (const void* p : ps)
+        if (!p || !aligned16(p)) return DIT_EINVAL;
+    if (d.w_dtype == DIT_FP8_E4M3) {
+        const float* ss[] = {w->s_wqkv, w->s_wo, w->s_wgate, w->s_wup, w->s_wdown};
+        for (const float* s : ss)
+            if (!s) return DIT_EINVAL;
+    }
+    return DIT_OK;
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+extern "C" {
+
+const char* dit_status_str(int32_t s) {
+    switch (s) {
+        case DIT_OK: return "ok";
+        case DIT_EINVAL: return "invalid argument";
+        case DIT_EUNSUPPORTED: return "unsupported configuration";
+        case DIT_EWORKSPACE: return "workspace too small";
+        case DIT_EHIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+int32_t dit_last_hip_error(void) { return g_last_hip; }
+
+int32_t dit_trace_enable(int32_t capacity) {
+    if (capacity < 0) return DIT_EINVAL;
+    for (hipEvent_t e : g_tr.ev) hipEventDestroy(e);
+    g_tr.ev.clear();
+    g_tr.name.clear();
+    g_tr.n = 0;
+    g_tr.cap = 0;
+    for (int i = 0; i < capacity; ++i) {
+        hipEvent_t e;
+        hipError_t err = hipEventCreate(&e);
+        if (err != hipSuccess) {
+            g_last_hip = (int)err;
+            return DIT_EHIP;
+        }
+        g_tr.ev.push_back(e);
+        g_tr.name.push_back("");
+    }
+    g_tr.cap = capacity;
+    return DIT_OK;
+}
+
+int32_t dit_trace_count(void) { return g_tr.n; }
+
+int32_t dit_trace_read(int32_t index, const char** name, float* ms) {
+    if (index < 0 || index + 1 >= g_tr.n || !name || !ms) return DIT_EINVAL;
+    *name = g_tr.name[index];
+    HIPCHK(hipEventSynchronize(g_tr.ev[index + 1]));
+    HIPCHK(hipEventElapsedTime(ms, g_tr.ev[index], g_tr.ev[index + 1]));
+    return DIT_OK;
+}
+
+int32_t dit_keep_dims(int32_t H, int32_t W, int32_t stride, int32_t* Hk, int32_t* Wk) {
+    if (H < 1 || W < 1 || stride < 1 || !Hk || !Wk) return DIT_EINVAL;
+    *Hk = keep_count(H, stride);
+    *Wk = keep_count(W, stride);
+    return DIT_OK;
+}
+
+int32_t dit_keep_index(int32_t T, int32_t H, int32_t W, int32_t stride, int32_t* keep, void* stream) {
+    if (T < 1 || H < 1 || W < 1 || stride < 1 || !keep || (long long)T * H * W > (1LL << 30)) return DIT_EINVAL;
+    HIPCHK(keep_index_launch(T, H, W, stride, keep_count(H, stride), keep_count(W, stride), keep, (hipStream_t)stream));
+    return DIT_OK;
+}
+
+int32_t dit_nearest_kept_map(int32_t T, int32_t H, int32_t W, int32_t stride, int32_t* nk, void* stream) {
+    if (T < 1 || H < 1 || W < 1 || stride < 1 || !nk || (long long)T * H * W > (1LL << 30)) return DIT_EINVAL;
+    HIPCHK(nearest_map_launch(T, H, W, stride, keep_count(H, stride), keep_count(W, stride), nk, (hipStream_t)stream));
+    return DIT_OK;
+}
+
+int32_t dit_block_workspace_size(const dit_dims* dims, int32_t compress_on, size_t* bytes) {
+    int r = validate_dims(dims);
+    if (r) return r;
+    if (!bytes) return DIT_EINVAL;
+    const int nv = dims->T * dims->H * dims->W;
+    const int nk = dims->T * keep_count(dims->H, dims->stride) * keep_count(dims->W, dims->stride);
+    *bytes = make_plan(*dims, compress_on ? nk : nv, compress_on != 0).total;
+    return DIT_OK;
+}
+
+int32_t dit_block_forward(const dit_dims* dims, const void* x_text, const void* x_video, const void* x_audio,
+                          const dit_block_weights* weights, int32_t compress_on, const int32_t* keep,
+                          const int32_t* nk, void* y_text, void* y_video, void* y_audio, void* ws, size_t ws_bytes,
+                          void* stream) {
+    int r = validate_dims(dims);
+    if (r) return r;
+    const dit_dims& d = *dims;
+    if ((r = check_weights(d, weights))) return r;
+    if (!x_video || !y_video || !aligned16(x_video) || !aligned16(y_video)) return DIT_EINVAL;
+    if (d.n_text > 0 && (!x_text || !y_text || !aligned16(x_text) || !aligned16(y_text))) return DIT_EINVAL;
+    if (d.n_audio > 0 && (!x_audio || !y_audio || !aligned16(x_audio) || !aligned16(y_audio))) return DIT_EINVAL;
+    if (compress_on && (!keep || !nk)) return DIT_EINVAL;
+    if (!ws || ((uintptr_t)ws & 255)) return DIT_EINVAL;
+    const int nv = d.T * d.H * d.W;
+    const int nkept = d.T * keep_count(d.H, d.stride) * keep_count(d.W, d.stride);
+    const Plan P = make_plan(d, compress_on ? nkept : nv, compress_on != 0);
+    if (ws_bytes < P.total) return DIT_EWORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    uint8_t* w8 = (uint8_t*)ws;
+
+    SeqIn in{x_text, x_video, x_audio, compress_on ? keep : nullptr, d.n_text, compress_on ? nkept : nv, d.n_audio};
+    SeqOut out{y_text, y_video, y_audio, compress_on ? (float*)(w8 + P.delta) : nullptr, nullptr, nullptr};
+    r = run_block(d, *weights, in, compress_on ? keep : nullptr, out, in, w8, P, st);
+    if (r) return r;
+    if (compress_on) {
+        TR("broadcast_residual");
+        HIPCHK(broadcast_residual_launch(d.act_dtype == DIT_BF16, x_video, (const float*)(w8 + P.delta), nk, y_video, nv,
+                                         d.d_model, st));
+    }
+    TR("end");
+    return DIT_OK;
+}
+
+int32_t dit_stack_workspace_size(const dit_dims* dims, const uint8_t* compressed_host, int32_t n_layers,
+                                 size_t* bytes) {
+    int r = validate_dims(dims);
+    if (r) return r;
+    if (!bytes || n_layers < 0 || (n_layers > 0 && !compressed_host)) return DIT_EINVAL;
+    const dit_dims& d = *dims;
+    const size_t es = esize(d.act_dtype);
+    const int nv = d.T * d.H * d.W;
+    const int nkept = d.T * keep_count(d.H, d.stride) * keep_count(d.W, d.stride);
+    const size_t Soff = (size_t)d.n_text + nv + d.n_audio, Son = (size_t)d.n_text + nkept + d.n_audio;
+    const Plan Pf = make_plan(d, nv, false), Pc = make_plan(d, nkept, true);
+    *bytes = align256(Soff * d.d_model * es) + align256(Son * d.d_model * es) + std::max(Pf.total, Pc.total);
+    return DIT_OK;
+}
+
+int32_t dit_stack_sample(const dit_dims* dims, const dit_block_weights* layers_host, int32_t n_layers,
+                         const uint8_t* compressed_host, int32_t n_evals, const float* t_video_host,
+                         const float* t_audio_host, const void* x_text, void* x_video, void* x_audio,
+                         const int32_t* keep, const int32_t* nk, void* ws, size_t ws_bytes, void* stream) {
+    int r = validate_dims(dims);
+    if (r) return r;
+    const dit_dims& d = *dims;
+    if (n_layers < 0 || n_evals < 0 || (n_layers > 0 && (!layers_host || !compressed_host))) return DIT_EINVAL;
+    if (n_evals > 0 && !t_video_host) return DIT_EINVAL;
+    bool any_c = false;
+    for (int l = 0; l < n_layers; ++l) {
+        if ((r = check_weights(d, &layers_host[l]))) return r;
+        any_c |= compressed_host[l] != 0;
+    }
+    if (any_c && (!keep || !nk)) return DIT_EINVAL;
+    if (!x_video || !aligned16(x_video)) return DIT_EINVAL;
+    if (d.n_text > 0 && (!x_text || !aligned16(x_text))) return DIT_EINVAL;
+    if (d.n_audio > 0 && (!x_audio || !aligned16(x_audio))) return DIT_EINVAL;
+    if (!ws || ((uintptr_t)ws & 255)) return DIT_EINVAL;
+    size_t need = 0;
+    dit_stack_workspace_size(dims, compressed_host, n_layers, &need);
+    if (ws_bytes < need) return DIT_EWORKSPACE;
+    if (n_evals == 0) return DIT_OK;
+
+    hipStream_t st = (hipStream_t)stream;
+    const size_t es = esize(d.act_dtype);
+    const bool bf = d.act_dtype == DIT_BF16;
+    const size_t D = d.d_model;
+    const int nv = d.T * d.H * d.W;
+    const int nkept = d.T * keep_count(d.H, d.stride) * keep_count(d.W, d.stride);
+    const size_t Soff = (size_t)d.n_text + nv + d.n_audio, Son = (size_t)d.n_text + nkept + d.n_audio;
+    uint8_t* w8 = (uint8_t*)ws;
+    uint8_t* Z = w8;
+    uint8_t* Zc = Z + align256(Soff * D * es);
+    uint8_t* bws = Zc + align256(Son * D * es);
+    const Plan Pf = make_plan(d, nv, false), Pc = make_plan(d, nkept, true);
+    float* delta = (float*)(bws + Pc.delta);
+
+    void* Zt = Z;
+    void* Zv = Z + (size_t)d.n_text * D * es;
+    void* Za = Z + ((size_t)d.n_text + nv) * D * es;
+    void* Zct = Zc;
+    void* Zcv = Zc + (size_t)d.n_text * D * es;
+    void* Zca = Zc + ((size_t)d.n_text + nkept) * D * es;
+
+    for (int ev = 0; ev < n_evals; ++ev) {
+        // current full-resolution state: the inputs for the first layer, Z after
+        SeqIn cur{x_text, x_video, x_audio, nullptr, d.n_text, nv, d.n_audio};
+        int l = 0;
+        while (l < n_layers) {
+            if (!compressed_host[l]) {
+                SeqOut out{Zt, Zv, Za, nullptr, nullptr, nullptr};
+                if ((r = run_block(d, layers_host[l], cur, nullptr, out, cur, bws, Pf, st))) return r;
+                cur = SeqIn{Zt, Zv, Za, nullptr, d.n_text, nv, d.n_audio};
+                ++l;
+                continue;
+            }
+            int e = l;
+            while (e < n_layers && compressed_host[e]) ++e;
+            // span [l, e): gather on read at its start, broadcast the summed update at its end
+            const SeqIn start{cur.xt, cur.xv, cur.xa, keep, d.n_text, nkept, d.n_audio};
+            const SeqIn packed{Zct, Zcv, Zca, nullptr, d.n_text, nkept, d.n_audio};
+            for (int i = l; i < e; ++i) {
+                const SeqIn& in = (i == l) ? start : packed;
+                SeqOut out = (i + 1 < e) ? SeqOut{Zct, Zcv, Zca, nullptr, nullptr, nullptr}
+                                         : SeqOut{Zt, nullptr, Za, delta, nullptr, nullptr};
+                if ((r = run_block(d, layers_host[i], in, keep, out, start, bws, Pc, st))) return r;
+            }
+            TR("broadcast_residual");
+            HIPCHK(broadcast_residual_launch(bf, cur.xv, delta, nk, Zv, nv, (int)D, st));
+            cur = SeqIn{Zt, Zv, Za, nullptr, d.n_text, nv, d.n_audio};
+            l = e;
+        }
+        const float dtv = (float)((double)t_video_host[ev + 1] - (double)t_video_host[ev]);
+        const float* ta = t_audio_host ? t_audio_host : t_video_host;
+        const float dta = (float)((double)ta[ev + 1] - (double)ta[ev]);
+        // velocity = the stack output (the state itself when there are no layers)
+        const void* vv = n_layers ? (const void*)Zv : (const void*)x_video;
+        const void* va = n_layers ? (const void*)Za : (const void*)x_audio;
+        TR("euler");
+        HIPCHK(euler_launch(bf, x_video, vv, (size_t)nv * D, dtv, st));
+        if (d.n_audio > 0) HIPCHK(euler_launch(bf, x_audio, va, (size_t)d.n_audio * D, dta, st));
+    }
+    TR("end");
+    return DIT_OK;
+}
+
+int32_t dit_quantize_fp8(const void* src, int32_t src_dtype, int64_t n, uint8_t* dst, float* scale, void* stream) {
+    if (!src || !dst || !scale || n <= 0 || n % 4 || !aligned16(src) || ((uintptr_t)dst & 3)) return DIT_EINVAL;
+    if (src_dtype != DIT_F32 && src_dtype != DIT_BF16) return DIT_EUNSUPPORTED;
+    hipStream_t st = (hipStream_t)stream;
+    const bool bf = src_dtype == DIT_BF16;
+    HIPCHK(fill_launch(scale, 1, 0.f, st));
+    HIPCHK(amax_launch(bf, src, (size_t)n, scale, st));
+    HIPCHK(quant_launch(bf, src, dst, scale, (size_t)n, st));
+    HIPCHK(amax_to_scale_launch(scale, st));
+    return DIT_OK;
+}
+
+int32_t dit_gather_kept(int32_t n_kept, int32_t D, int32_t dtype, const void* x_video, const int32_t* keep, void* out,
+                        void* stream) {
+    if (n_kept < 0 || D <= 0 || !x_video || !keep || !out || !aligned16(x_video) || !aligned16(out)) return DIT_EINVAL;
+    if (dtype != DIT_F32 && dtype != DIT_BF16) return DIT_EUNSUPPORTED;
+    const size_t rowbytes = (size_t)D * esize(dtype);
+    if (rowbytes % 16) return DIT_EINVAL;
+    if (n_kept == 0) return DIT_OK;
+    HIPCHK(gather_rows_launch(x_video, keep, out, n_kept, rowbytes, (hipStream_t)stream));
+    return DIT_OK;
+}
+
+int32_t dit_broadcast_residual(int32_t n_video, int32_t n_kept, int32_t D, int32_t dtype, const void* x_video,
+                               const float* delta, const int32_t* nk, void* out, void* stream) {
+    if (n_video < 0 || n_kept < 1 || D <= 0 || D % 8 || !x_video || !delta || !nk || !out) return DIT_EINVAL;
+    if (!aligned16(x_video) || !aligned16(delta) || !aligned16(out)) return DIT_EINVAL;
+    if (dtype != DIT_F32 && dtype != DIT_BF16) return DIT_EUNSUPPORTED;
+    if (n_video == 0) return DIT_OK;
+    HIPCHK(broadcast_residual_launch(dtype == DIT_BF16, x_video, delta, nk, out, n_video, D, (hipStream_t)stream));
+    return DIT_OK;
+}
+
+int32_t dit_attention_workspace_size(int32_t S, int32_t n_heads, int32_t head_dim, int32_t dtype, size_t* bytes) {
+    if (S < 1 || n_heads < 1 || !bytes) return DIT_EINVAL;
+    if (dtype != DIT_F32 && dtype != DIT_BF16) return DIT_EUNSUPPORTED;
+    if (head_dim != 128 && !(dtype == DIT_F32 && head_dim == 64)) return DIT_EUNSUPPORTED;
+    const size_t Sp = ((size_t)S + 127) / 128 * 128;
+    *bytes = 3 * align256(Sp * n_heads * head_dim * esize(dtype));
+    return DIT_OK;
+}
+
+int32_t dit_attention(int32_t S, int32_t n_heads, int32_t head_dim, int32_t dtype, float scale, const void* q,
+                      const void* k, const void* v, void* o, void* ws, size_t ws_bytes, void* stream) {
+    size_t need = 0;
+    int r = dit_attention_workspace_size(S, n_heads, head_dim, dtype, &need);
+    if (r) return r;
+    if (!q || !k || !v || !o || !ws || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        ((uintptr_t)ws & 255))
+        return DIT_EINVAL;
+    if (ws_bytes < need) return DIT_EWORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    const int Sp = (S + 127) / 128 * 128;
+    const size_t part = need / 3;
+    uint8_t* w8 = (uint8_t*)ws;
+    const float qscale = (float)((double)scale * 1.4426950408889634);
+    HIPCHK(attention_pack(dtype == DIT_BF16, q, k, v, w8, w8 + part, w8 + 2 * part, S, Sp, n_heads, head_dim, qscale, st));
+    if (dtype == DIT_BF16) HIPCHK(attention_bf16(w8, w8 + part, w8 + 2 * part, o, S, Sp, n_heads, head_dim, nullptr, st));
+    else HIPCHK(attention_f32(w8, w8 + part, w8 + 2 * part, o, S, Sp, n_heads, head_dim, st));
+    return DIT_OK;
+}
+
+}  // extern "C"

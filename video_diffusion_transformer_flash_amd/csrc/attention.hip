@@ -1,0 +1,337 @@
+// Joint-sequence attention for gfx950: o = softmax(q k^T / sqrt(dh)) v per
+// head, unmasked, over [text | video | audio] (tokendh.com article, backbone
+// section: one shared denoiser over all modalities; PaperDaily review,
+// section 2: attention cost grows strongly with sequence length, which the
+// compressed layers shorten).
+//
+// Inputs come from the QKV epilogue: q, k [head][Sp][dh] (q already rotated
+// and scaled by log2(e)/sqrt(dh), so the softmax uses exp2), v transposed
+// [head][dh][Sp]; rows [S, Sp) are zero. Output o [S][heads * dh].
+//
+// bf16 kernel: a workgroup of 4 waves takes 128 queries of one head, a wave
+// 32 queries. The wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
+// (keys on the MFMA rows, queries on its columns): a lane then owns one
+// query and 32 of its 64 scores per key tile, so the online-softmax row max
+// and sum need a single exchange with the partner lane l^32. P^T goes straight
+// from the accumulator to the B operand of O^T += V^T P^T; the key order
+// inside each 16-key step is the accumulator's order, and V^T is read from
+// LDS in that same order. K and V^T tiles of 64 keys are double-buffered in
+// LDS with XOR swizzles for the 64-bank LDS.
+#include "common.h"
+#include "kernels.h"
+
+namespace dit {
+
+namespace detail {
+
+constexpr int KT = 64;   // keys per tile
+constexpr int QW = 32;   // queries per wave
+typedef __attribute__((address_space(3))) uint8_t* LDSPTR;
+
+DIT_DEV int swzK(int row, int c) { return c ^ (row & 15); }          // 16-byte chunks, 256-byte K rows
+DIT_DEV int swzV(int row, int c) { return c ^ ((row >> 1) & 7); }    // 16-byte chunks, 128-byte V^T rows
+// Key order of the S^T rows: lane row i reads key rho(i) (bits 2 and 3
+// swapped) so that each lane's eight P values of a 16-key step are 8
+// consecutive keys, matching one 16-byte read of a V^T row.
+DIT_DEV int rho(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+
+__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
+                                                           const bf16_t* __restrict__ Vt, bf16_t* __restrict__ O,
+                                                           int S, int Sp, int nh, float* o_amax) {
+    constexpr int DH = 128;
+    __shared__ __attribute__((aligned(16))) uint8_t sK[2][KT * DH * 2];
+    __shared__ __attribute__((aligned(16))) uint8_t sV[2][DH * KT * 2];
+
+    const int nq = (S + 127) / 128;
+    const int blk = xcd_remap(blockIdx.x, nq * nh);
+    const int head = blk / nq;
+    const int qt = blk - head * nq;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lrow = lane & 31, lhalf = lane >> 5;
+    const int q0 = qt * 128 + wave * QW;
+
+    const bf16_t* Qh = Q + (size_t)head * Sp * DH;
+    const bf16_t* Kh = K + (size_t)head * Sp * DH;
+    const bf16_t* Vh = Vt + (size_t)head * DH * Sp;
+
+    // Q^T operand fragments for the 8 dh steps of 16
+    bf16x8_v qf[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[s] = *(const bf16x8_v*)(Qh + (size_t)(q0 + lrow) * DH + 16 * s + 8 * lhalf);
+
+    // Memory -> LDS fills (buffer_load ... lds, 16 bytes per lane). K: one
+    // instruction writes 4 rows of 256 B; instruction i of wave w rows
+    // 16 i + 4 w + L/16. V^T: 8 rows of 128 B; rows 32 i + 8 w + L/8. The
+    // swizzle is applied by fetching logical chunk (slot ^ swz(row)).
+    const __amdgpu_buffer_rsrc_t rsK = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, 0, Sp * DH * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsV = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, 0, Sp * DH * 2, 0x00020000);
+    const int krow = 4 * wave + (lane >> 4);
+    const int voK = krow * 256 + swzK(krow, lane & 15) * 16;
+    const int vrow = 8 * wave + (lane >> 3);
+    const int voV = vrow * Sp * 2 + swzV(vrow, lane & 7) * 16;
+    auto issue = [&](int kt, int buf) {
+        LDSPTR lk = (LDSPTR)(sK[buf] + wave * 1024);
+        LDSPTR lv = (LDSPTR)(sV[buf] + wave * 1024);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, lk + i * 4096, 16, voK, kt * KT * 256 + i * 16 * 256, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, lv + i * 4096, 16, voV, kt * KT * 2 + i * 32 * Sp * 2, 0, 0);
+        }
+    };
+
+    f32x16 o[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
+    float mrun = -INFINITY, lrun = 0.f;
+
+    const int nkt = (S + KT - 1) / KT;
+    issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    for (int kt = 0; kt < nkt; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nkt) issue(kt + 1, buf ^ 1);
+        const uint8_t* bK = sK[buf];
+        const uint8_t* bV = sV[buf];
+
+        // scores S^T for 2 blocks of 32 keys (row i of block b is key 32 b + rho(i))
+        f32x16 sc[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sc[b][r] = 0.f;
+            const int row = b * 32 + rho(lrow);
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                bf16x8_v kf = *(const bf16x8_v*)(bK + row * 256 + swzK(row, 2 * s + lhalf) * 16);
+                sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sc[b], 0, 0, 0);
+            }
+        }
+        // mask keys >= S (only in the last tile)
+        const int k0 = kt * KT;
+        if (k0 + KT > S) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    int key = k0 + b * 32 + rho(8 * (r >> 2) + 4 * lhalf + (r & 3));
+                    if (key >= S) sc[b][r] = -INFINITY;
+                }
+        }
+        float tmax = sc[0][0];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sc[b][r]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float mnew = fmaxf(mrun, tmax);
+        const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+        mrun = mnew;
+        float psum = 0.f;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float p = __builtin_amdgcn_exp2f(sc[b][r] - mnew);
+                sc[b][r] = p;
+                psum += p;
+            }
+        lrun = lrun * alpha + psum;
+        if (__ballot(alpha != 1.f)) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+        }
+        // P^T fragments: key step ks = registers 8 (ks % 2) .. +7 of block ks / 2,
+        // i.e. keys 16 ks + 8 h + 0..7 for lane half h
+        bf16x8_v pf[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int b = ks >> 1, r0 = 8 * (ks & 1);
+            uint4 w = make_uint4(pack_bf2(sc[b][r0 + 0], sc[b][r0 + 1]), pack_bf2(sc[b][r0 + 2], sc[b][r0 + 3]),
+                                 pack_bf2(sc[b][r0 + 4], sc[b][r0 + 5]), pack_bf2(sc[b][r0 + 6], sc[b][r0 + 7]));
+            pf[ks] = __builtin_bit_cast(bf16x8_v, w);
+        }
+        // O^T += V^T P^T; the A operand lane (dh row, half h) reads keys 16 ks + 8 h .. +7
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const int row = d * 32 + lrow;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                bf16x8_v vf = *(const bf16x8_v*)(bV + row * 128 + swzV(row, 2 * ks + lhalf) * 16);
+                o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[d], 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    const float ltot = lrun + __shfl_xor(lrun, 32, 64);
+    const float inv = 1.f / ltot;
+    const int q = q0 + lrow;
+    float mx = 0.f;
+    if (q < S) {
+        bf16_t* orow = O + (size_t)q * nh * DH + head * DH;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float v0 = o[d][4 * g] * inv, v1 = o[d][4 * g + 1] * inv;
+                float v2 = o[d][4 * g + 2] * inv, v3 = o[d][4 * g + 3] * inv;
+                uint2 w = make_uint2(pack_bf2(v0, v1), pack_bf2(v2, v3));
+                *(uint2*)(orow + d * 32 + 8 * g + 4 * lhalf) = w;
+                if (o_amax) {
+                    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(bf2f(f2bf(v0))), fabsf(bf2f(f2bf(v1)))),
+                                         fmaxf(fabsf(bf2f(f2bf(v2))), fabsf(bf2f(f2bf(v3))))));
+                }
+            }
+    }
+    if (o_amax) {
+        mx = wave_max(mx);
+        if (lane == 0) atomic_max_nonneg(o_amax, mx);
+    }
+}
+
+// fp32 attention: one thread per query, 64 queries of one head per block,
+// key tiles of 32 in LDS; exact fp32 online softmax (exp2 on pre-scaled q).
+template <int DH>
+__global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                                                      const float* __restrict__ Vt, float* __restrict__ O, int S,
+                                                      int Sp, int nh) {
+    constexpr int KB = 32;
+    __shared__ float sk[KB][DH + 1];
+    __shared__ float sv[KB][DH + 1];
+    const int nq = (S + 63) / 64;
+    const int head = blockIdx.x / nq;
+    const int qt = blockIdx.x - head * nq;
+    const int q = qt * 64 + threadIdx.x;
+    const float* Qh = Q + (size_t)head * Sp * DH;
+    const float* Kh = K + (size_t)head * Sp * DH;
+    const float* Vh = Vt + (size_t)head * DH * Sp;
+    float qr[DH], acc[DH];
+    const int qq = min(q, Sp - 1);
+#pragma unroll
+    for (int d = 0; d < DH; ++d) {
+        qr[d] = Qh[(size_t)qq * DH + d];
+        acc[d] = 0.f;
+    }
+    float m = -INFINITY, l = 0.f;
+    for (int k0 = 0; k0 < S; k0 += KB) {
+        __syncthreads();
+        for (int i = threadIdx.x; i < KB * DH; i += 64) {
+            int r = i / DH, d = i - r * DH;
+            int key = k0 + r;
+            sk[r][d] = key < Sp ? Kh[(size_t)key * DH + d] : 0.f;
+            int vd = i / KB, vr = i - vd * KB;
+            int vkey = k0 + vr;
+            sv[vr][vd] = vkey < Sp ? Vh[(size_t)vd * Sp + vkey] : 0.f;
+        }
+        __syncthreads();
+        float s[KB];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+            float a = 0.f;
+#pragma unroll
+            for (int d = 0; d < DH; ++d) a = fmaf(qr[d], sk[j][d], a);
+            s[j] = (k0 + j < S) ? a : -INFINITY;
+            tmax = fmaxf(tmax, s[j]);
+        }
+        const float mn = fmaxf(m, tmax);
+        const float alpha = exp2f(m - mn);
+        m = mn;
+        l *= alpha;
+#pragma unroll
+        for (int d = 0; d < DH; ++d) acc[d] *= alpha;
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+            const float p = exp2f(s[j] - mn);
+            l += p;
+#pragma unroll
+            for (int d = 0; d < DH; ++d) acc[d] = fmaf(p, sv[j][d], acc[d]);
+        }
+    }
+    if (q < S) {
+        float* orow = O + (size_t)q * nh * DH + head * DH;
+        const float inv = 1.f / l;
+#pragma unroll
+        for (int d = 0; d < DH; ++d) orow[d] = acc[d] * inv;
+    }
+}
+
+// [S][nh*dh] -> head-major padded layouts (q scaled), zero rows [S, Sp)
+template <typename T>
+__global__ void attn_pack_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                                 T* __restrict__ Qp, T* __restrict__ Kp, T* __restrict__ Vtp, int S, int Sp, int nh,
+                                 int dh, float qscale) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t total = (size_t)Sp * nh * dh;
+    if (i >= total) return;
+    const int d = (int)(i % dh);
+    const int hh = (int)((i / dh) % nh);
+    const int s = (int)(i / ((size_t)dh * nh));
+    float qv = 0.f, kv = 0.f, vv = 0.f;
+    if (s < S) {
+        const size_t src = (size_t)s * nh * dh + (size_t)hh * dh + d;
+        if constexpr (sizeof(T) == 2) {
+            qv = bf2f(q[src]); kv = bf2f(k[src]); vv = bf2f(v[src]);
+        } else {
+            qv = q[src]; kv = k[src]; vv = v[src];
+        }
+        qv *= qscale;
+    }
+    const size_t o = ((size_t)hh * Sp + s) * dh + d;
+    const size_t ov = ((size_t)hh * dh + d) * Sp + s;
+    if constexpr (sizeof(T) == 2) {
+        Qp[o] = f2bf(qv); Kp[o] = f2bf(kv); Vtp[ov] = f2bf(vv);
+    } else {
+        Qp[o] = qv; Kp[o] = kv; Vtp[ov] = vv;
+    }
+}
+
+}  // namespace detail
+using namespace detail;
+
+hipError_t attention_bf16(const void* Q, const void* K, const void* Vt, void* O, int S, int Sp, int nh, int dh,
+                          float* o_amax, hipStream_t st) {
+    if (dh != 128) return hipErrorInvalidValue;
+    const int nq = (S + 127) / 128;
+    hipLaunchKernelGGL(attn_bf16_kernel, dim3(nq * nh), dim3(256), 0, st, (const bf16_t*)Q, (const bf16_t*)K,
+                       (const bf16_t*)Vt, (bf16_t*)O, S, Sp, nh, o_amax);
+    return hipGetLastError();
+}
+
+hipError_t attention_f32(const void* Q, const void* K, const void* Vt, void* O, int S, int Sp, int nh, int dh,
+                         hipStream_t st) {
+    const int nq = (S + 63) / 64;
+    if (dh == 64)
+        hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(nq * nh), dim3(64), 0, st, (const float*)Q, (const float*)K,
+                           (const float*)Vt, (float*)O, S, Sp, nh);
+    else if (dh == 128)
+        hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(nq * nh), dim3(64), 0, st, (const float*)Q, (const float*)K,
+                           (const float*)Vt, (float*)O, S, Sp, nh);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t attention_pack(bool bf16, const void* q, const void* k, const void* v, void* Qp, void* Kp, void* Vtp,
+                          int S, int Sp, int nh, int dh, float qscale, hipStream_t st) {
+    const size_t total = (size_t)Sp * nh * dh;
+    const int blocks = (int)((total + 255) / 256);
+    if (bf16)
+        hipLaunchKernelGGL(attn_pack_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st, (const bf16_t*)q,
+                           (const bf16_t*)k, (const bf16_t*)v, (bf16_t*)Qp, (bf16_t*)Kp, (bf16_t*)Vtp, S, Sp, nh,
+                           dh, qscale);
+    else
+        hipLaunchKernelGGL(attn_pack_kernel<float>, dim3(blocks), dim3(256), 0, st, (const float*)q,
+                           (const float*)k, (const float*)v, (float*)Qp, (float*)Kp, (float*)Vtp, S, Sp, nh, dh,
+                           qscale);
+    return hipGetLastError();
+}
+
+}  // namespace dit

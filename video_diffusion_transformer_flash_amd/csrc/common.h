@@ -1,0 +1,145 @@
+// Shared device/host helpers of the gfx950 Flash DiT library (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/vdtflash.h"
+
+#define DIT_DEV __device__ __forceinline__
+
+typedef uint16_t bf16_t;                                    // raw bfloat16 bits
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_v;  // MFMA operand type
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+namespace dit {
+
+// ----------------------------------------------------------------- bf16 / fp32
+DIT_DEV float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// fp32 -> bf16, round to nearest even (inputs are finite in this library)
+DIT_DEV bf16_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+DIT_DEV uint32_t pack_bf2(float a, float b) { return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16); }
+
+// ----------------------------------------------------------------- fp8 e4m3
+// fp32 -> OCP e4m3 code: nearest value, ties to even, saturating at +-448,
+// sign kept. The code space is monotone in the magnitude: subnormal codes are
+// rint(a * 2^9) (a < 2^-6) and a normal a in [2^e, 2^(e+1)) has code
+// 8 (e + 6) + rint(a * 2^(3 - e)); both scalings are exact, so the only
+// rounding is the round-half-even of v_rndne_f32, and a carry out of the
+// mantissa moves to the next exponent by itself.
+DIT_DEV uint32_t f32_to_e4m3(float x) {
+    uint32_t s = (__float_as_uint(x) >> 24) & 0x80u;
+    float a = fminf(fabsf(x), 448.f);
+    uint32_t code;
+    if (a < 0.015625f) {
+        code = (uint32_t)__builtin_rintf(a * 512.f);
+    } else {
+        int e = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;
+        float scaled = a * __uint_as_float((uint32_t)(127 + 3 - e) << 23);
+        code = (uint32_t)(8 * (e + 6)) + (uint32_t)__builtin_rintf(scaled);
+    }
+    return s | code;
+}
+
+// ----------------------------------------------------------------- reductions
+DIT_DEV float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+DIT_DEV float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// Non-negative float max through integer ordering (valid for x >= 0).
+DIT_DEV void atomic_max_nonneg(float* addr, float x) { atomicMax((unsigned int*)addr, __float_as_uint(x)); }
+
+// ----------------------------------------------------------------- sequence layout
+// The joint sequence is [text | video tokens | audio]. Video tokens are either
+// every position of x_video (vidx == nullptr) or the rows listed in vidx.
+struct SeqIn {
+    const void* xt;
+    const void* xv;
+    const void* xa;
+    const int32_t* vidx;   // video token j -> row of xv (nullptr: j)
+    int nt, nv, na;
+};
+
+// Output rows of the block. With delta != nullptr the video rows are not
+// written to yv; instead delta[j] = y_j - ref_j (fp32) with ref_j the row
+// ref_v[ref_idx[j]] (ref_idx nullptr: j) of act dtype.
+struct SeqOut {
+    void* yt;
+    void* yv;
+    void* ya;
+    float* delta;
+    const void* ref_v;
+    const int32_t* ref_idx;
+};
+
+// Rotary geometry: per-token coordinates and fp32 (cos, sin) tables per band.
+struct Rope {
+    const float2* tab_t;   // [npos_t][rt/2]
+    const float2* tab_h;   // [H][rh/2]
+    const float2* tab_w;   // [W][rw/2]
+    const int32_t* vpos;   // video token j -> flat position (nullptr: j)
+    int rt, rh, rw;
+    int H, W;
+    int nt, nv;            // text / video token counts in the sequence
+};
+
+template <typename T>
+DIT_DEV const T* seq_row(const SeqIn& s, int m, int D) {
+    if (m < s.nt) return (const T*)s.xt + (size_t)m * D;
+    m -= s.nt;
+    if (m < s.nv) {
+        int r = s.vidx ? s.vidx[m] : m;
+        return (const T*)s.xv + (size_t)r * D;
+    }
+    return (const T*)s.xa + (size_t)(m - s.nv) * D;
+}
+
+// coordinates (t, h, w) of sequence row m; text -> (0,0,0), audio j -> (j,0,0)
+DIT_DEV int3 rope_coords(const Rope& r, int m) {
+    if (m < r.nt) return make_int3(0, 0, 0);
+    m -= r.nt;
+    if (m < r.nv) {
+        int p = r.vpos ? r.vpos[m] : m;
+        int hw = r.H * r.W;
+        int t = p / hw;
+        int rem = p - t * hw;
+        int h = rem / r.W;
+        return make_int3(t, h, rem - h * r.W);
+    }
+    return make_int3(m - r.nv, 0, 0);
+}
+
+// (cos, sin) for head-local feature d (even member of its pair) at coords c
+DIT_DEV float2 rope_cs(const Rope& r, int d, int3 c) {
+    if (d < r.rt) return r.tab_t[c.x * (r.rt >> 1) + (d >> 1)];
+    d -= r.rt;
+    if (d < r.rh) return r.tab_h[c.y * (r.rh >> 1) + (d >> 1)];
+    d -= r.rh;
+    return r.tab_w[c.z * (r.rw >> 1) + (d >> 1)];
+}
+
+// XCD-aware remap of a linear workgroup id: the hardware deals workgroups
+// round-robin to the 8 XCDs; consecutive logical tiles should share an XCD
+// (and its L2), so logical = (bid % 8) * (n / 8) + bid / 8 on the full part.
+DIT_DEV int xcd_remap(int bid, int n) {
+    int full = (n / 8) * 8;
+    if (bid >= full) return bid;
+    return (bid & 7) * (n >> 3) + (bid >> 3);
+}
+
+}  // namespace dit

@@ -1,0 +1,214 @@
+// GEMM epilogues of the Flash DiT block (internal).
+//
+// Every projection GEMM computes acc[m][n] = sum_k A[m][k] W[n][k] with the
+// token index m and the output feature n; the MFMA kernels hand the epilogue
+// four consecutive features n0..n0+3 of one token (the lane-owned run of the
+// 32x32 accumulator layout), the fp32 kernel does the same. The epilogues fuse
+// what follows each projection in the block (PaperDaily review, section 2:
+// norm, quantisation, rotary embedding and residual update are fused):
+//   QKV   : rotary embedding on q and k (pairs (2i, 2i+1) of each band), q
+//           pre-scaled by log2(e)/sqrt(head_dim) for the exp2 softmax, written
+//           head-major: q, k [head][Sp][dh], v transposed [head][dh][Sp];
+//   RESID : h = X + acc in fp32 (attention output projection);
+//   SWIGLU: u = silu(gate) * up, with the running |u| max for fp8;
+//   DOWN  : y = h + acc to the text / video / audio outputs, or for kept video
+//           rows of a compressed block delta = y - X_ref in fp32.
+#pragma once
+
+#include <type_traits>
+
+#include "common.h"
+
+namespace dit {
+
+enum EpiMode { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_DOWN = 3 };
+
+struct EpiParams {
+    int M;          // valid token rows
+    int Mpad;       // QKV: token rows [M, Mpad) are written as zeros
+    int D, I, F, dh;
+    // fp8: acc *= (amax_a / 448) * (*s_w); both on the device. nullptr: no scaling
+    const float* amax_a;
+    const float* s_w;
+    const float* s_w2;      // SWIGLU: scale of the up weights (gate uses s_w)
+    // QKV
+    void* q;
+    void* k;
+    void* vt;
+    int Sp;
+    float qscale;
+    Rope rope;
+    // RESID
+    SeqIn xin;
+    float* h;
+    // SWIGLU
+    void* u;
+    float* u_amax;          // nullptr: no max tracking
+    // DOWN
+    const float* hres;
+    SeqOut out;
+    SeqIn refin;            // reference rows for delta (video segment only)
+};
+
+template <typename T> DIT_DEV void store4(T* p, const float v[4]);
+template <> DIT_DEV void store4<float>(float* p, const float v[4]) { *(float4*)p = make_float4(v[0], v[1], v[2], v[3]); }
+template <> DIT_DEV void store4<bf16_t>(bf16_t* p, const float v[4]) {
+    *(uint2*)p = make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
+}
+template <typename T> DIT_DEV void load4(const T* p, float v[4]);
+template <> DIT_DEV void load4<float>(const float* p, float v[4]) {
+    float4 x = *(const float4*)p;
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+}
+template <> DIT_DEV void load4<bf16_t>(const bf16_t* p, float v[4]) {
+    uint2 x = *(const uint2*)p;
+    v[0] = __uint_as_float(x.x << 16); v[1] = __uint_as_float(x.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(x.y << 16); v[3] = __uint_as_float(x.y & 0xFFFF0000u);
+}
+template <typename T> DIT_DEV T cvt_out(float v);
+template <> DIT_DEV float cvt_out<float>(float v) { return v; }
+template <> DIT_DEV bf16_t cvt_out<bf16_t>(float v) { return f2bf(v); }
+// the value a store of type T keeps
+template <typename T> DIT_DEV float stored(float v);
+template <> DIT_DEV float stored<float>(float v) { return v; }
+template <> DIT_DEV float stored<bf16_t>(float v) { return bf2f(f2bf(v)); }
+
+DIT_DEV float epi_scale(const float* amax_a, const float* s_w) {
+    if (!amax_a) return 1.f;
+    float a = *amax_a;
+    float sa = a > 0.f ? a / 448.f : 1.f;
+    return sa * (*s_w);
+}
+
+// m: token row, n0: first of four consecutive output features (n0 % 4 == 0)
+template <typename T>
+DIT_DEV void epi_qkv(const EpiParams& p, int m, int n0, float v[4], float sc) {
+    if (m >= p.Mpad) return;
+    const int which = n0 / p.I;
+    const int rem = n0 - which * p.I;
+    const int head = rem / p.dh;
+    const int d0 = rem - head * p.dh;
+    if (m >= p.M) {
+        v[0] = v[1] = v[2] = v[3] = 0.f;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] *= sc;
+        if (which < 2) {
+            const int3 c = rope_coords(p.rope, m);
+#pragma unroll
+            for (int j = 0; j < 4; j += 2) {
+                float2 cs = rope_cs(p.rope, d0 + j, c);
+                float a = v[j], b = v[j + 1];
+                v[j] = a * cs.x - b * cs.y;
+                v[j + 1] = a * cs.y + b * cs.x;
+            }
+            if (which == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] *= p.qscale;
+            }
+        }
+    }
+    if (which == 0) {
+        store4<T>((T*)p.q + ((size_t)head * p.Sp + m) * p.dh + d0, v);
+    } else if (which == 1) {
+        store4<T>((T*)p.k + ((size_t)head * p.Sp + m) * p.dh + d0, v);
+    } else {
+        T* vt = (T*)p.vt + ((size_t)head * p.dh + d0) * p.Sp + m;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vt[(size_t)i * p.Sp] = cvt_out<T>(v[i]);
+    }
+}
+
+template <typename T>
+DIT_DEV void epi_resid(const EpiParams& p, int m, int n0, float v[4], float sc) {
+    if (m >= p.M) return;
+    float x[4];
+    load4<T>(seq_row<T>(p.xin, m, p.D) + n0, x);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] += v[i] * sc;
+    store4<float>(p.h + (size_t)m * p.D + n0, x);
+}
+
+// gate / up for ffn features f0..f0+3
+template <typename T>
+DIT_DEV float epi_swiglu(const EpiParams& p, int m, int f0, const float g[4], const float up[4], float sg, float su) {
+    if (m >= p.M) return 0.f;
+    float o[4];
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float z = g[i] * sg;
+        o[i] = z / (1.f + __expf(-z)) * (up[i] * su);
+    }
+    store4<T>((T*)p.u + (size_t)m * p.F + f0, o);
+    if (p.u_amax) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(stored<T>(o[i])));  // max of the stored values
+    }
+    return mx;
+}
+
+template <typename T>
+DIT_DEV void epi_down(const EpiParams& p, int m, int n0, float v[4], float sc) {
+    if (m >= p.M) return;
+    float y[4];
+    load4<float>(p.hres + (size_t)m * p.D + n0, y);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] += v[i] * sc;
+    const SeqOut& o = p.out;
+    const int nt = p.xin.nt, nv = p.xin.nv;
+    if (m < nt) {
+        store4<T>((T*)o.yt + (size_t)m * p.D + n0, y);
+    } else if (m < nt + nv) {
+        const int j = m - nt;
+        if (o.delta) {
+            float x[4];
+            load4<T>(seq_row<T>(p.refin, m, p.D) + n0, x);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] -= x[i];
+            store4<float>(o.delta + (size_t)j * p.D + n0, y);
+        } else {
+            store4<T>((T*)o.yv + (size_t)j * p.D + n0, y);
+        }
+    } else {
+        store4<T>((T*)o.ya + (size_t)(m - nt - nv) * p.D + n0, y);
+    }
+}
+
+// Compile-time loop: f(integral_constant<int, i>) for i = 0 .. N-1, so that
+// register arrays are only ever indexed by constants.
+template <int N, int I = 0, class F>
+DIT_DEV void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
+}
+
+// One 32x32 MFMA accumulator block of a lane: token m, features
+// nb + 8 g + 4 h + {0..3} in registers 4 g .. 4 g + 3 (g = 0..3, h = lane / 32).
+template <int MODE, typename T>
+DIT_DEV void epi_block(const EpiParams& p, int m, int nb, int h, const f32x16& acc, float sc) {
+    static_for<4>([&](auto g) {
+        float v[4] = {acc[4 * g + 0], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+        const int n0 = nb + 8 * g + 4 * h;
+        if constexpr (MODE == EPI_QKV) epi_qkv<T>(p, m, n0, v, sc);
+        else if constexpr (MODE == EPI_RESID) epi_resid<T>(p, m, n0, v, sc);
+        else epi_down<T>(p, m, n0, v, sc);
+    });
+}
+
+// SwiGLU: gate block and up block of the same ffn features fb + 8 g + 4 h + {0..3}
+template <typename T>
+DIT_DEV float epi_block_swiglu(const EpiParams& p, int m, int fb, int h, const f32x16& gacc, const f32x16& uacc,
+                               float sg, float su) {
+    float mx = 0.f;
+    static_for<4>([&](auto g) {
+        float gv[4] = {gacc[4 * g + 0], gacc[4 * g + 1], gacc[4 * g + 2], gacc[4 * g + 3]};
+        float uv[4] = {uacc[4 * g + 0], uacc[4 * g + 1], uacc[4 * g + 2], uacc[4 * g + 3]};
+        mx = fmaxf(mx, epi_swiglu<T>(p, m, fb + 8 * g + 4 * h, gv, uv, sg, su));
+    });
+    return mx;
+}
+
+}  // namespace dit

@@ -1,0 +1,41 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <algorithm>
+
+#include "common.h"
+
+namespace dit {
+
+struct EpiParams;
+
+hipError_t keep_index_launch(int T, int H, int W, int s, int Hk, int Wk, int32_t* keep, hipStream_t st);
+hipError_t nearest_map_launch(int T, int H, int W, int s, int Hk, int Wk, int32_t* nk, hipStream_t st);
+hipError_t rope_tables_launch(float2* tab, int n_t, int rt, int n_h, int rh, int n_w, int rw, double base,
+                              hipStream_t st);
+hipError_t rmsnorm_launch(int act, bool seq_input, const SeqIn& seq, const float* dense, const void* g, void* out,
+                          int M, int D, float eps, hipStream_t st);
+hipError_t rmsnorm_fp8_launch(bool seq_input, const SeqIn& seq, const float* dense, const void* g, uint8_t* out,
+                              float* rinv, float* amax, int M, int D, float eps, hipStream_t st);
+hipError_t fill_launch(float* p, int n, float v, hipStream_t st);
+hipError_t quant_launch(bool bf16, const void* src, uint8_t* dst, const float* amax, size_t n, hipStream_t st);
+hipError_t amax_launch(bool bf16, const void* src, size_t n, float* amax, hipStream_t st);
+hipError_t amax_to_scale_launch(float* p, hipStream_t st);
+hipError_t gather_rows_launch(const void* x, const int32_t* idx, void* out, int n, size_t rowbytes, hipStream_t st);
+hipError_t broadcast_residual_launch(bool bf16, const void* x, const float* delta, const int32_t* nk, void* out,
+                                     int n_video, int D, hipStream_t st);
+hipError_t euler_launch(bool bf16, void* x, const void* v, size_t n, float dt, hipStream_t st);
+
+hipError_t gemm_mfma(bool fp8, int mode, const void* A, const void* W0, const void* W1, int M, int N, int K,
+                     const EpiParams& ep, hipStream_t st);
+hipError_t gemm_f32(int mode, const void* A, const void* W0, const void* W1, int M, int N, int K, const EpiParams& ep,
+                    hipStream_t st);
+
+hipError_t attention_bf16(const void* Q, const void* K, const void* Vt, void* O, int S, int Sp, int nh, int dh,
+                          float* o_amax, hipStream_t st);
+hipError_t attention_f32(const void* Q, const void* K, const void* Vt, void* O, int S, int Sp, int nh, int dh,
+                         hipStream_t st);
+hipError_t attention_pack(bool bf16, const void* q, const void* k, const void* v, void* Qp, void* Kp, void* Vtp,
+                          int S, int Sp, int nh, int dh, float qscale, hipStream_t st);
+
+}  // namespace dit

@@ -1,0 +1,342 @@
+// Bandwidth-bound row kernels of the Flash DiT block for gfx950: index maps of
+// the spatial token compression, rotary tables, RMSNorm (+ e4m3 activation
+// quantisation), kept-row gather, nearest-kept update broadcast with the
+// full-resolution residual, Euler update, fp8 weight quantisation.
+#include "common.h"
+#include "kernels.h"
+
+namespace dit {
+
+namespace detail {
+
+// ----------------------------------------------------------------- compression index maps
+// Kept indices along an axis of length n at stride s (PaperDaily review,
+// section 2; tokendh.com article, training section): multiples of s plus the
+// last index. Rank a -> index min(a*s, n-1). Nearest kept index to r (ties
+// to the lower): the multiple L = floor(r/s)*s below r or the next kept index
+// U = min(L + s, n - 1) above it.
+DIT_DEV int kept_at(int a, int n, int s) { return min(a * s, n - 1); }
+DIT_DEV int kept_rank(int k, int n, int s, int nk) { return k == n - 1 ? nk - 1 : k / s; }
+DIT_DEV int nearest_kept(int r, int n, int s) {
+    const int L = (r / s) * s;
+    if (L == r) return r;
+    const int U = min(L + s, n - 1);
+    return (r - L <= U - r) ? L : U;
+}
+
+__global__ void keep_index_kernel(int T, int H, int W, int s, int Hk, int Wk, int32_t* keep) {
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= T * Hk * Wk) return;
+    const int t = j / (Hk * Wk);
+    const int r = j - t * Hk * Wk;
+    const int a = r / Wk, b = r - (r / Wk) * Wk;
+    keep[j] = t * H * W + kept_at(a, H, s) * W + kept_at(b, W, s);
+}
+
+__global__ void nearest_map_kernel(int T, int H, int W, int s, int Hk, int Wk, int32_t* nk) {
+    const int p = blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= T * H * W) return;
+    const int t = p / (H * W);
+    const int r = p - t * H * W;
+    const int h = r / W, w = r - (r / W) * W;
+    const int rh = kept_rank(nearest_kept(h, H, s), H, s, Hk);
+    const int rw = kept_rank(nearest_kept(w, W, s), W, s, Wk);
+    nk[p] = t * Hk * Wk + rh * Wk + rw;
+}
+
+// ----------------------------------------------------------------- rotary tables
+// (cos, sin) of pos * base^(-2i/width) in fp64, stored fp32; three bands back to back.
+__global__ void rope_table_kernel(float2* tab, int n_t, int rt, int n_h, int rh, int n_w, int rw, double base) {
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    const int et = n_t * (rt / 2), eh = n_h * (rh / 2), ew = n_w * (rw / 2);
+    if (e >= et + eh + ew) return;
+    int pos, i, width;
+    if (e < et) { pos = e / (rt / 2); i = e % (rt / 2); width = rt; }
+    else if (e < et + eh) { int x = e - et; pos = x / (rh / 2); i = x % (rh / 2); width = rh; }
+    else { int x = e - et - eh; pos = x / (rw / 2); i = x % (rw / 2); width = rw; }
+    const double theta = pow(base, -2.0 * i / (double)width);
+    const double ang = (double)pos * theta;
+    tab[e] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+// ----------------------------------------------------------------- RMSNorm
+template <typename T> DIT_DEV void ld4(const T* p, float v[4]);
+template <> DIT_DEV void ld4<float>(const float* p, float v[4]) {
+    float4 x = *(const float4*)p;
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+}
+template <> DIT_DEV void ld4<bf16_t>(const bf16_t* p, float v[4]) {
+    uint2 x = *(const uint2*)p;
+    v[0] = __uint_as_float(x.x << 16); v[1] = __uint_as_float(x.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(x.y << 16); v[3] = __uint_as_float(x.y & 0xFFFF0000u);
+}
+template <typename T> DIT_DEV void st4(T* p, const float v[4]);
+template <> DIT_DEV void st4<float>(float* p, const float v[4]) { *(float4*)p = make_float4(v[0], v[1], v[2], v[3]); }
+template <> DIT_DEV void st4<bf16_t>(bf16_t* p, const float v[4]) {
+    *(uint2*)p = make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
+}
+
+// One wave per row: n = x / sqrt(mean(x^2) + eps) * g. Input rows come from
+// the joint-sequence segments (SEQ) or from a dense fp32 [M][D] tensor.
+// MODE 0: write n (TO). MODE 1: only the row factor rinv[m] and the tensor's
+// max |n| (atomic). MODE 2: write e4m3 codes of n * 448 / amax.
+template <typename TI, typename TG, typename TO, bool SEQ, int MODE>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(SeqIn seq, const float* __restrict__ dense,
+                                                      const TG* __restrict__ g, TO* __restrict__ out,
+                                                      float* __restrict__ rinv, float* __restrict__ amax, int M,
+                                                      int D, float eps) {
+    const int lane = threadIdx.x & 63;
+    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (m >= M) return;
+    const TI* x = SEQ ? seq_row<TI>(seq, m, D) : (const TI*)(dense + (size_t)m * D);
+    float r;
+    if (MODE == 2) {
+        r = rinv[m];
+    } else {
+        float ss = 0.f;
+        for (int c = lane * 4; c < D; c += 256) {
+            float v[4];
+            ld4<TI>(x + c, v);
+            ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+        }
+        ss = wave_sum(ss);
+        r = 1.f / sqrtf(ss / (float)D + eps);
+    }
+    float mx = 0.f;
+    float qs = 1.f;
+    if (MODE == 2) {
+        const float a = *amax;
+        qs = a > 0.f ? 448.f / a : 1.f;
+    }
+    for (int c = lane * 4; c < D; c += 256) {
+        float v[4], gv[4];
+        ld4<TI>(x + c, v);
+        ld4<TG>(g + c, gv);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = v[i] * r * gv[i];
+        if constexpr (MODE == 0) {
+            st4<TO>(out + (size_t)m * D + c, v);
+        } else if constexpr (MODE == 1) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(v[i]));
+        } else {
+            uint32_t w = f32_to_e4m3(v[0] * qs) | (f32_to_e4m3(v[1] * qs) << 8) | (f32_to_e4m3(v[2] * qs) << 16) |
+                         (f32_to_e4m3(v[3] * qs) << 24);
+            *(uint32_t*)((uint8_t*)out + (size_t)m * D + c) = w;
+        }
+    }
+    if (MODE == 1) {
+        if (lane == 0) rinv[m] = r;
+        mx = wave_max(mx);
+        if (lane == 0) atomic_max_nonneg(amax, mx);
+    }
+}
+
+// ----------------------------------------------------------------- quantisation
+// e4m3 codes of src * 448 / amax for a bf16 / fp32 tensor (amax on the device)
+template <typename T>
+__global__ void quant_kernel(const T* __restrict__ src, uint8_t* __restrict__ dst, const float* __restrict__ amax,
+                             size_t n4) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n4) return;
+    const float a = *amax;
+    const float qs = a > 0.f ? __fdiv_rn(448.f, a) : 1.f;
+    float v[4];
+    ld4<T>(src + 4 * i, v);
+    uint32_t w = f32_to_e4m3(v[0] * qs) | (f32_to_e4m3(v[1] * qs) << 8) | (f32_to_e4m3(v[2] * qs) << 16) |
+                 (f32_to_e4m3(v[3] * qs) << 24);
+    ((uint32_t*)dst)[i] = w;
+}
+
+template <typename T>
+__global__ void amax_kernel(const T* __restrict__ src, size_t n4, float* amax) {
+    float mx = 0.f;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x) {
+        float v[4];
+        ld4<T>(src + 4 * i, v);
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+    }
+    mx = wave_max(mx);
+    if ((threadIdx.x & 63) == 0) atomic_max_nonneg(amax, mx);
+}
+
+__global__ void fill_kernel(float* p, int n, float v) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// scale = amax / 448 (amax 0 -> 1), in place
+__global__ void amax_to_scale_kernel(float* p) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
+        const float a = *p;
+        *p = a > 0.f ? __fdiv_rn(a, 448.f) : 1.f;
+    }
+}
+
+// ----------------------------------------------------------------- gather / broadcast
+// out[j] = x[idx[j]], rows of `rowbytes` (multiple of 16)
+__global__ void gather_rows_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__ idx,
+                                   uint8_t* __restrict__ out, int n, int chunks) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (size_t)n * chunks) return;
+    const int j = (int)(i / chunks);
+    const int c = (int)(i - (size_t)j * chunks);
+    const int src = idx[j];
+    ((uint4*)out)[(size_t)j * chunks + c] = ((const uint4*)x)[(size_t)src * chunks + c];
+}
+
+// out[p] = x[p] + delta[nk[p]]: 8 elements per thread
+template <typename T>
+__global__ void broadcast_residual_kernel(const T* __restrict__ x, const float* __restrict__ delta,
+                                          const int32_t* __restrict__ nk, T* __restrict__ out, int n_video, int D) {
+    const int per_row = D / 8;
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (size_t)n_video * per_row) return;
+    const int p = (int)(i / per_row);
+    const int c = (int)(i - (size_t)p * per_row) * 8;
+    const float* d = delta + (size_t)nk[p] * D + c;
+    const float4 d0 = *(const float4*)d, d1 = *(const float4*)(d + 4);
+    float a[4], b[4];
+    ld4<T>(x + (size_t)p * D + c, a);
+    ld4<T>(x + (size_t)p * D + c + 4, b);
+    a[0] += d0.x; a[1] += d0.y; a[2] += d0.z; a[3] += d0.w;
+    b[0] += d1.x; b[1] += d1.y; b[2] += d1.z; b[3] += d1.w;
+    st4<T>(out + (size_t)p * D + c, a);
+    st4<T>(out + (size_t)p * D + c + 4, b);
+}
+
+// x += dt * v (4 elements per thread)
+template <typename T>
+__global__ void euler_kernel(T* __restrict__ x, const T* __restrict__ v, size_t n4, float dt) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n4) return;
+    float a[4], b[4];
+    ld4<T>(x + 4 * i, a);
+    ld4<T>(v + 4 * i, b);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] += dt * b[k];
+    st4<T>(x + 4 * i, a);
+}
+
+inline unsigned nblk(size_t n, unsigned b = 256) { return (unsigned)((n + b - 1) / b); }
+
+}  // namespace detail
+using namespace detail;
+
+hipError_t keep_index_launch(int T, int H, int W, int s, int Hk, int Wk, int32_t* keep, hipStream_t st) {
+    const int n = T * Hk * Wk;
+    hipLaunchKernelGGL(keep_index_kernel, dim3(nblk(n)), dim3(256), 0, st, T, H, W, s, Hk, Wk, keep);
+    return hipGetLastError();
+}
+
+hipError_t nearest_map_launch(int T, int H, int W, int s, int Hk, int Wk, int32_t* nk, hipStream_t st) {
+    const int n = T * H * W;
+    hipLaunchKernelGGL(nearest_map_kernel, dim3(nblk(n)), dim3(256), 0, st, T, H, W, s, Hk, Wk, nk);
+    return hipGetLastError();
+}
+
+hipError_t rope_tables_launch(float2* tab, int n_t, int rt, int n_h, int rh, int n_w, int rw, double base,
+                              hipStream_t st) {
+    const int n = n_t * (rt / 2) + n_h * (rh / 2) + n_w * (rw / 2);
+    hipLaunchKernelGGL(rope_table_kernel, dim3(nblk(n)), dim3(256), 0, st, tab, n_t, rt, n_h, rh, n_w, rw, base);
+    return hipGetLastError();
+}
+
+hipError_t rmsnorm_launch(int act, bool seq_input, const SeqIn& seq, const float* dense, const void* g, void* out,
+                          int M, int D, float eps, hipStream_t st) {
+    const dim3 grid(nblk(M, 4)), block(256);
+    if (act == DIT_F32) {
+        if (seq_input)
+            hipLaunchKernelGGL((rmsnorm_kernel<float, float, float, true, 0>), grid, block, 0, st, seq, dense,
+                               (const float*)g, (float*)out, (float*)nullptr, (float*)nullptr, M, D, eps);
+        else
+            hipLaunchKernelGGL((rmsnorm_kernel<float, float, float, false, 0>), grid, block, 0, st, seq, dense,
+                               (const float*)g, (float*)out, (float*)nullptr, (float*)nullptr, M, D, eps);
+    } else {
+        if (seq_input)
+            hipLaunchKernelGGL((rmsnorm_kernel<bf16_t, bf16_t, bf16_t, true, 0>), grid, block, 0, st, seq, dense,
+                               (const bf16_t*)g, (bf16_t*)out, (float*)nullptr, (float*)nullptr, M, D, eps);
+        else
+            hipLaunchKernelGGL((rmsnorm_kernel<float, bf16_t, bf16_t, false, 0>), grid, block, 0, st, seq, dense,
+                               (const bf16_t*)g, (bf16_t*)out, (float*)nullptr, (float*)nullptr, M, D, eps);
+    }
+    return hipGetLastError();
+}
+
+// bf16 activations, fp8 output: stats pass (rinv, amax) then quantise pass
+hipError_t rmsnorm_fp8_launch(bool seq_input, const SeqIn& seq, const float* dense, const void* g, uint8_t* out,
+                              float* rinv, float* amax, int M, int D, float eps, hipStream_t st) {
+    const dim3 grid(nblk(M, 4)), block(256);
+    hipLaunchKernelGGL(fill_kernel, dim3(1), dim3(64), 0, st, amax, 1, 0.f);
+    if (seq_input) {
+        hipLaunchKernelGGL((rmsnorm_kernel<bf16_t, bf16_t, uint8_t, true, 1>), grid, block, 0, st, seq, dense,
+                           (const bf16_t*)g, out, rinv, amax, M, D, eps);
+        hipLaunchKernelGGL((rmsnorm_kernel<bf16_t, bf16_t, uint8_t, true, 2>), grid, block, 0, st, seq, dense,
+                           (const bf16_t*)g, out, rinv, amax, M, D, eps);
+    } else {
+        hipLaunchKernelGGL((rmsnorm_kernel<float, bf16_t, uint8_t, false, 1>), grid, block, 0, st, seq, dense,
+                           (const bf16_t*)g, out, rinv, amax, M, D, eps);
+        hipLaunchKernelGGL((rmsnorm_kernel<float, bf16_t, uint8_t, false, 2>), grid, block, 0, st, seq, dense,
+                           (const bf16_t*)g, out, rinv, amax, M, D, eps);
+    }
+    return hipGetLastError();
+}
+
+hipError_t fill_launch(float* p, int n, float v, hipStream_t st) {
+    hipLaunchKernelGGL(fill_kernel, dim3(nblk(n)), dim3(256), 0, st, p, n, v);
+    return hipGetLastError();
+}
+
+hipError_t quant_launch(bool bf16, const void* src, uint8_t* dst, const float* amax, size_t n, hipStream_t st) {
+    const size_t n4 = n / 4;
+    if (bf16)
+        hipLaunchKernelGGL(quant_kernel<bf16_t>, dim3(nblk(n4)), dim3(256), 0, st, (const bf16_t*)src, dst, amax, n4);
+    else
+        hipLaunchKernelGGL(quant_kernel<float>, dim3(nblk(n4)), dim3(256), 0, st, (const float*)src, dst, amax, n4);
+    return hipGetLastError();
+}
+
+hipError_t amax_launch(bool bf16, const void* src, size_t n, float* amax, hipStream_t st) {
+    const size_t n4 = n / 4;
+    const unsigned blocks = (unsigned)std::min<size_t>(nblk(n4), 4096);
+    if (bf16)
+        hipLaunchKernelGGL(amax_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st, (const bf16_t*)src, n4, amax);
+    else
+        hipLaunchKernelGGL(amax_kernel<float>, dim3(blocks), dim3(256), 0, st, (const float*)src, n4, amax);
+    return hipGetLastError();
+}
+
+hipError_t amax_to_scale_launch(float* p, hipStream_t st) {
+    hipLaunchKernelGGL(amax_to_scale_kernel, dim3(1), dim3(64), 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t gather_rows_launch(const void* x, const int32_t* idx, void* out, int n, size_t rowbytes, hipStream_t st) {
+    const int chunks = (int)(rowbytes / 16);
+    hipLaunchKernelGGL(gather_rows_kernel, dim3(nblk((size_t)n * chunks)), dim3(256), 0, st, (const uint8_t*)x, idx,
+                       (uint8_t*)out, n, chunks);
+    return hipGetLastError();
+}
+
+hipError_t broadcast_residual_launch(bool bf16, const void* x, const float* delta, const int32_t* nk, void* out,
+                                     int n_video, int D, hipStream_t st) {
+    const size_t n = (size_t)n_video * (D / 8);
+    if (bf16)
+        hipLaunchKernelGGL(broadcast_residual_kernel<bf16_t>, dim3(nblk(n)), dim3(256), 0, st, (const bf16_t*)x, delta,
+                           nk, (bf16_t*)out, n_video, D);
+    else
+        hipLaunchKernelGGL(broadcast_residual_kernel<float>, dim3(nblk(n)), dim3(256), 0, st, (const float*)x, delta,
+                           nk, (float*)out, n_video, D);
+    return hipGetLastError();
+}
+
+hipError_t euler_launch(bool bf16, void* x, const void* v, size_t n, float dt, hipStream_t st) {
+    const size_t n4 = n / 4;
+    if (bf16)
+        hipLaunchKernelGGL(euler_kernel<bf16_t>, dim3(nblk(n4)), dim3(256), 0, st, (bf16_t*)x, (const bf16_t*)v, n4, dt);
+    else
+        hipLaunchKernelGGL(euler_kernel<float>, dim3(nblk(n4)), dim3(256), 0, st, (float*)x, (const float*)v, n4, dt);
+    return hipGetLastError();
+}
+
+}  // namespace dit
