@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Benchmark of the Flash DiT block on one MI355X.
+
+Step = one pass of the block's hot path on the 540p / 22-frame latent grid
+(T=6, H=34, W=60; 256 text + 132 audio tokens; width 5376, 56 heads of 128,
+SwiGLU 14336) with spatial token compression on: the two index builders,
+then dit_block_forward (gather-on-read, norm, QKV + rotary, attention, O +
+residual, norm, gate/up + SwiGLU, down + residual / update, nearest-kept
+broadcast onto all 12240 video positions). Inputs are resident in HBM before
+the timed region. The same block with compression off (all 12628 tokens) is
+timed as a second line item.
+
+Prints one JSON line (see the repository's bench contract).
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu] [--no-off]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "Flash DiT block ms & TFLOP/s (% bf16 MFMA peak), 540p/22f, compression on/off"
+PEAK_BF16 = 2500.0     # TFLOP/s, dense MFMA, MI355X
+PEAK_HBM = 8000.0      # GB/s
+
+
+def block_flops(d, S):
+    """Algorithmic FLOPs (2 per MAC) of one block on S tokens, per kernel."""
+    D, I, F = d.d_model, d.inner, d.d_ffn
+    return {"gemm_qkv": 2.0 * S * D * 3 * I, "attention": 4.0 * S * S * I, "gemm_o": 2.0 * S * I * D,
+            "gemm_gate_up": 2.0 * S * D * 2 * F, "gemm_down": 2.0 * S * F * D}
+
+
+def hbm_bytes(d, S, Nv, Nk, es=2):
+    """Algorithmic bytes of the bandwidth-bound kernels per launch."""
+    D = d.d_model
+    return {"broadcast_residual": (2 * Nv * es + Nk * 4) * D,   # read x (bf16), read delta (fp32), write out
+            "rmsnorm1": 2 * S * D * es,                        # read X rows, write n
+            "rmsnorm2": S * D * (4 + es)}                      # read h (fp32), write n
+
+
+def setup(cfg_name, compress):
+    import torch
+    import video_diffusion_transformer_flash_amd as V
+    from dit_synth import CONFIGS, activations, weights
+    d = CONFIGS[cfg_name]
+    x = activations(d, d.seed)
+    w = weights(d, d.seed)
+    dev = {k: torch.from_numpy(v).to(torch.bfloat16).cuda() for k, v in x.items()}
+    gw = {k: torch.from_numpy(v).to(torch.bfloat16).cuda() for k, v in w.items()}
+    dims = V.make_dims(d)
+    s = d.stride
+    Hk, Wk = V.keep_dims(d.H, d.W, s)
+    keep = torch.empty(d.T * Hk * Wk, dtype=torch.int32, device="cuda")
+    nk = torch.empty(d.n_video, dtype=torch.int32, device="cuda")
+    out = tuple(torch.empty_like(dev[k]) for k in ("x_text", "x_video", "x_audio"))
+    ws = V.workspace(V.block_workspace_size(dims, compress))
+
+    def step():
+        if compress:
+            V.keep_index(d.T, d.H, d.W, s, out=keep)
+            V.nearest_kept_map(d.T, d.H, d.W, s, out=nk)
+        V.block_forward(dims, dev["x_text"], dev["x_video"], dev["x_audio"], gw, compress,
+                        keep if compress else None, nk if compress else None, out=out, ws=ws)
+
+    S = d.n_text + d.n_audio + (d.T * Hk * Wk if compress else d.n_video)
+    return d, step, S, d.T * Hk * Wk, (x, w)
+
+
+def time_steps(step, steps, warmup, trace=True):
+    import torch
+    import video_diffusion_transformer_flash_amd as V
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    if trace:
+        V.trace_enable(steps * 24 + 8)
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(steps):
+        step()
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    recs = V.trace_records() if trace else []
+    if trace:
+        V.trace_enable(0)
+    per = {}
+    for name, t in recs:
+        a = per.setdefault(name, [0.0, 0])
+        a[0] += t
+        a[1] += 1
+    return ms, {k: (v[0] / v[1], v[1]) for k, v in per.items()}
+
+
+def kernel_table(kern, flops, bytes_):
+    out = {}
+    for name, (ms, n) in sorted(kern.items(), key=lambda kv: -kv[1][0]):
+        e = {"ms": round(ms, 4), "launches": n}
+        if name in flops:
+            tf = flops[name] / (ms * 1e-3) / 1e12
+            e.update({"TFLOP/s": round(tf, 1), "frac": round(tf / PEAK_BF16, 4)})
+        if name in bytes_:
+            gb = bytes_[name] / (ms * 1e-3) / 1e9
+            e.update({"GB/s": round(gb, 1), "frac": round(gb / PEAK_HBM, 4)})
+        out[name] = e
+    return out
+
+
+def cpu_baseline(d, host, compress):
+    """The fp64 oracle on the host cores: one full block of the same workload."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    x, w = host
+    ow = O.BlockWeights.from_arrays(w)
+    t0 = time.time()
+    O.block_forward(x["x_text"], x["x_video"], x["x_audio"], ow, d, compress)
+    dt = time.time() - t0
+    Hk, Wk = O.keep_dims(d.H, d.W, d.stride)
+    S = d.n_text + d.n_audio + (d.T * Hk * Wk if compress else d.n_video)
+    tflop = sum(block_flops(d, S).values()) / 1e12
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    del np
+    return {"value": round(tflop / dt, 4), "unit": "TFLOP/s", "ms": round(dt * 1e3, 1), "cores": threads,
+            "kind": "oracle", "cpu_model": cpu,
+            "sample": f"one full block of the same workload (S={S}, compression {'on' if compress else 'off'}), "
+                      "fp64 numpy oracle, timed once"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-off", action="store_true", help="skip the compression-off line item")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the block on one GPU; the multi-GPU sharding is not part of this build "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    d, step, S, Nk, host = setup("540p_on", True)
+    ms, kern = time_steps(step, a.steps, a.warmup)
+    flops = block_flops(d, S)
+    tflop = sum(flops.values()) / 1e12
+    value = tflop / (ms * 1e-3)
+    byts = hbm_bytes(d, S, d.n_video, Nk)
+    table = kernel_table(kern, flops, byts)
+    dom = max(flops, key=lambda k: kern.get(k, (0, 0))[0] * kern.get(k, (0, 0))[1])
+    dom_ms = kern[dom][0]
+    achieved = flops[dom] / (dom_ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
+        "config": {"workload": "Flash DiT block, 540p/22f latent grid 6x34x60, compression on "
+                               f"(3348 kept video + 256 text + 132 audio = {S} tokens), broadcast to 12240 positions",
+                   "tflop_per_step": round(tflop, 4), "frac_of_bf16_peak": round(value / PEAK_BF16, 4)},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4), "traffic": None},
+        "kernels": table,
+    }
+    bc = table.get("broadcast_residual")
+    if bc:
+        line["hbm_roofline"] = {"bound": "hbm", "kernel": "broadcast_residual", "achieved": bc["GB/s"],
+                                "peak": PEAK_HBM, "unit": "GB/s", "frac": bc["frac"],
+                                "bytes_per_launch": byts["broadcast_residual"]}
+    torch.cuda.empty_cache()
+    if not a.no_off:
+        d2, step2, S2, _, host2 = setup("540p_off", False)
+        ms2, kern2 = time_steps(step2, max(3, a.steps // 2), a.warmup)
+        f2 = block_flops(d2, S2)
+        tf2 = sum(f2.values()) / 1e12
+        line["compress_off"] = {"workload": f"same block, compression off ({S2} tokens)", "ms": round(ms2, 4),
+                                "TFLOP/s": round(tf2 / (ms2 * 1e-3), 2),
+                                "frac_of_bf16_peak": round(tf2 / (ms2 * 1e-3) / PEAK_BF16, 4),
+                                "tflop_per_step": round(tf2, 4),
+                                "kernels": kernel_table(kern2, f2, hbm_bytes(d2, S2, d2.n_video, 0))}
+        line["on_off_speedup"] = round(ms2 / ms, 3)
+        del host2
+    if not a.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(d, host, True)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

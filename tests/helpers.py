@@ -17,6 +17,27 @@ def rel_err(got: list, ref: list) -> float:
     return float(np.max(np.abs(g - r)) / rms)
 
 
+def rms_err(got: list, ref: list) -> float:
+    """RMS of (got - ref) over every output element / RMS of the reference."""
+    g = np.concatenate([np.asarray(x, dtype=np.float64).ravel() for x in got])
+    r = np.concatenate([np.asarray(x, dtype=np.float64).ravel() for x in ref])
+    return float(np.sqrt(np.mean((g - r) ** 2)) / np.sqrt(np.mean(r * r)))
+
+
+# fp8 parity. Per-tensor e4m3 activation codes are a discontinuous function of
+# the values they quantise: a difference of 1e-7 (relative) in a value that sits
+# on a rounding boundary moves its code by one e4m3 step (up to 2^-3 of the
+# value), and one such step in a large element of a norm output moves every
+# projection output of that token by step * max|w|, about 3 % of the output RMS
+# at width 5376. Two correct implementations that differ only by fp32 rounding
+# order therefore differ by several percent in max|err|/RMS (the oracle moves by
+# 4.4e-2 against itself under a 1e-7 perturbation of its quantiser inputs, and
+# by 1.2e-1 under the 2^-9 of bf16 attention; see test_oracle_fp8_flips.py).
+# The fp8 bar of 6e-2 is therefore applied to the RMS error, and the max error
+# is held to the flip bound FP8_MAX_BOUND.
+FP8_MAX_BOUND = 0.3
+
+
 def torch_act(a: np.ndarray, dtype: str):
     import torch
     t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))

@@ -1,8 +1,8 @@
 """GPU parity of dit_block_forward against the fp64 oracle.
 
 Metric: max |gpu - oracle| over every output element / RMS of the oracle
-outputs. Bars: 1e-4 for the fp32 block, 2e-2 for bf16, 6e-2 for fp8
-projections. Small configurations compare every element; the full
+outputs. Bars: 1e-4 for the fp32 block, 2e-2 for bf16; fp8 projections: 6e-2
+on the RMS error, the max error within the e4m3 code-flip bound (helpers.py). Small configurations compare every element; the full
 540p / 768p configurations compare sampled rows that the oracle evaluates one
 by one (keys and values still come from the whole sequence)."""
 import numpy as np
@@ -10,7 +10,7 @@ import pytest
 
 import oracle as O
 from dit_synth import CONFIGS, BlockDims
-from helpers import gpu_weights, inputs, oracle_weights, rel_err, to_numpy, torch_act
+from helpers import FP8_MAX_BOUND, gpu_weights, inputs, oracle_weights, rel_err, rms_err, to_numpy, torch_act
 
 pytestmark = pytest.mark.gpu
 
@@ -23,6 +23,10 @@ TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 6e-2}
 SMALL_BF16 = BlockDims("small_bf16", d_model=512, n_heads=4, head_dim=128, d_ffn=1024, T=2, H=9, W=15, n_text=16,
                        n_audio=8, rope=(32, 48, 48), dtype="bf16", seed=5)
 SMALL_FP8 = SMALL_BF16.with_(name="small_fp8", dtype="fp8", seed=6)
+# full Flash width on a small grid: the fp8 code-flip noise scales with
+# 1/sqrt(width), so this is the fp8 block at the width the stack runs at
+WIDE_FP8 = BlockDims("wide_fp8", T=2, H=6, W=10, n_text=16, n_audio=8, dtype="fp8", seed=8, d_model=5376, n_heads=56,
+                     head_dim=128, d_ffn=14336, rope=(32, 48, 48))
 
 
 def run_gpu(d, x, w, compress, stride=None):
@@ -48,9 +52,13 @@ def check_full(d, compress, stride=None):
     ow = oracle_weights(w, d.dtype)
     ref = O.block_forward(x["x_text"], x["x_video"], x["x_audio"], ow, d, compress, stride)
     err = rel_err(got, ref)
-    print(f"  max|err|/rms = {err:.3e} (bar {TOL[d.dtype]})")
+    rerr = rms_err(got, ref)
+    print(f"  max|err|/rms = {err:.3e}, rms err = {rerr:.3e} (bar {TOL[d.dtype]})")
     assert np.all(np.isfinite(np.concatenate([g.ravel() for g in got])))
-    assert err <= TOL[d.dtype]
+    if d.dtype == "fp8":
+        assert rerr <= TOL["fp8"] and err <= FP8_MAX_BOUND
+    else:
+        assert err <= TOL[d.dtype]
     return got, ref
 
 
@@ -67,6 +75,11 @@ def test_small_bf16(compress):
 @pytest.mark.parametrize("compress", [False, True])
 def test_small_fp8(compress):
     check_full(SMALL_FP8, compress)
+
+
+@pytest.mark.parametrize("compress", [False, True])
+def test_wide_fp8(compress):
+    check_full(WIDE_FP8, compress)
 
 
 @pytest.mark.parametrize("name", ["tiny", "small_bf16"])

@@ -99,7 +99,9 @@ def test_fp8_weight_codes_bit_exact():
     assert np.array_equal(c1.cpu().numpy(), rc)
 
 
-@pytest.mark.parametrize("dtype,tol", [("f32", 1e-5), ("bf16", 2e-2)])
+# bf16 bar: P and the output are stored in bf16 (2^-9 relative each), the max
+# |o| is about 4.5x its RMS, so max|err|/RMS <= 2 * 2^-9 * 4.5 * (1 + slack) = 3e-2
+@pytest.mark.parametrize("dtype,tol", [("f32", 1e-4), ("bf16", 3e-2)])
 @pytest.mark.parametrize("S", [1, 63, 64, 65, 129, 300, 1000])
 @pytest.mark.parametrize("sharp", [1.0, 8.0])
 def test_attention_standalone(dtype, tol, S, sharp):

@@ -26,6 +26,10 @@ def test_all_bf16_patterns_match_torch():
     x = x[np.isfinite(x)]
     x = np.clip(x, -448.0, 448.0).astype(np.float32)
     assert np.array_equal(O.e4m3_encode(x), _torch_codes(x))
+    # and the brute-force nearest-table map agrees, including every exact tie
+    assert np.array_equal(O.fp8.e4m3_encode_nearest(x), O.e4m3_encode(x))
+    ties = (O.fp8._POS[1:] + O.fp8._POS[:-1]) / 2
+    assert np.array_equal(O.fp8.e4m3_encode_nearest(ties), O.e4m3_encode(ties))
 
 
 def test_dense_fp32_sample_matches_torch():

@@ -123,7 +123,7 @@ Plan make_plan(const dit_dims& d, int nv_seq, bool delta) {
     p.o = take((size_t)p.S * I * es);
     p.o8 = fp8 ? take((size_t)p.S * I) : 0;
     p.h = take((size_t)p.S * D * 4);
-    p.u = take((size_t)p.S * F * es);
+    p.u = take((size_t)p.S * F * (fp8 ? 4 : es));   // fp8: fp32 u, quantised from full precision
     p.u8 = fp8 ? take((size_t)p.S * F) : 0;
     p.delta = delta ? take((size_t)nv_seq * D * 4) : 0;
     p.sc = take(16 * sizeof(float));
@@ -170,7 +170,7 @@ int run_block(const dit_dims& d, const dit_block_weights& w, const SeqIn& in, co
     EpiParams ep{};
     ep.M = S; ep.Mpad = Sp; ep.D = D; ep.I = I; ep.F = F; ep.dh = dh;
     ep.q = q; ep.k = k; ep.vt = vt; ep.Sp = Sp;
-    ep.qscale = (float)(1.4426950408889634 / sqrt((double)dh));
+    const float csoft = (float)(1.4426950408889634 / sqrt((double)dh));   // log2(e) / sqrt(dh)
     ep.rope = rope;
     ep.xin = in;
     ep.h = h;
@@ -196,10 +196,10 @@ int run_block(const dit_dims& d, const dit_block_weights& w, const SeqIn& in, co
     // 3. attention
     TR("attention");
     if (f32) {
-        HIPCHK(attention_f32(q, k, vt, o, S, Sp, nh, dh, st));
+        HIPCHK(attention_f32(q, k, vt, o, S, Sp, nh, dh, csoft, st));
     } else {
         if (fp8) HIPCHK(fill_launch(sc + 1, 1, 0.f, st));
-        HIPCHK(attention_bf16(q, k, vt, o, S, Sp, nh, dh, fp8 ? sc + 1 : nullptr, st));
+        HIPCHK(attention_bf16(q, k, vt, o, S, Sp, nh, dh, csoft, fp8 ? sc + 1 : nullptr, st));
     }
     // 4. O projection + residual -> h (fp32)
     if (fp8) {
@@ -234,7 +234,7 @@ int run_block(const dit_dims& d, const dit_block_weights& w, const SeqIn& in, co
     // 7. down projection + residual -> outputs / delta
     if (fp8) {
         TR("quant_u");
-        HIPCHK(quant_launch(true, u, u8, sc + 3, (size_t)S * F, st));
+        HIPCHK(quant_launch(false, u, u8, sc + 3, (size_t)S * F, st));
         ep.amax_a = sc + 3; ep.s_w = w.s_wdown; ep.s_w2 = nullptr;
         TR("gemm_down");
         HIPCHK(gemm_mfma(true, EPI_DOWN, u8, w.wdown, nullptr, S, D, F, ep, st));
@@ -529,10 +529,10 @@ int32_t dit_attention(int32_t S, int32_t n_heads, int32_t head_dim, int32_t dtyp
     const int Sp = (S + 127) / 128 * 128;
     const size_t part = need / 3;
     uint8_t* w8 = (uint8_t*)ws;
-    const float qscale = (float)((double)scale * 1.4426950408889634);
-    HIPCHK(attention_pack(dtype == DIT_BF16, q, k, v, w8, w8 + part, w8 + 2 * part, S, Sp, n_heads, head_dim, qscale, st));
-    if (dtype == DIT_BF16) HIPCHK(attention_bf16(w8, w8 + part, w8 + 2 * part, o, S, Sp, n_heads, head_dim, nullptr, st));
-    else HIPCHK(attention_f32(w8, w8 + part, w8 + 2 * part, o, S, Sp, n_heads, head_dim, st));
+    const float c = (float)((double)scale * 1.4426950408889634);
+    HIPCHK(attention_pack(dtype == DIT_BF16, q, k, v, w8, w8 + part, w8 + 2 * part, S, Sp, n_heads, head_dim, 1.f, st));
+    if (dtype == DIT_BF16) HIPCHK(attention_bf16(w8, w8 + part, w8 + 2 * part, o, S, Sp, n_heads, head_dim, c, nullptr, st));
+    else HIPCHK(attention_f32(w8, w8 + part, w8 + 2 * part, o, S, Sp, n_heads, head_dim, c, st));
     return DIT_OK;
 }
 

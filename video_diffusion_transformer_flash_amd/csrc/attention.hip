@@ -4,9 +4,10 @@
 // section 2: attention cost grows strongly with sequence length, which the
 // compressed layers shorten).
 //
-// Inputs come from the QKV epilogue: q, k [head][Sp][dh] (q already rotated
-// and scaled by log2(e)/sqrt(dh), so the softmax uses exp2), v transposed
-// [head][dh][Sp]; rows [S, Sp) are zero. Output o [S][heads * dh].
+// Inputs come from the QKV epilogue: q, k [head][Sp][dh] (rotated), v
+// transposed [head][dh][Sp]; rows [S, Sp) are zero. Output o [S][heads * dh].
+// The softmax runs in base 2: c = log2(e) * scale multiplies the raw scores
+// inside the exp2 argument (one fma per score), so q keeps its own rounding.
 //
 // bf16 kernel: a workgroup of 4 waves takes 128 queries of one head, a wave
 // 32 queries. The wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
@@ -37,7 +38,7 @@ DIT_DEV int rho(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                                                            const bf16_t* __restrict__ Vt, bf16_t* __restrict__ O,
-                                                           int S, int Sp, int nh, float* o_amax) {
+                                                           int S, int Sp, int nh, float c, float* o_amax) {
     constexpr int DH = 128;
     __shared__ __attribute__((aligned(16))) uint8_t sK[2][KT * DH * 2];
     __shared__ __attribute__((aligned(16))) uint8_t sV[2][DH * KT * 2];
@@ -128,14 +129,15 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
             for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sc[b][r]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
         const float mnew = fmaxf(mrun, tmax);
-        const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+        const float alpha = __builtin_amdgcn_exp2f((mrun - mnew) * c);
         mrun = mnew;
+        const float mc = -mnew * c;
         float psum = 0.f;
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float p = __builtin_amdgcn_exp2f(sc[b][r] - mnew);
+                float p = __builtin_amdgcn_exp2f(fmaf(sc[b][r], c, mc));
                 sc[b][r] = p;
                 psum += p;
             }
@@ -197,11 +199,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
 }
 
 // fp32 attention: one thread per query, 64 queries of one head per block,
-// key tiles of 32 in LDS; exact fp32 online softmax (exp2 on pre-scaled q).
+// key tiles of 32 in LDS; fp32 online softmax.
 template <int DH>
 __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                       const float* __restrict__ Vt, float* __restrict__ O, int S,
-                                                      int Sp, int nh) {
+                                                      int Sp, int nh, float c) {
     constexpr int KB = 32;
     __shared__ float sk[KB][DH + 1];
     __shared__ float sv[KB][DH + 1];
@@ -242,14 +244,14 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
             tmax = fmaxf(tmax, s[j]);
         }
         const float mn = fmaxf(m, tmax);
-        const float alpha = exp2f(m - mn);
+        const float alpha = exp2f((m - mn) * c);
         m = mn;
         l *= alpha;
 #pragma unroll
         for (int d = 0; d < DH; ++d) acc[d] *= alpha;
 #pragma unroll
         for (int j = 0; j < KB; ++j) {
-            const float p = exp2f(s[j] - mn);
+            const float p = exp2f(fmaf(s[j], c, -mn * c));
             l += p;
 #pragma unroll
             for (int d = 0; d < DH; ++d) acc[d] = fmaf(p, sv[j][d], acc[d]);
@@ -297,23 +299,23 @@ __global__ void attn_pack_kernel(const T* __restrict__ q, const T* __restrict__ 
 using namespace detail;
 
 hipError_t attention_bf16(const void* Q, const void* K, const void* Vt, void* O, int S, int Sp, int nh, int dh,
-                          float* o_amax, hipStream_t st) {
+                          float c, float* o_amax, hipStream_t st) {
     if (dh != 128) return hipErrorInvalidValue;
     const int nq = (S + 127) / 128;
     hipLaunchKernelGGL(attn_bf16_kernel, dim3(nq * nh), dim3(256), 0, st, (const bf16_t*)Q, (const bf16_t*)K,
-                       (const bf16_t*)Vt, (bf16_t*)O, S, Sp, nh, o_amax);
+                       (const bf16_t*)Vt, (bf16_t*)O, S, Sp, nh, c, o_amax);
     return hipGetLastError();
 }
 
 hipError_t attention_f32(const void* Q, const void* K, const void* Vt, void* O, int S, int Sp, int nh, int dh,
-                         hipStream_t st) {
+                         float c, hipStream_t st) {
     const int nq = (S + 63) / 64;
     if (dh == 64)
         hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(nq * nh), dim3(64), 0, st, (const float*)Q, (const float*)K,
-                           (const float*)Vt, (float*)O, S, Sp, nh);
+                           (const float*)Vt, (float*)O, S, Sp, nh, c);
     else if (dh == 128)
         hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(nq * nh), dim3(64), 0, st, (const float*)Q, (const float*)K,
-                           (const float*)Vt, (float*)O, S, Sp, nh);
+                           (const float*)Vt, (float*)O, S, Sp, nh, c);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

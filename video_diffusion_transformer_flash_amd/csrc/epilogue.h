@@ -6,11 +6,11 @@
 // 32x32 accumulator layout), the fp32 kernel does the same. The epilogues fuse
 // what follows each projection in the block (PaperDaily review, section 2:
 // norm, quantisation, rotary embedding and residual update are fused):
-//   QKV   : rotary embedding on q and k (pairs (2i, 2i+1) of each band), q
-//           pre-scaled by log2(e)/sqrt(head_dim) for the exp2 softmax, written
-//           head-major: q, k [head][Sp][dh], v transposed [head][dh][Sp];
+//   QKV   : rotary embedding on q and k (pairs (2i, 2i+1) of each band),
+//           written head-major: q, k [head][Sp][dh], v transposed [head][dh][Sp];
 //   RESID : h = X + acc in fp32 (attention output projection);
-//   SWIGLU: u = silu(gate) * up, with the running |u| max for fp8;
+//   SWIGLU: u = silu(gate) * up, with the running |u| max for fp8 (then u
+//           is kept in fp32 until its quantisation);
 //   DOWN  : y = h + acc to the text / video / audio outputs, or for kept video
 //           rows of a compressed block delta = y - X_ref in fp32.
 #pragma once
@@ -36,7 +36,6 @@ struct EpiParams {
     void* k;
     void* vt;
     int Sp;
-    float qscale;
     Rope rope;
     // RESID
     SeqIn xin;
@@ -101,10 +100,6 @@ DIT_DEV void epi_qkv(const EpiParams& p, int m, int n0, float v[4], float sc) {
                 float a = v[j], b = v[j + 1];
                 v[j] = a * cs.x - b * cs.y;
                 v[j + 1] = a * cs.y + b * cs.x;
-            }
-            if (which == 0) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] *= p.qscale;
             }
         }
     }

@@ -202,7 +202,9 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint8_t* __restric
             const int m = t0 + wt * WT + a * 32 + lrow;
             static_for<NBF / 2>([&](auto bp) {
                 const int fbase = f0 / 2 + wf * (WF / 2) + bp * 32;
-                mx = fmaxf(mx, epi_block_swiglu<TOUT>(ep, m, fbase, lhalf, acc[a][2 * bp], acc[a][2 * bp + 1], sg, su));
+                // fp8: u stays fp32 so that its e4m3 codes come from full-precision values
+                using UT = std::conditional_t<FP8, float, TOUT>;
+                mx = fmaxf(mx, epi_block_swiglu<UT>(ep, m, fbase, lhalf, acc[a][2 * bp], acc[a][2 * bp + 1], sg, su));
             });
         });
         if (ep.u_amax) {

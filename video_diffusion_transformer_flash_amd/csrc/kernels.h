@@ -32,9 +32,9 @@ hipError_t gemm_f32(int mode, const void* A, const void* W0, const void* W1, int
                     hipStream_t st);
 
 hipError_t attention_bf16(const void* Q, const void* K, const void* Vt, void* O, int S, int Sp, int nh, int dh,
-                          float* o_amax, hipStream_t st);
+                          float c, float* o_amax, hipStream_t st);
 hipError_t attention_f32(const void* Q, const void* K, const void* Vt, void* O, int S, int Sp, int nh, int dh,
-                         hipStream_t st);
+                         float c, hipStream_t st);
 hipError_t attention_pack(bool bf16, const void* q, const void* k, const void* v, void* Qp, void* Kp, void* Vtp,
                           int S, int Sp, int nh, int dh, float qscale, hipStream_t st);
 
