@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
     const int blk = xcd_remap(blockIdx.x, nq * nh);
     const int head = blk / nq;
     const int qt = blk - head * nq;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lrow = lane & 31, lhalf = lane >> 5;
     const int q0 = qt * 128 + wave * QW;
 
@@ -64,8 +64,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
     // instruction writes 4 rows of 256 B; instruction i of wave w rows
     // 16 i + 4 w + L/16. V^T: 8 rows of 128 B; rows 32 i + 8 w + L/8. The
     // swizzle is applied by fetching logical chunk (slot ^ swz(row)).
-    const __amdgpu_buffer_rsrc_t rsK = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, 0, Sp * DH * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rsV = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, 0, Sp * DH * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsK = make_rsrc(Kh, Sp * DH * 2);
+    const __amdgpu_buffer_rsrc_t rsV = make_rsrc(Vh, Sp * DH * 2);
     const int krow = 4 * wave + (lane >> 4);
     const int voK = krow * 256 + swzK(krow, lane & 15) * 16;
     const int vrow = 8 * wave + (lane >> 3);

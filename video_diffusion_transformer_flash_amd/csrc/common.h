@@ -133,6 +133,18 @@ DIT_DEV float2 rope_cs(const Rope& r, int d, int3 c) {
     return r.tab_w[c.z * (r.rw >> 1) + (d >> 1)];
 }
 
+// Raw buffer resource over [p, p + bytes) (reads past the end return zero).
+// The pieces go through readfirstlane so that the compiler keeps the
+// descriptor in scalar registers (a vector-held descriptor would turn every
+// buffer access into a waterfall loop).
+DIT_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const int n = __builtin_amdgcn_readfirstlane(bytes);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), 0, n, 0x00020000);
+}
+
 // XCD-aware remap of a linear workgroup id: the hardware deals workgroups
 // round-robin to the 8 XCDs; consecutive logical tiles should share an XCD
 // (and its L2), so logical = (bid % 8) * (n / 8) + bid / 8 on the full part.

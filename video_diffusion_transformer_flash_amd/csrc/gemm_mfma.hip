@@ -7,9 +7,10 @@
 // consecutive features: rotary pairs and the SwiGLU gate/up pair are then in
 // the lane's own registers (see epilogue.h).
 //
-// Tiling: 256 threads = 4 waves (2 token halves x 2 feature halves); a tile
-// of BT tokens x BF features; a K step of 128 bytes per row (64 bf16 or 128
-// fp8); operands staged through LDS in two buffers (one barrier per K step)
+// Tiling: WGT x WGF waves (token groups x feature groups); a tile of BT
+// tokens x BF features, each wave BT/WGT x BF/WGF; a K step of 128 bytes per
+// row (64 bf16 or 128 fp8); operands staged through LDS in two buffers (one
+// barrier per K step)
 // with a 16-byte-chunk XOR swizzle so that 16 lanes reading one chunk column
 // of 16 consecutive rows hit 16 distinct bank groups of the 64-bank LDS.
 // Workgroup ids are remapped so that neighbouring tiles share an XCD (L2).
@@ -39,26 +40,29 @@ struct Elem<true> {
     static constexpr int SUB = 2;       // 64 each
 };
 
-template <int BT, int BF, bool FP8, int MODE, typename TOUT>
-__global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ W0,
+template <int BT, int BF, int WGT, int WGF, bool FP8, int MODE, typename TOUT>
+__global__ __launch_bounds__(64 * WGT * WGF) void gemm_mfma_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ W0,
                                                         const uint8_t* __restrict__ W1, int M, int N, int K,
                                                         EpiParams ep) {
 #if defined(__HIP_DEVICE_COMPILE__)
     using E = Elem<FP8>;
-    constexpr int WT = BT / 2, WF = BF / 2;  // per-wave tile
+    constexpr int NW = WGT * WGF;            // waves
+    constexpr int WT = BT / WGT, WF = BF / WGF;  // per-wave tile
+    static_assert(NW >= 2 && WT % 32 == 0 && WF % 64 == 0 && BT % (8 * NW) == 0 && BF % (8 * NW) == 0, "tile");
     constexpr int NBT = WT / 32, NBF = WF / 32;
     constexpr int ESZ = FP8 ? 1 : 2;
     constexpr int LDS_T = BT * ROWB, LDS_F = BF * ROWB;
 
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    // buffer b: features at smem + b * (LDS_F + LDS_T), tokens right after
-    auto sF = [&](int b) { return smem + b * (LDS_F + LDS_T); };
-    auto sT = [&](int b) { return smem + b * (LDS_F + LDS_T) + LDS_F; };
+    // LDS: feature tiles of buffers 0 and 1, then token tiles of buffers 0 and
+    // 1, so that buffer 1 is buffer 0 plus a constant (an immediate offset).
+    constexpr int OFF_T = 2 * LDS_F;
+    constexpr int NR = FP8 ? 2 : 1;              // 16-byte LDS reads per operand fragment
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wt = wave & 1, wf = wave >> 1;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keep it scalar
+    const int wt = wave % WGT, wf = wave / WGT;
 
     // tile coordinates: XCD-aware, grouped along tokens (GM token tiles share W)
     const int ntt = (M + BT - 1) / BT;
@@ -83,27 +87,64 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint8_t* __restric
     // 64 lanes writing consecutive 16-byte slots; the swizzle is applied on
     // the memory side by fetching, for LDS slot (row, L % 8), the logical
     // chunk (L % 8) ^ swz(row). Instruction i of wave w covers rows
-    // 32 i + 8 w .. +7 of the tile.
-    const int r8 = 8 * wave + (lane >> 3);                 // row within a 32-row group
-    const int cswz = ((lane & 7) ^ swz(r8, 0)) * 16;       // swz(r8 + 32 i) == swz(r8)
+    // 8 NW i + 8 w .. +7 of the tile.
+    constexpr int RPI = 8 * NW;                            // rows per round of instructions
+    const int r8 = 8 * wave + (lane >> 3);                 // row within a round
+    const int cswz = ((lane & 7) ^ swz(r8, 0)) * 16;       // swz(r8 + RPI i) == swz(r8): RPI % 16 == 0
     // token rows past M read as zero: the bound check sees only the lane offset
     const int tvalid = min(M - t0, BT);
-    const __amdgpu_buffer_rsrc_t rsT =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(A + (size_t)t0 * rowbytes), 0, tvalid * rowbytes, 0x00020000);
-    int voT[BT / 32];
+    const __amdgpu_buffer_rsrc_t rsT = make_rsrc(A + (size_t)t0 * rowbytes, tvalid * rowbytes);
+    int voT[BT / RPI];
 #pragma unroll
-    for (int i = 0; i < BT / 32; ++i) voT[i] = (32 * i + r8) * rowbytes + cswz;
+    for (int i = 0; i < BT / RPI; ++i) voT[i] = (RPI * i + r8) * rowbytes + cswz;
     __amdgpu_buffer_rsrc_t rsF0, rsF1;
     if constexpr (MODE == EPI_SWIGLU) {
-        rsF0 = __builtin_amdgcn_make_buffer_rsrc((void*)(W0 + (size_t)(f0 / 2) * rowbytes), 0, (BF / 2) * rowbytes,
-                                                 0x00020000);
-        rsF1 = __builtin_amdgcn_make_buffer_rsrc((void*)(W1 + (size_t)(f0 / 2) * rowbytes), 0, (BF / 2) * rowbytes,
-                                                 0x00020000);
+        rsF0 = make_rsrc(W0 + (size_t)(f0 / 2) * rowbytes, (BF / 2) * rowbytes);
+        rsF1 = make_rsrc(W1 + (size_t)(f0 / 2) * rowbytes, (BF / 2) * rowbytes);
     } else {
-        rsF0 = __builtin_amdgcn_make_buffer_rsrc((void*)(W0 + (size_t)f0 * rowbytes), 0, BF * rowbytes, 0x00020000);
+        rsF0 = make_rsrc(W0 + (size_t)f0 * rowbytes, BF * rowbytes);
         rsF1 = rsF0;
     }
-    const int voF = r8 * rowbytes + cswz;
+    const int voF = (lane >> 3) * rowbytes + cswz;         // lane part; the wave's row goes in soffset
+
+    const int nk = K / E::BK;
+
+    auto issue = [&](int kt, int buf) {
+        const int koff = kt * ROWB;
+        LDSPTR lt = (LDSPTR)(smem + OFF_T + buf * LDS_T + wave * 1024);   // 8 rows of 128 B per wave
+        LDSPTR lf = (LDSPTR)(smem + buf * LDS_F + wave * 1024);
+#pragma unroll
+        for (int i = 0; i < BT / RPI; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsT, lt + i * RPI * ROWB, 16, voT[i] + koff, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < BF / RPI; ++i) {
+            const int rowr = RPI * i + 8 * wave;               // first of this wave's 8 rows (uniform)
+            if constexpr (MODE == EPI_SWIGLU) {
+                // 32-row blocks of the tile alternate gate / up rows of the same
+                // ffn features: block b holds gate (b even) or up rows b/2*32 ..
+                const int blk = rowr / 32;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds((blk & 1) ? rsF1 : rsF0, lf + i * RPI * ROWB, 16, voF + koff,
+                                                         ((blk >> 1) * 32 + rowr % 32) * rowbytes, 0, 0);
+            } else {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsF0, lf + i * RPI * ROWB, 16, voF + koff, rowr * rowbytes, 0,
+                                                         0);
+            }
+        }
+    };
+
+    // Per-lane LDS byte offsets (buffer 0) of the operand fragments: fragment
+    // (s, block) read r is the 16-byte chunk c = NR * (2 s + h) + r of the
+    // lane's row. A lane's rows differ by multiples of 32 between blocks, so
+    // the swizzle term (row >> 1) & 7 is the same for all of them and a block
+    // is a constant 32 * ROWB further: one VGPR per (s, r), blocks and buffers
+    // as immediate offsets.
+    const int xs = (lrow >> 1) & 7;
+    const int rowF0 = (wf * WF + lrow) * ROWB, rowT0 = OFF_T + (wt * WT + lrow) * ROWB;
+    uint32_t aC[E::SUB][NR];
+#pragma unroll
+    for (int s = 0; s < E::SUB; ++s)
+#pragma unroll
+        for (int r = 0; r < NR; ++r) aC[s][r] = ((NR * (2 * s + lhalf) + r) ^ xs) * 16;
 
     f32x16 acc[NBT][NBF];
 #pragma unroll
@@ -113,84 +154,70 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint8_t* __restric
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-    const int nk = K / E::BK;
+    // two fragment register sets: substep s computes from one while s+1 loads into the other
+    uint4 fF[2][NBF][NR], fT[2][NBT][NR];
 
-    auto issue = [&](int kt, int buf) {
-        const int koff = kt * ROWB;
-        LDSPTR lt = (LDSPTR)(sT(buf) + wave * 1024);
-        LDSPTR lf = (LDSPTR)(sF(buf) + wave * 1024);
+    auto load_frags = [&](auto setc, auto sc, auto bufc) {
+        constexpr int SET = decltype(setc)::value, S = decltype(sc)::value, BUF = decltype(bufc)::value;
 #pragma unroll
-        for (int i = 0; i < BT / 32; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsT, lt + i * 4096, 16, voT[i] + koff, 0, 0, 0);
+        for (int r = 0; r < NR; ++r) {
+            const uint8_t* pF = smem + rowF0 + aC[S][r] + BUF * LDS_F;
+            const uint8_t* pT = smem + rowT0 + aC[S][r] + BUF * LDS_T;
 #pragma unroll
-        for (int i = 0; i < BF / 32; ++i) {
-            if constexpr (MODE == EPI_SWIGLU) {
-                // 32-row blocks alternate gate / up rows of the same ffn features
-                __builtin_amdgcn_raw_ptr_buffer_load_lds((i & 1) ? rsF1 : rsF0, lf + i * 4096, 16, voF + koff,
-                                                         (i >> 1) * 32 * rowbytes, 0, 0);
-            } else {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsF0, lf + i * 4096, 16, voF + koff, i * 32 * rowbytes, 0, 0);
-            }
+            for (int b = 0; b < NBF; ++b) fF[SET][b][r] = *(const uint4*)(pF + b * 32 * ROWB);
+#pragma unroll
+            for (int a = 0; a < NBT; ++a) fT[SET][a][r] = *(const uint4*)(pT + a * 32 * ROWB);
         }
     };
+    auto mfmas = [&](auto setc) {
+        constexpr int SET = decltype(setc)::value;
+#pragma unroll
+        for (int a = 0; a < NBT; ++a)
+#pragma unroll
+            for (int b = 0; b < NBF; ++b) {
+                if constexpr (!FP8) {
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_v, fF[SET][b][0]),
+                                                                         __builtin_bit_cast(bf16x8_v, fT[SET][a][0]),
+                                                                         acc[a][b], 0, 0, 0);
+                } else {
+                    const uint4 x0 = fF[SET][b][0], x1 = fF[SET][b][1], y0 = fT[SET][a][0], y1 = fT[SET][a][1];
+                    const i32x8 fa = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z,
+                                      (int)x1.w};
+                    const i32x8 fb = {(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w, (int)y1.x, (int)y1.y, (int)y1.z,
+                                      (int)y1.w};
+                    acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, acc[a][b], 0, 0, 0, 0, 0, 0);
+                }
+            }
+    };
 
-    // LDS read offsets of this lane's operand rows
-    int rowT[NBT], rowF[NBF];
-#pragma unroll
-    for (int a = 0; a < NBT; ++a) rowT[a] = wt * WT + a * 32 + lrow;
-#pragma unroll
-    for (int b = 0; b < NBF; ++b) rowF[b] = wf * WF + b * 32 + lrow;
+    // One K step on LDS buffer BUF: the fragments of substep 0 are already in
+    // set 0. Substeps 0..SUB-2 load the next substep's fragments while their
+    // MFMAs run; the last substep's fragments are in registers before the
+    // barrier, so after it the next step's first fragments (other buffer)
+    // load while the last MFMAs run.
+    auto kstep = [&](auto bufc, int kt) {
+        constexpr int BUF = decltype(bufc)::value;
+        if (kt + 1 < nk) issue(kt + 1, BUF ^ 1);
+        static_for<E::SUB - 1>([&](auto s) {
+            load_frags(std::integral_constant<int, (s + 1) & 1>{}, std::integral_constant<int, s + 1>{}, bufc);
+            mfmas(std::integral_constant<int, s & 1>{});
+            __builtin_amdgcn_sched_barrier(0);   // keep later fragment loads out of this substep
+        });
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's LDS fills for the next step have landed
+        __syncthreads();                 // ... and everyone's; nobody reads this buffer any more
+        if (kt + 1 < nk) load_frags(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
+                                    std::integral_constant<int, BUF ^ 1>{});
+        mfmas(std::integral_constant<int, (E::SUB - 1) & 1>{});
+        __builtin_amdgcn_sched_barrier(0);
+    };
 
     issue(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) issue(kt + 1, buf ^ 1);
-        const uint8_t* bT = sT(buf);
-        const uint8_t* bF = sF(buf);
-#pragma unroll
-        for (int s = 0; s < E::SUB; ++s) {
-            if constexpr (!FP8) {
-                bf16x8_v fa[NBF], fb[NBT];
-                const int c = 2 * s + lhalf;
-#pragma unroll
-                for (int b = 0; b < NBF; ++b)
-                    fa[b] = *(const bf16x8_v*)(bF + rowF[b] * ROWB + swz(rowF[b], c) * 16);
-#pragma unroll
-                for (int a = 0; a < NBT; ++a)
-                    fb[a] = *(const bf16x8_v*)(bT + rowT[a] * ROWB + swz(rowT[a], c) * 16);
-#pragma unroll
-                for (int a = 0; a < NBT; ++a)
-#pragma unroll
-                    for (int b = 0; b < NBF; ++b)
-                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[b], fb[a], acc[a][b], 0, 0, 0);
-            } else {
-                i32x8 fa[NBF], fb[NBT];
-                const int c = 4 * s + 2 * lhalf;
-#pragma unroll
-                for (int b = 0; b < NBF; ++b) {
-                    uint4 x0 = *(const uint4*)(bF + rowF[b] * ROWB + swz(rowF[b], c) * 16);
-                    uint4 x1 = *(const uint4*)(bF + rowF[b] * ROWB + swz(rowF[b], c + 1) * 16);
-                    fa[b] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-                }
-#pragma unroll
-                for (int a = 0; a < NBT; ++a) {
-                    uint4 x0 = *(const uint4*)(bT + rowT[a] * ROWB + swz(rowT[a], c) * 16);
-                    uint4 x1 = *(const uint4*)(bT + rowT[a] * ROWB + swz(rowT[a], c + 1) * 16);
-                    fb[a] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-                }
-#pragma unroll
-                for (int a = 0; a < NBT; ++a)
-#pragma unroll
-                    for (int b = 0; b < NBF; ++b)
-                        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[b], fb[a], acc[a][b], 0, 0, 0,
-                                                                                     0, 0, 0);
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's LDS fills for the next step have landed
-        __syncthreads();                 // ... and everyone's; the current buffer is free
+    load_frags(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    for (int kt = 0; kt < nk; kt += 2) {
+        kstep(std::integral_constant<int, 0>{}, kt);
+        if (kt + 1 < nk) kstep(std::integral_constant<int, 1>{}, kt + 1);
     }
 
     // ---------------------------------------------------------------- epilogue
@@ -205,6 +232,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint8_t* __restric
                 // fp8: u stays fp32 so that its e4m3 codes come from full-precision values
                 using UT = std::conditional_t<FP8, float, TOUT>;
                 mx = fmaxf(mx, epi_block_swiglu<UT>(ep, m, fbase, lhalf, acc[a][2 * bp], acc[a][2 * bp + 1], sg, su));
+                __builtin_amdgcn_sched_barrier(0);   // one block at a time: bounded register pressure
             });
         });
         if (ep.u_amax) {
@@ -217,26 +245,27 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint8_t* __restric
             const int m = t0 + wt * WT + a * 32 + lrow;
             static_for<NBF>([&](auto b) {
                 epi_block<MODE, TOUT>(ep, m, f0 + wf * WF + b * 32, lhalf, acc[a][b], sc);
+                __builtin_amdgcn_sched_barrier(0);   // one block at a time: bounded register pressure
             });
         });
     }
 #endif  // device pass only: the host pass keeps just the launch stub
 }
 
-template <int BT, int BF, bool FP8, int MODE>
+template <int BT, int BF, int WGT, int WGF, bool FP8, int MODE>
 hipError_t launch_t(const void* A, const void* W0, const void* W1, int M, int N, int K, const EpiParams& ep,
                     hipStream_t st) {
-    constexpr int smem = 2 * (BT + BF) * ROWB;
+    constexpr int smem = 2 * (BT + BF) * ROWB;   // two buffers of each operand tile
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void*)&gemm_mfma_kernel<BT, BF, FP8, MODE, bf16_t>,
+        hipError_t e = hipFuncSetAttribute((const void*)&gemm_mfma_kernel<BT, BF, WGT, WGF, FP8, MODE, bf16_t>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, smem);
         if (e != hipSuccess) return e;
         attr = true;
     }
     const int tiles = ((M + BT - 1) / BT) * (N / BF);
-    hipLaunchKernelGGL((gemm_mfma_kernel<BT, BF, FP8, MODE, bf16_t>), dim3(tiles), dim3(256), smem, st, (const uint8_t*)A, (const uint8_t*)W0,
-                       (const uint8_t*)W1, M, N, K, ep);
+    hipLaunchKernelGGL((gemm_mfma_kernel<BT, BF, WGT, WGF, FP8, MODE, bf16_t>), dim3(tiles), dim3(64 * WGT * WGF), smem,
+                       st, (const uint8_t*)A, (const uint8_t*)W0, (const uint8_t*)W1, M, N, K, ep);
     return hipGetLastError();
 }
 
@@ -245,10 +274,10 @@ hipError_t dispatch(const void* A, const void* W0, const void* W1, int M, int N,
                     hipStream_t st) {
     // big tiles when there are enough of them to fill 256 CUs several times
     const long t256 = (long)((M + 255) / 256) * (N / 256);
-    if (N % 256 == 0 && t256 >= 512) return launch_t<256, 256, FP8, MODE>(A, W0, W1, M, N, K, ep, st);
+    if (N % 256 == 0 && t256 >= 512) return launch_t<256, 256, 2, 4, FP8, MODE>(A, W0, W1, M, N, K, ep, st);
     if (N % 256 == 0 && (long)((M + 127) / 128) * (N / 256) >= 256)
-        return launch_t<128, 256, FP8, MODE>(A, W0, W1, M, N, K, ep, st);
-    return launch_t<128, 128, FP8, MODE>(A, W0, W1, M, N, K, ep, st);
+        return launch_t<128, 256, 2, 2, FP8, MODE>(A, W0, W1, M, N, K, ep, st);
+    return launch_t<128, 128, 2, 2, FP8, MODE>(A, W0, W1, M, N, K, ep, st);
 }
 
 }  // namespace detail
