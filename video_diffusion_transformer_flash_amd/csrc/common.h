@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/vdtflash.h"
+#include "vdtflash.h"
 
 #define DIT_DEV __device__ __forceinline__
 
@@ -19,14 +19,14 @@ namespace dit {
 // ----------------------------------------------------------------- bf16 / fp32
 DIT_DEV float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// fp32 -> bf16, round to nearest even (inputs are finite in this library)
-DIT_DEV bf16_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (bf16_t)(u >> 16);
+// fp32 -> bf16, round to nearest even: gfx950's v_cvt_pk_bf16_f32 (one
+// instruction per pair; the library's values are finite)
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_v;
+DIT_DEV bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+DIT_DEV uint32_t pack_bf2(float a, float b) {
+    const bf16x2_v v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
 }
-
-DIT_DEV uint32_t pack_bf2(float a, float b) { return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16); }
 
 // ----------------------------------------------------------------- fp8 e4m3
 // fp32 -> OCP e4m3 code: nearest value, ties to even, saturating at +-448,

@@ -40,7 +40,7 @@ struct Elem<true> {
     static constexpr int SUB = 2;       // 64 each
 };
 
-template <int BT, int BF, int WGT, int WGF, bool FP8, int MODE, typename TOUT>
+template <int BT, int BF, int WGT, int WGF, int NS, bool FP8, int MODE, typename TOUT>
 __global__ __launch_bounds__(64 * WGT * WGF) void gemm_mfma_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ W0,
                                                         const uint8_t* __restrict__ W1, int M, int N, int K,
                                                         EpiParams ep) {
@@ -54,9 +54,9 @@ __global__ __launch_bounds__(64 * WGT * WGF) void gemm_mfma_kernel(const uint8_t
     constexpr int LDS_T = BT * ROWB, LDS_F = BF * ROWB;
 
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    // LDS: feature tiles of buffers 0 and 1, then token tiles of buffers 0 and
-    // 1, so that buffer 1 is buffer 0 plus a constant (an immediate offset).
-    constexpr int OFF_T = 2 * LDS_F;
+    // LDS: NS stages; the feature tiles of all stages, then the token tiles, so
+    // that stage b is stage 0 plus a constant (an immediate offset).
+    constexpr int OFF_T = NS * LDS_F;
     constexpr int NR = FP8 ? 2 : 1;              // 16-byte LDS reads per operand fragment
 
     const int tid = threadIdx.x;
@@ -190,34 +190,47 @@ __global__ __launch_bounds__(64 * WGT * WGF) void gemm_mfma_kernel(const uint8_t
             }
     };
 
-    // One K step on LDS buffer BUF: the fragments of substep 0 are already in
-    // set 0. Substeps 0..SUB-2 load the next substep's fragments while their
-    // MFMAs run; the last substep's fragments are in registers before the
-    // barrier, so after it the next step's first fragments (other buffer)
-    // load while the last MFMAs run.
+    // vmcnt immediate (gfx9 encoding, expcnt / lgkmcnt left at their maxima)
+    constexpr int LPS = BT / RPI + BF / RPI;                       // memory -> LDS loads per step per wave
+    constexpr int VM_KEEP = LPS * (NS - 2);                         // loads of later steps left in flight
+    static_assert(VM_KEEP < 64, "vmcnt range");
+    constexpr int WAIT_KEEP = (VM_KEEP & 15) | (7 << 4) | (15 << 8) | ((VM_KEEP >> 4) << 14);
+
+    // One K step on LDS stage BUF: the fragments of substep 0 are already in
+    // set 0, the loads for the next NS - 2 steps are in flight. Issue the loads
+    // of step kt + NS - 1 into the stage freed by the previous step; substeps
+    // 0..SUB-2 load the next substep's fragments while their MFMAs run; the
+    // last substep's fragments are in registers before the barrier, so after
+    // it the next step's first fragments load while the last MFMAs run.
     auto kstep = [&](auto bufc, int kt) {
         constexpr int BUF = decltype(bufc)::value;
-        if (kt + 1 < nk) issue(kt + 1, BUF ^ 1);
+        if (kt + NS - 1 < nk) issue(kt + NS - 1, (BUF + NS - 1) % NS);
         static_for<E::SUB - 1>([&](auto s) {
             load_frags(std::integral_constant<int, (s + 1) & 1>{}, std::integral_constant<int, s + 1>{}, bufc);
             mfmas(std::integral_constant<int, s & 1>{});
             __builtin_amdgcn_sched_barrier(0);   // keep later fragment loads out of this substep
         });
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's LDS fills for the next step have landed
-        __syncthreads();                 // ... and everyone's; nobody reads this buffer any more
+        // step kt + 1's LDS fills (this wave's) have landed; then everyone's
+        if (kt + NS - 1 < nk) __builtin_amdgcn_s_waitcnt(WAIT_KEEP);
+        else __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();                 // nobody reads stage BUF any more
         if (kt + 1 < nk) load_frags(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
-                                    std::integral_constant<int, BUF ^ 1>{});
+                                    std::integral_constant<int, (BUF + 1) % NS>{});
         mfmas(std::integral_constant<int, (E::SUB - 1) & 1>{});
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    issue(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int b = 0; b < NS - 1; ++b)
+        if (b < nk) issue(b, b);
+    if (NS - 1 <= nk) __builtin_amdgcn_s_waitcnt(WAIT_KEEP);
+    else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     load_frags(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-    for (int kt = 0; kt < nk; kt += 2) {
-        kstep(std::integral_constant<int, 0>{}, kt);
-        if (kt + 1 < nk) kstep(std::integral_constant<int, 1>{}, kt + 1);
+    for (int kt = 0; kt < nk; kt += NS) {
+        static_for<NS>([&](auto b) {
+            if (kt + b < nk) kstep(b, kt + b);
+        });
     }
 
     // ---------------------------------------------------------------- epilogue
@@ -252,19 +265,20 @@ __global__ __launch_bounds__(64 * WGT * WGF) void gemm_mfma_kernel(const uint8_t
 #endif  // device pass only: the host pass keeps just the launch stub
 }
 
-template <int BT, int BF, int WGT, int WGF, bool FP8, int MODE>
+template <int BT, int BF, int WGT, int WGF, int NS, bool FP8, int MODE>
 hipError_t launch_t(const void* A, const void* W0, const void* W1, int M, int N, int K, const EpiParams& ep,
                     hipStream_t st) {
-    constexpr int smem = 2 * (BT + BF) * ROWB;   // two buffers of each operand tile
+    constexpr int smem = NS * (BT + BF) * ROWB;   // NS stages of each operand tile
+    static_assert(smem <= 160 * 1024, "LDS");
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void*)&gemm_mfma_kernel<BT, BF, WGT, WGF, FP8, MODE, bf16_t>,
+        hipError_t e = hipFuncSetAttribute((const void*)&gemm_mfma_kernel<BT, BF, WGT, WGF, NS, FP8, MODE, bf16_t>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, smem);
         if (e != hipSuccess) return e;
         attr = true;
     }
     const int tiles = ((M + BT - 1) / BT) * (N / BF);
-    hipLaunchKernelGGL((gemm_mfma_kernel<BT, BF, WGT, WGF, FP8, MODE, bf16_t>), dim3(tiles), dim3(64 * WGT * WGF), smem,
+    hipLaunchKernelGGL((gemm_mfma_kernel<BT, BF, WGT, WGF, NS, FP8, MODE, bf16_t>), dim3(tiles), dim3(64 * WGT * WGF), smem,
                        st, (const uint8_t*)A, (const uint8_t*)W0, (const uint8_t*)W1, M, N, K, ep);
     return hipGetLastError();
 }
@@ -274,10 +288,10 @@ hipError_t dispatch(const void* A, const void* W0, const void* W1, int M, int N,
                     hipStream_t st) {
     // big tiles when there are enough of them to fill 256 CUs several times
     const long t256 = (long)((M + 255) / 256) * (N / 256);
-    if (N % 256 == 0 && t256 >= 512) return launch_t<256, 256, 2, 4, FP8, MODE>(A, W0, W1, M, N, K, ep, st);
+    if (N % 256 == 0 && t256 >= 512) return launch_t<256, 256, 2, 4, 2, FP8, MODE>(A, W0, W1, M, N, K, ep, st);
     if (N % 256 == 0 && (long)((M + 127) / 128) * (N / 256) >= 256)
-        return launch_t<128, 256, 2, 2, FP8, MODE>(A, W0, W1, M, N, K, ep, st);
-    return launch_t<128, 128, 2, 2, FP8, MODE>(A, W0, W1, M, N, K, ep, st);
+        return launch_t<128, 256, 2, 2, 3, FP8, MODE>(A, W0, W1, M, N, K, ep, st);
+    return launch_t<128, 128, 2, 2, 3, FP8, MODE>(A, W0, W1, M, N, K, ep, st);
 }
 
 }  // namespace detail

@@ -185,24 +185,68 @@ __global__ void gather_rows_kernel(const uint8_t* __restrict__ x, const int32_t*
     ((uint4*)out)[(size_t)j * chunks + c] = ((const uint4*)x)[(size_t)src * chunks + c];
 }
 
-// out[p] = x[p] + delta[nk[p]]: 8 elements per thread
+// out[p] = x[p] + delta[nk[p]]. One workgroup per video position p (so the
+// kept slot nk[p] is a scalar), 8 elements per 16/32-byte access, up to four
+// accesses in flight per thread; the output is written non-temporally (it is
+// not read again by this block).
 template <typename T>
-__global__ void broadcast_residual_kernel(const T* __restrict__ x, const float* __restrict__ delta,
-                                          const int32_t* __restrict__ nk, T* __restrict__ out, int n_video, int D) {
+struct Chunk8;
+template <>
+struct Chunk8<bf16_t> {
+    uint4 v;
+    DIT_DEV void load(const bf16_t* p) { v = *(const uint4*)p; }
+    DIT_DEV void add_store(bf16_t* p, float4 d0, float4 d1) const {
+        uint4 o;
+        o.x = pack_bf2(__uint_as_float(v.x << 16) + d0.x, __uint_as_float(v.x & 0xFFFF0000u) + d0.y);
+        o.y = pack_bf2(__uint_as_float(v.y << 16) + d0.z, __uint_as_float(v.y & 0xFFFF0000u) + d0.w);
+        o.z = pack_bf2(__uint_as_float(v.z << 16) + d1.x, __uint_as_float(v.z & 0xFFFF0000u) + d1.y);
+        o.w = pack_bf2(__uint_as_float(v.w << 16) + d1.z, __uint_as_float(v.w & 0xFFFF0000u) + d1.w);
+        __builtin_nontemporal_store(o, (uint4*)p);
+    }
+};
+template <>
+struct Chunk8<float> {
+    float4 a, b;
+    DIT_DEV void load(const float* p) {
+        a = *(const float4*)p;
+        b = *(const float4*)(p + 4);
+    }
+    DIT_DEV void add_store(float* p, float4 d0, float4 d1) const {
+        __builtin_nontemporal_store(make_float4(a.x + d0.x, a.y + d0.y, a.z + d0.z, a.w + d0.w), (float4*)p);
+        __builtin_nontemporal_store(make_float4(b.x + d1.x, b.y + d1.y, b.z + d1.z, b.w + d1.w), (float4*)(p + 4));
+    }
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void broadcast_residual_kernel(const T* x, const float* __restrict__ delta,
+                                                                 const int32_t* __restrict__ nk, T* out, int n_video,
+                                                                 int D) {
+    // x and out may be the same buffer: every element is read, then written, by one thread
+    constexpr int U = 4;
+    const int p = blockIdx.x;
+    const int j = __builtin_amdgcn_readfirstlane(nk[p]);
     const int per_row = D / 8;
-    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (size_t)n_video * per_row) return;
-    const int p = (int)(i / per_row);
-    const int c = (int)(i - (size_t)p * per_row) * 8;
-    const float* d = delta + (size_t)nk[p] * D + c;
-    const float4 d0 = *(const float4*)d, d1 = *(const float4*)(d + 4);
-    float a[4], b[4];
-    ld4<T>(x + (size_t)p * D + c, a);
-    ld4<T>(x + (size_t)p * D + c + 4, b);
-    a[0] += d0.x; a[1] += d0.y; a[2] += d0.z; a[3] += d0.w;
-    b[0] += d1.x; b[1] += d1.y; b[2] += d1.z; b[3] += d1.w;
-    st4<T>(out + (size_t)p * D + c, a);
-    st4<T>(out + (size_t)p * D + c + 4, b);
+    const T* xr = x + (size_t)p * D;
+    const float* dr = delta + (size_t)j * D;
+    T* orow = out + (size_t)p * D;
+    for (int c0 = threadIdx.x; c0 < per_row; c0 += U * 256) {
+        Chunk8<T> xv[U];
+        float4 d0[U], d1[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + u * 256;
+            if (c < per_row) {
+                xv[u].load(xr + 8 * c);
+                d0[u] = *(const float4*)(dr + 8 * c);
+                d1[u] = *(const float4*)(dr + 8 * c + 4);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + u * 256;
+            if (c < per_row) xv[u].add_store(orow + 8 * c, d0[u], d1[u]);
+        }
+    }
 }
 
 // x += dt * v (4 elements per thread)
@@ -320,12 +364,11 @@ hipError_t gather_rows_launch(const void* x, const int32_t* idx, void* out, int 
 
 hipError_t broadcast_residual_launch(bool bf16, const void* x, const float* delta, const int32_t* nk, void* out,
                                      int n_video, int D, hipStream_t st) {
-    const size_t n = (size_t)n_video * (D / 8);
     if (bf16)
-        hipLaunchKernelGGL(broadcast_residual_kernel<bf16_t>, dim3(nblk(n)), dim3(256), 0, st, (const bf16_t*)x, delta,
+        hipLaunchKernelGGL(broadcast_residual_kernel<bf16_t>, dim3(n_video), dim3(256), 0, st, (const bf16_t*)x, delta,
                            nk, (bf16_t*)out, n_video, D);
     else
-        hipLaunchKernelGGL(broadcast_residual_kernel<float>, dim3(nblk(n)), dim3(256), 0, st, (const float*)x, delta,
+        hipLaunchKernelGGL(broadcast_residual_kernel<float>, dim3(n_video), dim3(256), 0, st, (const float*)x, delta,
                            nk, (float*)out, n_video, D);
     return hipGetLastError();
 }
