@@ -53,10 +53,20 @@ __global__ __launch_bounds__(64 * WGT * WGF) void gemm_mfma_kernel(const uint8_t
     constexpr int ESZ = FP8 ? 1 : 2;
     constexpr int LDS_T = BT * ROWB, LDS_F = BF * ROWB;
 
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    // LDS: NS stages; the feature tiles of all stages, then the token tiles, so
-    // that stage b is stage 0 plus a constant (an immediate offset).
-    constexpr int OFF_T = NS * LDS_F;
+    // LDS: one array per pipeline stage (feature tile, then token tile). With
+    // separate arrays the compiler can tell that the memory -> LDS loads into
+    // one stage do not alias the LDS reads of another, and does not make those
+    // reads wait for the loads. Stage addresses are constants.
+    constexpr int SB = LDS_F + LDS_T;
+    __shared__ __attribute__((aligned(16))) uint8_t st0[SB];
+    __shared__ __attribute__((aligned(16))) uint8_t st1[SB];
+    __shared__ __attribute__((aligned(16))) uint8_t st2[NS > 2 ? SB : 16];
+    auto stage = [&](auto bc) -> uint8_t* {
+        constexpr int B = decltype(bc)::value;
+        if constexpr (B == 0) return st0;
+        else if constexpr (B == 1) return st1;
+        else return st2;
+    };
     constexpr int NR = FP8 ? 2 : 1;              // 16-byte LDS reads per operand fragment
 
     const int tid = threadIdx.x;
@@ -109,10 +119,10 @@ __global__ __launch_bounds__(64 * WGT * WGF) void gemm_mfma_kernel(const uint8_t
 
     const int nk = K / E::BK;
 
-    auto issue = [&](int kt, int buf) {
+    auto issue = [&](int kt, auto bufc) {
         const int koff = kt * ROWB;
-        LDSPTR lt = (LDSPTR)(smem + OFF_T + buf * LDS_T + wave * 1024);   // 8 rows of 128 B per wave
-        LDSPTR lf = (LDSPTR)(smem + buf * LDS_F + wave * 1024);
+        LDSPTR lt = (LDSPTR)(stage(bufc) + LDS_F + wave * 1024);   // 8 rows of 128 B per wave
+        LDSPTR lf = (LDSPTR)(stage(bufc) + wave * 1024);
 #pragma unroll
         for (int i = 0; i < BT / RPI; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsT, lt + i * RPI * ROWB, 16, voT[i] + koff, 0, 0, 0);
@@ -139,7 +149,7 @@ __global__ __launch_bounds__(64 * WGT * WGF) void gemm_mfma_kernel(const uint8_t
     // is a constant 32 * ROWB further: one VGPR per (s, r), blocks and buffers
     // as immediate offsets.
     const int xs = (lrow >> 1) & 7;
-    const int rowF0 = (wf * WF + lrow) * ROWB, rowT0 = OFF_T + (wt * WT + lrow) * ROWB;
+    const int rowF0 = (wf * WF + lrow) * ROWB, rowT0 = LDS_F + (wt * WT + lrow) * ROWB;
     uint32_t aC[E::SUB][NR];
 #pragma unroll
     for (int s = 0; s < E::SUB; ++s)
@@ -161,8 +171,8 @@ __global__ __launch_bounds__(64 * WGT * WGF) void gemm_mfma_kernel(const uint8_t
         constexpr int SET = decltype(setc)::value, S = decltype(sc)::value, BUF = decltype(bufc)::value;
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            const uint8_t* pF = smem + rowF0 + aC[S][r] + BUF * LDS_F;
-            const uint8_t* pT = smem + rowT0 + aC[S][r] + BUF * LDS_T;
+            const uint8_t* pF = stage(bufc) + rowF0 + aC[S][r];
+            const uint8_t* pT = stage(bufc) + rowT0 + aC[S][r];
 #pragma unroll
             for (int b = 0; b < NBF; ++b) fF[SET][b][r] = *(const uint4*)(pF + b * 32 * ROWB);
 #pragma unroll
@@ -204,7 +214,7 @@ __global__ __launch_bounds__(64 * WGT * WGF) void gemm_mfma_kernel(const uint8_t
     // it the next step's first fragments load while the last MFMAs run.
     auto kstep = [&](auto bufc, int kt) {
         constexpr int BUF = decltype(bufc)::value;
-        if (kt + NS - 1 < nk) issue(kt + NS - 1, (BUF + NS - 1) % NS);
+        if (kt + NS - 1 < nk) issue(kt + NS - 1, std::integral_constant<int, (BUF + NS - 1) % NS>{});
         static_for<E::SUB - 1>([&](auto s) {
             load_frags(std::integral_constant<int, (s + 1) & 1>{}, std::integral_constant<int, s + 1>{}, bufc);
             mfmas(std::integral_constant<int, s & 1>{});
@@ -220,9 +230,9 @@ __global__ __launch_bounds__(64 * WGT * WGF) void gemm_mfma_kernel(const uint8_t
         __builtin_amdgcn_sched_barrier(0);
     };
 
-#pragma unroll
-    for (int b = 0; b < NS - 1; ++b)
+    static_for<NS - 1>([&](auto b) {
         if (b < nk) issue(b, b);
+    });
     if (NS - 1 <= nk) __builtin_amdgcn_s_waitcnt(WAIT_KEEP);
     else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -265,20 +275,220 @@ __global__ __launch_bounds__(64 * WGT * WGF) void gemm_mfma_kernel(const uint8_t
 #endif  // device pass only: the host pass keeps just the launch stub
 }
 
+// Ping-pong variant for the large projections: 256 x 256 tile, 8 waves in two
+// groups of four (one wave of each group per SIMD), wave tile 128 tokens x 64
+// features. The groups run half a step apart: while one group issues its
+// MFMAs for K step k, the other reads all of its fragments of a step from LDS
+// (and group A also starts the memory -> LDS loads of step k + 1), so each
+// SIMD always has a wave feeding the matrix core. Every phase ends in a
+// workgroup barrier; group B takes one extra barrier at the start and group A
+// one at the end. Two LDS stages: step k + 1 is loaded while step k is read,
+// and its loads have two phases to land.
+template <bool FP8, int MODE, typename TOUT>
+__global__ __launch_bounds__(512) void gemm_pingpong_kernel(const uint8_t* __restrict__ A,
+                                                            const uint8_t* __restrict__ W0,
+                                                            const uint8_t* __restrict__ W1, int M, int N, int K,
+                                                            EpiParams ep) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    using E = Elem<FP8>;
+    constexpr int BT = 256, BF = 256, WT = 128, WF = 64;
+    constexpr int NBT = WT / 32, NBF = WF / 32;
+    constexpr int ESZ = FP8 ? 1 : 2;
+    constexpr int LDS_T = BT * ROWB, LDS_F = BF * ROWB;
+    constexpr int NR = FP8 ? 2 : 1;
+
+    // one LDS array per stage (feature tile, then token tile): see gemm_mfma_kernel
+    __shared__ __attribute__((aligned(16))) uint8_t st0[LDS_F + LDS_T];
+    __shared__ __attribute__((aligned(16))) uint8_t st1[LDS_F + LDS_T];
+    auto stage = [&](auto bc) -> uint8_t* {
+        if constexpr (decltype(bc)::value == 0) return st0;
+        else return st1;
+    };
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;                 // 0: group A (loads + compute), 1: group B
+    const int wt = wave & 1, wf = (wave >> 1) & 3;
+
+    const int ntt = (M + BT - 1) / BT;
+    const int ntf = N / BF;
+    const int ntiles = ntt * ntf;
+    int tile = xcd_remap(blockIdx.x, ntiles);
+    constexpr int GM = 4;
+    const int group = tile / (GM * ntf);
+    const int first_t = group * GM;
+    const int gsz = min(ntt - first_t, GM);
+    const int in_g = tile - group * GM * ntf;
+    const int t0 = (first_t + in_g % gsz) * BT;
+    const int f0 = (in_g / gsz) * BF;
+
+    const int rowbytes = K * ESZ;
+    const int lrow = lane & 31, lhalf = lane >> 5;
+
+    // memory -> LDS, by group A only: wave a (0..3) fills rows 32 i + 8 a .. +7
+    // of each tile (i = 0..7), lanes fetching swizzled chunks
+    const int a4 = wave & 3;
+    const int r8 = 8 * a4 + (lane >> 3);
+    const int cswz = ((lane & 7) ^ swz(r8, 0)) * 16;
+    const int tvalid = min(M - t0, BT);
+    const __amdgpu_buffer_rsrc_t rsT = make_rsrc(A + (size_t)t0 * rowbytes, tvalid * rowbytes);
+    int voT[BT / 32];
+#pragma unroll
+    for (int i = 0; i < BT / 32; ++i) voT[i] = (32 * i + r8) * rowbytes + cswz;
+    __amdgpu_buffer_rsrc_t rsF0, rsF1;
+    if constexpr (MODE == EPI_SWIGLU) {
+        rsF0 = make_rsrc(W0 + (size_t)(f0 / 2) * rowbytes, (BF / 2) * rowbytes);
+        rsF1 = make_rsrc(W1 + (size_t)(f0 / 2) * rowbytes, (BF / 2) * rowbytes);
+    } else {
+        rsF0 = make_rsrc(W0 + (size_t)f0 * rowbytes, BF * rowbytes);
+        rsF1 = rsF0;
+    }
+    const int voF = r8 * rowbytes + cswz;
+    const int nk = K / E::BK;
+
+    auto issue = [&](int kt, auto bufc) {
+        const int koff = kt * ROWB;
+        LDSPTR lt = (LDSPTR)(stage(bufc) + LDS_F + a4 * 1024);
+        LDSPTR lf = (LDSPTR)(stage(bufc) + a4 * 1024);
+#pragma unroll
+        for (int i = 0; i < BT / 32; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsT, lt + i * 4096, 16, voT[i] + koff, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < BF / 32; ++i) {
+            if constexpr (MODE == EPI_SWIGLU)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds((i & 1) ? rsF1 : rsF0, lf + i * 4096, 16, voF + koff,
+                                                         (i >> 1) * 32 * rowbytes, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsF0, lf + i * 4096, 16, voF + koff, i * 32 * rowbytes, 0, 0);
+        }
+    };
+
+    const int xs = (lrow >> 1) & 7;
+    const int rowF0 = (wf * WF + lrow) * ROWB, rowT0 = LDS_F + (wt * WT + lrow) * ROWB;
+    uint32_t aC[E::SUB][NR];
+#pragma unroll
+    for (int s = 0; s < E::SUB; ++s)
+#pragma unroll
+        for (int r = 0; r < NR; ++r) aC[s][r] = ((NR * (2 * s + lhalf) + r) ^ xs) * 16;
+
+    f32x16 acc[NBT][NBF];
+#pragma unroll
+    for (int a = 0; a < NBT; ++a)
+#pragma unroll
+        for (int b = 0; b < NBF; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+    uint4 fF[E::SUB][NBF][NR], fT[E::SUB][NBT][NR];   // one whole step of fragments
+    auto read_step = [&](auto bufc) {
+        constexpr int BUF = decltype(bufc)::value;
+#pragma unroll
+        for (int s = 0; s < E::SUB; ++s)
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                const uint8_t* pF = stage(bufc) + rowF0 + aC[s][r];
+                const uint8_t* pT = stage(bufc) + rowT0 + aC[s][r];
+#pragma unroll
+                for (int b = 0; b < NBF; ++b) fF[s][b][r] = *(const uint4*)(pF + b * 32 * ROWB);
+#pragma unroll
+                for (int a = 0; a < NBT; ++a) fT[s][a][r] = *(const uint4*)(pT + a * 32 * ROWB);
+            }
+    };
+    auto compute_step = [&]() {
+#pragma unroll
+        for (int s = 0; s < E::SUB; ++s)
+#pragma unroll
+            for (int a = 0; a < NBT; ++a)
+#pragma unroll
+                for (int b = 0; b < NBF; ++b) {
+                    if constexpr (!FP8) {
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8_v, fF[s][b][0]), __builtin_bit_cast(bf16x8_v, fT[s][a][0]),
+                            acc[a][b], 0, 0, 0);
+                    } else {
+                        const uint4 x0 = fF[s][b][0], x1 = fF[s][b][1], y0 = fT[s][a][0], y1 = fT[s][a][1];
+                        const i32x8 fa = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                                          (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+                        const i32x8 fb = {(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w,
+                                          (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
+                        acc[a][b] =
+                            __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, acc[a][b], 0, 0, 0, 0, 0, 0);
+                    }
+                }
+    };
+    // one step: memory phase (reads of stage BUF; group A also issues step
+    // kt + 1), barrier, compute phase, (A: wait for step kt + 1), barrier
+    auto step = [&](auto bufc, int kt) {
+        constexpr int BUF = decltype(bufc)::value;
+        if (grp == 0 && kt + 1 < nk) issue(kt + 1, std::integral_constant<int, BUF ^ 1>{});
+        read_step(bufc);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's fragments are in registers
+        __syncthreads();
+        __builtin_amdgcn_s_setprio(1);
+        compute_step();
+        __builtin_amdgcn_s_setprio(0);
+        if (grp == 0) __builtin_amdgcn_s_waitcnt(0);   // its LDS fills for step kt + 1 have landed
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+    };
+
+    if (grp == 0) issue(0, std::integral_constant<int, 0>{});
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (grp == 1) __syncthreads();          // group B runs one phase behind
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(std::integral_constant<int, 0>{}, kt);
+        if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
+    }
+    if (grp == 0) __syncthreads();          // match group B's barrier count
+
+    // ---------------------------------------------------------------- epilogue
+    if constexpr (MODE == EPI_SWIGLU) {
+        const float sg = epi_scale(ep.amax_a, ep.s_w);
+        const float su = epi_scale(ep.amax_a, ep.s_w2);
+        float mx = 0.f;
+        static_for<NBT>([&](auto a) {
+            const int m = t0 + wt * WT + a * 32 + lrow;
+            static_for<NBF / 2>([&](auto bp) {
+                const int fbase = f0 / 2 + wf * (WF / 2) + bp * 32;
+                using UT = std::conditional_t<FP8, float, TOUT>;
+                mx = fmaxf(mx, epi_block_swiglu<UT>(ep, m, fbase, lhalf, acc[a][2 * bp], acc[a][2 * bp + 1], sg, su));
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        });
+        if (ep.u_amax) {
+            mx = wave_max(mx);
+            if (lane == 0) atomic_max_nonneg(ep.u_amax, mx);
+        }
+    } else {
+        const float sc = epi_scale(ep.amax_a, ep.s_w);
+        static_for<NBT>([&](auto a) {
+            const int m = t0 + wt * WT + a * 32 + lrow;
+            static_for<NBF>([&](auto b) {
+                epi_block<MODE, TOUT>(ep, m, f0 + wf * WF + b * 32, lhalf, acc[a][b], sc);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        });
+    }
+#endif
+}
+
+template <bool FP8, int MODE>
+hipError_t launch_pingpong(const void* A, const void* W0, const void* W1, int M, int N, int K, const EpiParams& ep,
+                           hipStream_t st) {
+    const int tiles = ((M + 255) / 256) * (N / 256);
+    hipLaunchKernelGGL((gemm_pingpong_kernel<FP8, MODE, bf16_t>), dim3(tiles), dim3(512), 0, st,
+                       (const uint8_t*)A, (const uint8_t*)W0, (const uint8_t*)W1, M, N, K, ep);
+    return hipGetLastError();
+}
+
 template <int BT, int BF, int WGT, int WGF, int NS, bool FP8, int MODE>
 hipError_t launch_t(const void* A, const void* W0, const void* W1, int M, int N, int K, const EpiParams& ep,
                     hipStream_t st) {
-    constexpr int smem = NS * (BT + BF) * ROWB;   // NS stages of each operand tile
-    static_assert(smem <= 160 * 1024, "LDS");
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void*)&gemm_mfma_kernel<BT, BF, WGT, WGF, NS, FP8, MODE, bf16_t>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+    static_assert(NS * (BT + BF) * ROWB <= 160 * 1024, "LDS");   // NS stages of each operand tile
     const int tiles = ((M + BT - 1) / BT) * (N / BF);
-    hipLaunchKernelGGL((gemm_mfma_kernel<BT, BF, WGT, WGF, NS, FP8, MODE, bf16_t>), dim3(tiles), dim3(64 * WGT * WGF), smem,
+    hipLaunchKernelGGL((gemm_mfma_kernel<BT, BF, WGT, WGF, NS, FP8, MODE, bf16_t>), dim3(tiles), dim3(64 * WGT * WGF), 0,
                        st, (const uint8_t*)A, (const uint8_t*)W0, (const uint8_t*)W1, M, N, K, ep);
     return hipGetLastError();
 }
@@ -288,10 +498,8 @@ hipError_t dispatch(const void* A, const void* W0, const void* W1, int M, int N,
                     hipStream_t st) {
     // big tiles when there are enough of them to fill 256 CUs several times
     const long t256 = (long)((M + 255) / 256) * (N / 256);
-    if (N % 256 == 0 && t256 >= 512) return launch_t<256, 256, 2, 4, 2, FP8, MODE>(A, W0, W1, M, N, K, ep, st);
-    if (N % 256 == 0 && (long)((M + 127) / 128) * (N / 256) >= 256)
-        return launch_t<128, 256, 2, 2, 3, FP8, MODE>(A, W0, W1, M, N, K, ep, st);
-    return launch_t<128, 128, 2, 2, 3, FP8, MODE>(A, W0, W1, M, N, K, ep, st);
+    if (N % 256 == 0 && t256 >= 512) return launch_pingpong<FP8, MODE>(A, W0, W1, M, N, K, ep, st);
+    return launch_t<128, 128, 2, 2, 2, FP8, MODE>(A, W0, W1, M, N, K, ep, st);
 }
 
 }  // namespace detail

@@ -189,6 +189,8 @@ __global__ void gather_rows_kernel(const uint8_t* __restrict__ x, const int32_t*
 // kept slot nk[p] is a scalar), 8 elements per 16/32-byte access, up to four
 // accesses in flight per thread; the output is written non-temporally (it is
 // not read again by this block).
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_v;
+typedef __attribute__((ext_vector_type(4))) float f32x4_v;
 template <typename T>
 struct Chunk8;
 template <>
@@ -201,7 +203,8 @@ struct Chunk8<bf16_t> {
         o.y = pack_bf2(__uint_as_float(v.y << 16) + d0.z, __uint_as_float(v.y & 0xFFFF0000u) + d0.w);
         o.z = pack_bf2(__uint_as_float(v.z << 16) + d1.x, __uint_as_float(v.z & 0xFFFF0000u) + d1.y);
         o.w = pack_bf2(__uint_as_float(v.w << 16) + d1.z, __uint_as_float(v.w & 0xFFFF0000u) + d1.w);
-        __builtin_nontemporal_store(o, (uint4*)p);
+        const u32x4_v ov = {o.x, o.y, o.z, o.w};
+        __builtin_nontemporal_store(ov, (u32x4_v*)p);
     }
 };
 template <>
@@ -212,8 +215,10 @@ struct Chunk8<float> {
         b = *(const float4*)(p + 4);
     }
     DIT_DEV void add_store(float* p, float4 d0, float4 d1) const {
-        __builtin_nontemporal_store(make_float4(a.x + d0.x, a.y + d0.y, a.z + d0.z, a.w + d0.w), (float4*)p);
-        __builtin_nontemporal_store(make_float4(b.x + d1.x, b.y + d1.y, b.z + d1.z, b.w + d1.w), (float4*)(p + 4));
+        const f32x4_v u = {a.x + d0.x, a.y + d0.y, a.z + d0.z, a.w + d0.w};
+        const f32x4_v v = {b.x + d1.x, b.y + d1.y, b.z + d1.z, b.w + d1.w};
+        __builtin_nontemporal_store(u, (f32x4_v*)p);
+        __builtin_nontemporal_store(v, (f32x4_v*)(p + 4));
     }
 };
 
