@@ -39,9 +39,23 @@ DIT_DEV int rho(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                                                            const bf16_t* __restrict__ Vt, bf16_t* __restrict__ O,
                                                            int S, int Sp, int nh, float c, float* o_amax) {
+#if defined(__HIP_DEVICE_COMPILE__)
     constexpr int DH = 128;
-    __shared__ __attribute__((aligned(16))) uint8_t sK[2][KT * DH * 2];
-    __shared__ __attribute__((aligned(16))) uint8_t sV[2][DH * KT * 2];
+    // one LDS array per stage and operand: the memory -> LDS loads into one
+    // stage then do not alias, for the compiler, the reads of the other, and
+    // every LDS address is a per-lane offset plus a constant
+    __shared__ __attribute__((aligned(16))) uint8_t sK0[KT * DH * 2];
+    __shared__ __attribute__((aligned(16))) uint8_t sK1[KT * DH * 2];
+    __shared__ __attribute__((aligned(16))) uint8_t sV0[DH * KT * 2];
+    __shared__ __attribute__((aligned(16))) uint8_t sV1[DH * KT * 2];
+    auto stK = [&](auto bc) -> uint8_t* {
+        if constexpr (decltype(bc)::value == 0) return sK0;
+        else return sK1;
+    };
+    auto stV = [&](auto bc) -> uint8_t* {
+        if constexpr (decltype(bc)::value == 0) return sV0;
+        else return sV1;
+    };
 
     const int nq = (S + 127) / 128;
     const int blk = xcd_remap(blockIdx.x, nq * nh);
@@ -70,9 +84,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
     const int voK = krow * 256 + swzK(krow, lane & 15) * 16;
     const int vrow = 8 * wave + (lane >> 3);
     const int voV = vrow * Sp * 2 + swzV(vrow, lane & 7) * 16;
-    auto issue = [&](int kt, int buf) {
-        LDSPTR lk = (LDSPTR)(sK[buf] + wave * 1024);
-        LDSPTR lv = (LDSPTR)(sV[buf] + wave * 1024);
+    auto issue = [&](int kt, auto bc) {
+        LDSPTR lk = (LDSPTR)(stK(bc) + wave * 1024);
+        LDSPTR lv = (LDSPTR)(stV(bc) + wave * 1024);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, lk + i * 4096, 16, voK, kt * KT * 256 + i * 16 * 256, 0, 0);
@@ -80,37 +94,48 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
         }
     };
 
+    // Per-lane LDS offsets. K fragment (block b, dh step s): row b 32 + rho(lrow),
+    // chunk 2 s + h; the swizzle term depends on row & 15 = rho(lrow) & 15 only,
+    // so block b is a constant 8192 bytes further. V^T fragment (dh block d,
+    // key step ks): row d 32 + lrow, chunk 2 ks + h; block d is 4096 further.
+    int kOff[8], vOff[4];
+    {
+        const int kr = rho(lrow);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) kOff[s] = kr * 256 + swzK(kr, 2 * s + lhalf) * 16;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) vOff[ks] = lrow * 128 + swzV(lrow, 2 * ks + lhalf) * 16;
+    }
+
     f32x16 o[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
-    float mrun = -INFINITY, lrun = 0.f;
+    float mrun = -INFINITY, lrun = 0.f;   // lrun: this lane's half of the row sum
+    const bf16x2_v ones = {(__bf16)1.f, (__bf16)1.f};
 
     const int nkt = (S + KT - 1) / KT;
-    issue(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
 
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nkt) issue(kt + 1, buf ^ 1);
-        const uint8_t* bK = sK[buf];
-        const uint8_t* bV = sV[buf];
+    auto tile = [&](int kt, auto bc) {
+        if (kt + 1 < nkt) issue(kt + 1, std::integral_constant<int, 1 - decltype(bc)::value>{});
+        const uint8_t* bK = stK(bc);
+        const uint8_t* bV = stV(bc);
 
         // scores S^T for 2 blocks of 32 keys (row i of block b is key 32 b + rho(i))
+        // (the two blocks interleave, so no MFMA waits on the one before it)
         f32x16 sc[2];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) sc[b][r] = 0.f;
-            const int row = b * 32 + rho(lrow);
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                bf16x8_v kf = *(const bf16x8_v*)(bK + row * 256 + swzK(row, 2 * s + lhalf) * 16);
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const bf16x8_v kf = *(const bf16x8_v*)(bK + kOff[s] + b * 8192);
                 sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sc[b], 0, 0, 0);
             }
-        }
         // mask keys >= S (only in the last tile)
         const int k0 = kt * KT;
         if (k0 + KT > S) {
@@ -118,7 +143,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
             for (int b = 0; b < 2; ++b)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    int key = k0 + b * 32 + rho(8 * (r >> 2) + 4 * lhalf + (r & 3));
+                    const int key = k0 + b * 32 + rho(8 * (r >> 2) + 4 * lhalf + (r & 3));
                     if (key >= S) sc[b][r] = -INFINITY;
                 }
         }
@@ -132,15 +157,22 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
         const float alpha = __builtin_amdgcn_exp2f((mrun - mnew) * c);
         mrun = mnew;
         const float mc = -mnew * c;
+        // P = exp2(c s - c m), rounded to bf16 once: the packed values feed both
+        // the P V product and the row sum (dot product with (1, 1)), so the
+        // normaliser sums exactly the weights that multiplied V
+        uint32_t pk[2][8];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                pk[b][j] = pack_bf2(__builtin_amdgcn_exp2f(fmaf(sc[b][2 * j], c, mc)),
+                                    __builtin_amdgcn_exp2f(fmaf(sc[b][2 * j + 1], c, mc)));
         float psum = 0.f;
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float p = __builtin_amdgcn_exp2f(fmaf(sc[b][r], c, mc));
-                sc[b][r] = p;
-                psum += p;
-            }
+            for (int j = 0; j < 8; ++j)
+                psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, pk[b][j]), ones, psum, false);
         lrun = lrun * alpha + psum;
         if (__ballot(alpha != 1.f)) {
 #pragma unroll
@@ -148,28 +180,30 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
         }
-        // P^T fragments: key step ks = registers 8 (ks % 2) .. +7 of block ks / 2,
-        // i.e. keys 16 ks + 8 h + 0..7 for lane half h
-        bf16x8_v pf[4];
+        // O^T += V^T P^T. P^T key step ks = registers 8 (ks % 2) .. +7 of block
+        // ks / 2, i.e. keys 16 ks + 8 h + 0..7 for lane half h; the A operand
+        // lane (dh row, half h) reads the same keys of V^T
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const int b = ks >> 1, r0 = 8 * (ks & 1);
-            uint4 w = make_uint4(pack_bf2(sc[b][r0 + 0], sc[b][r0 + 1]), pack_bf2(sc[b][r0 + 2], sc[b][r0 + 3]),
-                                 pack_bf2(sc[b][r0 + 4], sc[b][r0 + 5]), pack_bf2(sc[b][r0 + 6], sc[b][r0 + 7]));
-            pf[ks] = __builtin_bit_cast(bf16x8_v, w);
-        }
-        // O^T += V^T P^T; the A operand lane (dh row, half h) reads keys 16 ks + 8 h .. +7
+            const int b = ks >> 1, j0 = 4 * (ks & 1);
+            const bf16x8_v pf =
+                __builtin_bit_cast(bf16x8_v, make_uint4(pk[b][j0], pk[b][j0 + 1], pk[b][j0 + 2], pk[b][j0 + 3]));
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const int row = d * 32 + lrow;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                bf16x8_v vf = *(const bf16x8_v*)(bV + row * 128 + swzV(row, 2 * ks + lhalf) * 16);
-                o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[d], 0, 0, 0);
+            for (int d = 0; d < 4; ++d) {
+                const bf16x8_v vf = *(const bf16x8_v*)(bV + vOff[ks] + d * 4096);
+                o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[d], 0, 0, 0);
             }
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    };
+
+    issue(0, std::integral_constant<int, 0>{});
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = 0; kt < nkt; kt += 2) {
+        tile(kt, std::integral_constant<int, 0>{});
+        if (kt + 1 < nkt) tile(kt + 1, std::integral_constant<int, 1>{});
     }
 
     const float ltot = lrun + __shfl_xor(lrun, 32, 64);
@@ -196,6 +230,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
         mx = wave_max(mx);
         if (lane == 0) atomic_max_nonneg(o_amax, mx);
     }
+#endif  // device pass only: the host pass keeps just the launch stub
 }
 
 // fp32 attention: one thread per query, 64 queries of one head per block,

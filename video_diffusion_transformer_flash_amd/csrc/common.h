@@ -133,6 +133,19 @@ DIT_DEV float2 rope_cs(const Rope& r, int d, int3 c) {
     return r.tab_w[c.z * (r.rw >> 1) + (d >> 1)];
 }
 
+// Workgroup barrier for LDS pipelines fed by memory -> LDS loads: waits for
+// this wave's LDS instructions only (lgkmcnt 0). __syncthreads() would also
+// wait for every load still in flight (vmcnt 0), draining the deeper stages of
+// the pipeline; those loads are waited for explicitly, per stage, with
+// s_waitcnt vmcnt(n) before the barrier. The empty asm statements keep the
+// compiler from moving memory accesses across it.
+DIT_DEV void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0), vmcnt / expcnt untouched
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Raw buffer resource over [p, p + bytes) (reads past the end return zero).
 // The pieces go through readfirstlane so that the compiler keeps the
 // descriptor in scalar registers (a vector-held descriptor would turn every
