@@ -10,8 +10,17 @@ broadcast onto all 12240 video positions). Inputs are resident in HBM before
 the timed region. The same block with compression off (all 12628 tokens) is
 timed as a second line item.
 
+The bandwidth-bound kernels (gather of the kept rows, nearest-kept broadcast
+plus residual) are also timed alone on the same shapes with the 256 MB
+Infinity Cache flushed before every repetition (a 1 GiB write), which is the
+number their HBM roofline fraction is judged on.
+
 Prints one JSON line (see the repository's bench contract).
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu] [--no-off]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu] [--no-off] [--copy-calib]
+
+--copy-calib adds three plain 1 GiB device copies after the timed region: the
+reference dispatches that scale rocprofv3's FETCH_SIZE / WRITE_SIZE counters
+to bytes (see TRAFFIC).
 """
 from __future__ import annotations
 
@@ -24,6 +33,31 @@ import time
 METRIC = "Flash DiT block ms & TFLOP/s (% bf16 MFMA peak), 540p/22f, compression on/off"
 PEAK_BF16 = 2500.0     # TFLOP/s, dense MFMA, MI355X
 PEAK_HBM = 8000.0      # GB/s
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+# HBM traffic of the dominant kernel, from two rocprofv3 counter runs of
+# `bench.py --no-cpu --no-off --steps 2 --warmup 1 --copy-calib` (FETCH_SIZE,
+# then WRITE_SIZE; KiB per dispatch), each divided by what the same counter
+# reads per byte of a plain 1 GiB copy. Valid only for the kernel source it was
+# taken on (sha256 of the listed files); otherwise reported as null.
+TRAFFIC = {}
+
+
+def _src_sha(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(HERE, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel):
+    t = TRAFFIC.get(kernel)
+    if not t or _src_sha(t["files"]) != t["sha"]:
+        return None
+    return {"bytes": t["fetch_bytes"] + t["write_bytes"], "fetch_bytes": t["fetch_bytes"],
+            "write_bytes": t["write_bytes"], "copy_scale": t["copy_scale"], "source": t["source"]}
 
 
 def block_flops(d, S):
@@ -111,6 +145,54 @@ def kernel_table(kern, flops, bytes_):
     return out
 
 
+def bandwidth_kernels(d, reps=10):
+    """Gather and broadcast alone on the workload's shapes, Infinity Cache
+    flushed (1 GiB write) before every repetition; median of reps."""
+    import torch
+    import video_diffusion_transformer_flash_amd as V
+    Hk, Wk = V.keep_dims(d.H, d.W, d.stride)
+    Nk, Nv, D = d.T * Hk * Wk, d.n_video, d.d_model
+    g = torch.Generator(device="cuda").manual_seed(1000 + d.seed)
+    x = torch.randn(Nv, D, device="cuda", generator=g).to(torch.bfloat16)
+    delta = torch.randn(Nk, D, device="cuda", generator=g)
+    keep = V.keep_index(d.T, d.H, d.W, d.stride)
+    nk = V.nearest_kept_map(d.T, d.H, d.W, d.stride)
+    xc = torch.empty(Nk, D, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(x)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    fns = {"gather_kept": lambda: V.gather_kept(x, keep, out=xc),
+           "broadcast_residual": lambda: V.broadcast_residual(x, delta, nk, out=out)}
+    byts = {"gather_kept": 2 * Nk * D * 2, "broadcast_residual": (2 * Nv * 2 + Nk * 4) * D}
+    times = {k: [] for k in fns}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for r in range(reps + 2):
+        for name, fn in fns.items():
+            flush.fill_(r & 255)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if r >= 2:
+                times[name].append(e0.elapsed_time(e1))
+    res = {}
+    for name, ts in times.items():
+        ms = sorted(ts)[len(ts) // 2]
+        gbs = byts[name] / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 4), "bytes": byts[name], "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM, 4)}
+    del flush
+    return res
+
+
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """Plain device copies of a known size (reference dispatches for the HBM counters)."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+
+
 def cpu_baseline(d, host, compress):
     """The fp64 oracle on the host cores: one full block of the same workload."""
     import numpy as np
@@ -150,6 +232,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-off", action="store_true", help="skip the compression-off line item")
+    ap.add_argument("--copy-calib", action="store_true", help="add 1 GiB reference copies (counter calibration)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures the block on one GPU; the multi-GPU sharding is not part of this build "
@@ -176,14 +259,20 @@ def main():
                                f"(3348 kept video + 256 text + 132 audio = {S} tokens), broadcast to 12240 positions",
                    "tflop_per_step": round(tflop, 4), "frac_of_bf16_peak": round(value / PEAK_BF16, 4)},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4),
+                     "flop_per_launch": flops[dom], "launch_ms": round(dom_ms, 4), "traffic": traffic_for(dom)},
         "kernels": table,
     }
-    bc = table.get("broadcast_residual")
-    if bc:
-        line["hbm_roofline"] = {"bound": "hbm", "kernel": "broadcast_residual", "achieved": bc["GB/s"],
-                                "peak": PEAK_HBM, "unit": "GB/s", "frac": bc["frac"],
-                                "bytes_per_launch": byts["broadcast_residual"]}
+    if a.copy_calib:
+        copy_calibration()
+    torch.cuda.empty_cache()
+    bw = bandwidth_kernels(d)
+    bc = bw["broadcast_residual"]
+    line["hbm_roofline"] = {"bound": "hbm", "kernel": "broadcast_residual", "achieved": bc["GB/s"],
+                            "peak": PEAK_HBM, "unit": "GB/s", "frac": bc["frac"], "bytes_per_launch": bc["bytes"],
+                            "launch_ms": bc["ms"], "cache": "Infinity Cache flushed before each launch",
+                            "traffic": traffic_for("broadcast_residual")}
+    line["bandwidth_kernels"] = bw
     torch.cuda.empty_cache()
     if not a.no_off:
         d2, step2, S2, _, host2 = setup("540p_off", False)

@@ -87,6 +87,7 @@ int validate_dims(const dit_dims* d) {
         const int I = d->n_heads * d->head_dim;
         if (d->head_dim != 128) return DIT_EUNSUPPORTED;
         if (d->d_model % 128 || I % 128 || d->d_ffn % 128) return DIT_EUNSUPPORTED;
+        if (d->rope_t % 8 || d->rope_h % 8 || d->rope_w % 8) return DIT_EUNSUPPORTED;
     }
     return DIT_OK;
 }
@@ -94,7 +95,7 @@ int validate_dims(const dit_dims* d) {
 // ------------------------------------------------------------------ workspace plan
 struct Plan {
     int S, Sp, nv_seq;
-    size_t tab, n, rinv, q, k, vt, o, o8, h, u, u8, delta, sc, total;
+    size_t tab, rrows, n, rinv, q, k, vt, o, o8, h, u, u8, delta, sc, total;
     int ntab_t;
 };
 
@@ -115,6 +116,7 @@ Plan make_plan(const dit_dims& d, int nv_seq, bool delta) {
     };
     const size_t ntab = (size_t)p.ntab_t * (d.rope_t / 2) + (size_t)d.H * (d.rope_h / 2) + (size_t)d.W * (d.rope_w / 2);
     p.tab = take(std::max<size_t>(ntab, 1) * sizeof(float2));
+    p.rrows = d.act_dtype == DIT_F32 ? 0 : take((size_t)p.S * (d.head_dim / 2) * sizeof(float2));
     p.n = take((size_t)p.S * D * (fp8 ? 1 : es));
     p.rinv = take((size_t)p.S * 4);
     p.q = take((size_t)d.n_heads * p.Sp * d.head_dim * es);
@@ -154,6 +156,11 @@ int run_block(const dit_dims& d, const dit_block_weights& w, const SeqIn& in, co
     rope.rt = d.rope_t; rope.rh = d.rope_h; rope.rw = d.rope_w;
     rope.H = d.H; rope.W = d.W;
     rope.nt = in.nt; rope.nv = in.nv;
+    if (d.act_dtype != DIT_F32) {
+        TR("rope_rows");
+        HIPCHK(rope_rows_launch(rope, (float2*)(ws + P.rrows), P.S, d.head_dim / 2, st));
+        rope.rows = (const float2*)(ws + P.rrows);
+    }
 
     void* n = ws + P.n;
     float* rinv = (float*)(ws + P.rinv);

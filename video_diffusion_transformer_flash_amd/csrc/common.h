@@ -93,6 +93,7 @@ struct Rope {
     const float2* tab_h;   // [H][rh/2]
     const float2* tab_w;   // [W][rw/2]
     const int32_t* vpos;   // video token j -> flat position (nullptr: j)
+    const float2* rows;    // per sequence row: (cos, sin) of all head_dim / 2 pairs (MFMA epilogue)
     int rt, rh, rw;
     int H, W;
     int nt, nv;            // text / video token counts in the sequence

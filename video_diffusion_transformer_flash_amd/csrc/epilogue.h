@@ -170,6 +170,110 @@ DIT_DEV void epi_down(const EpiParams& p, int m, int n0, float v[4], float sc) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Row layout (MFMA kernels): the accumulators are staged through LDS and each
+// lane then takes eight consecutive outputs n0 .. n0 + 7 (n0 % 8 == 0) of one
+// token m, already scaled; every global access is 16 or 32 contiguous bytes.
+
+template <typename T> DIT_DEV void store8(T* p, const float v[8]);
+template <> DIT_DEV void store8<float>(float* p, const float v[8]) {
+    ((float4*)p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    ((float4*)p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+template <> DIT_DEV void store8<bf16_t>(bf16_t* p, const float v[8]) {
+    *(uint4*)p = make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7]));
+}
+template <typename T> DIT_DEV void load8(const T* p, float v[8]);
+template <> DIT_DEV void load8<float>(const float* p, float v[8]) {
+    const float4 a = ((const float4*)p)[0], b = ((const float4*)p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+template <> DIT_DEV void load8<bf16_t>(const bf16_t* p, float v[8]) {
+    const uint4 x = *(const uint4*)p;
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+
+// q or k (dst = p.q or p.k): rotary embedding with the row's (cos, sin) pairs
+// (32 contiguous bytes per lane), head-major row; rows [M, Mpad) zero
+template <typename T>
+DIT_DEV void epi8_qk(const EpiParams& p, void* dst, int head, int m, int d0, float v[8]) {
+    if (m >= p.Mpad) return;
+    if (m >= p.M) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.f;
+    } else {
+        const float4* t = (const float4*)(p.rope.rows + (size_t)m * (p.dh >> 1) + (d0 >> 1));
+        const float4 c01 = t[0], c23 = t[1];
+        const float2 cs[4] = {make_float2(c01.x, c01.y), make_float2(c01.z, c01.w), make_float2(c23.x, c23.y),
+                              make_float2(c23.z, c23.w)};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float a = v[2 * j], b = v[2 * j + 1];
+            v[2 * j] = a * cs[j].x - b * cs[j].y;
+            v[2 * j + 1] = a * cs[j].y + b * cs[j].x;
+        }
+    }
+    store8<T>((T*)dst + ((size_t)head * p.Sp + m) * p.dh + d0, v);
+}
+
+template <typename T>
+DIT_DEV void epi8_resid(const EpiParams& p, int m, int n0, const float v[8]) {
+    if (m >= p.M) return;
+    float x[8];
+    load8<T>(seq_row<T>(p.xin, m, p.D) + n0, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] += v[i];
+    store8<float>(p.h + (size_t)m * p.D + n0, x);
+}
+
+// u = silu(gate) * up for ffn features f0 .. f0 + 7; returns max |stored u|
+template <typename T>
+DIT_DEV float epi8_swiglu(const EpiParams& p, int m, int f0, const float g[8], const float up[8]) {
+    if (m >= p.M) return 0.f;
+    float o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = g[i] / (1.f + __expf(-g[i])) * up[i];
+    store8<T>((T*)p.u + (size_t)m * p.F + f0, o);
+    float mx = 0.f;
+    if (p.u_amax) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(stored<T>(o[i])));
+    }
+    return mx;
+}
+
+template <typename T>
+DIT_DEV void epi8_down(const EpiParams& p, int m, int n0, const float v[8]) {
+    if (m >= p.M) return;
+    float y[8];
+    load8<float>(p.hres + (size_t)m * p.D + n0, y);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] += v[i];
+    const SeqOut& o = p.out;
+    const int nt = p.xin.nt, nv = p.xin.nv;
+    if (m < nt) {
+        store8<T>((T*)o.yt + (size_t)m * p.D + n0, y);
+    } else if (m < nt + nv) {
+        const int j = m - nt;
+        if (o.delta) {
+            float x[8];
+            load8<T>(seq_row<T>(p.refin, m, p.D) + n0, x);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) y[i] -= x[i];
+            store8<float>(o.delta + (size_t)j * p.D + n0, y);
+        } else {
+            store8<T>((T*)o.yv + (size_t)j * p.D + n0, y);
+        }
+    } else {
+        store8<T>((T*)o.ya + (size_t)(m - nt - nv) * p.D + n0, y);
+    }
+}
+
 // Compile-time loop: f(integral_constant<int, i>) for i = 0 .. N-1, so that
 // register arrays are only ever indexed by constants.
 template <int N, int I = 0, class F>

@@ -374,33 +374,97 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
     }
 
     // ---------------------------------------------------------------- epilogue
+    // Each wave stages 32 tokens x its 64 outputs (fp32, scaled) per round in
+    // a private LDS slice, rows padded to 272 bytes so that both the writes
+    // from the accumulator layout and the row reads are free of bank
+    // conflicts, then works in row layout: a lane takes eight consecutive
+    // outputs of one token (for v^T: one output column and eight consecutive
+    // tokens), so every global load and store is 16-32 contiguous bytes per
+    // lane and 128-256 per token row. The pipeline's LDS is free here: every
+    // wave has passed the last step's barrier, after which nobody reads it.
+    static_assert(WF == 64, "a wave's rows hold 64 outputs");
+    constexpr int RS = 64 * 4 + 16;
+    static_assert((NW / 2) * 32 * RS <= SB, "epilogue slices fit in two stages");
+    uint8_t* wl = ((wave & 1) ? st1 : st0) + (wave >> 1) * 32 * RS;
+    float scb[NBF];
     if constexpr (MODE == EPI_SWIGLU) {
-        const float sg = epi_scale(ep.amax_a, ep.s_w);
-        const float su = epi_scale(ep.amax_a, ep.s_w2);
-        float mx = 0.f;
-        static_for<NBT>([&](auto a) {
-            const int m = t0 + wt * WT + a * 32 + lrow;
-            static_for<NBF / 2>([&](auto bp) {
-                const int fbase = f0 / 2 + wf * (WF / 2) + bp * 32;
-                // fp8: u stays fp32 so that its e4m3 codes come from full-precision values
-                using UT = std::conditional_t<FP8, float, TOUT>;
-                mx = fmaxf(mx, epi_block_swiglu<UT>(ep, m, fbase, lhalf, acc[a][2 * bp], acc[a][2 * bp + 1], sg, su));
-                __builtin_amdgcn_sched_barrier(0);   // one block at a time: bounded register pressure
+        const float sg = epi_scale(ep.amax_a, ep.s_w), su = epi_scale(ep.amax_a, ep.s_w2);
+#pragma unroll
+        for (int b = 0; b < NBF; ++b) scb[b] = (b & 1) ? su : sg;   // 32-row blocks: gate, up
+    } else {
+        const float sc = epi_scale(ep.amax_a, ep.s_w);
+#pragma unroll
+        for (int b = 0; b < NBF; ++b) scb[b] = sc;
+    }
+    const int fw = f0 + wf * WF;          // first output (for SwiGLU: interleaved gate/up row) of the wave
+    float mx = 0.f;
+    auto row8 = [&](int r, int c0, float v[8]) {
+        const float4 x = *(const float4*)(wl + r * RS + c0 * 4), y = *(const float4*)(wl + r * RS + c0 * 4 + 16);
+        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w; v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+    };
+    static_for<NBT>([&](auto a) {
+        // accumulator layout -> LDS rows: lane (token lrow) holds outputs b 32 + 8 g + 4 h .. + 3
+        static_for<NBF>([&](auto b) {
+            static_for<4>([&](auto g) {
+                *(float4*)(wl + lrow * RS + (b * 32 + 8 * g + 4 * lhalf) * 4) =
+                    make_float4(acc[a][b][4 * g] * scb[b], acc[a][b][4 * g + 1] * scb[b],
+                                acc[a][b][4 * g + 2] * scb[b], acc[a][b][4 * g + 3] * scb[b]);
             });
         });
+        const int mb = t0 + wt * WT + a * 32;   // first token of the round
+        if constexpr (MODE == EPI_QKV) {
+            const int which = fw / ep.I;
+            const int rem = fw - which * ep.I;
+            const int head = rem / ep.dh;
+            const int dw = rem - head * ep.dh;  // head-local feature of output column 0
+            if (which < 2) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = (lane >> 3) + 8 * i, c0 = (lane & 7) * 8;
+                    float v[8];
+                    row8(r, c0, v);
+                    epi8_qk<TOUT>(ep, which ? ep.k : ep.q, head, mb + r, dw + c0, v);
+                }
+            } else {
+                // v^T [head][dh][Sp]: lane = output column, eight consecutive tokens per store
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int m0 = mb + 8 * i;
+                    if (m0 < ep.Mpad) {
+                        float v[8];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) v[j] = m0 + j < ep.M ? *(const float*)(wl + (8 * i + j) * RS + lane * 4) : 0.f;
+                        store8<TOUT>((TOUT*)ep.vt + ((size_t)head * ep.dh + dw + lane) * ep.Sp + m0, v);
+                    }
+                }
+            }
+        } else if constexpr (MODE == EPI_SWIGLU) {
+            // columns 0..31 gate, 32..63 up of ffn features fw / 2 .. + 31; four lanes per token
+            using UT = std::conditional_t<FP8, float, TOUT>;   // fp8: u stays fp32 until its quantisation
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = (lane >> 2) + 16 * i, j0 = (lane & 3) * 8;
+                float g[8], u[8];
+                row8(r, j0, g);
+                row8(r, 32 + j0, u);
+                mx = fmaxf(mx, epi8_swiglu<UT>(ep, mb + r, fw / 2 + j0, g, u));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = (lane >> 3) + 8 * i, c0 = (lane & 7) * 8;
+                float v[8];
+                row8(r, c0, v);
+                if constexpr (MODE == EPI_RESID) epi8_resid<TOUT>(ep, mb + r, fw + c0, v);
+                else epi8_down<TOUT>(ep, mb + r, fw + c0, v);
+            }
+        }
+    });
+    if constexpr (MODE == EPI_SWIGLU) {
         if (ep.u_amax) {
             mx = wave_max(mx);
             if (lane == 0) atomic_max_nonneg(ep.u_amax, mx);
         }
-    } else {
-        const float sc = epi_scale(ep.amax_a, ep.s_w);
-        static_for<NBT>([&](auto a) {
-            const int m = t0 + wt * WT + a * 32 + lrow;
-            static_for<NBF>([&](auto b) {
-                epi_block<MODE, TOUT>(ep, m, f0 + wf * WF + b * 32, lhalf, acc[a][b], sc);
-                __builtin_amdgcn_sched_barrier(0);   // one block at a time: bounded register pressure
-            });
-        });
     }
 #endif  // device pass only: the host pass keeps just the launch stub
 }

@@ -13,6 +13,8 @@ hipError_t keep_index_launch(int T, int H, int W, int s, int Hk, int Wk, int32_t
 hipError_t nearest_map_launch(int T, int H, int W, int s, int Hk, int Wk, int32_t* nk, hipStream_t st);
 hipError_t rope_tables_launch(float2* tab, int n_t, int rt, int n_h, int rh, int n_w, int rw, double base,
                               hipStream_t st);
+// rows[m][i] = (cos, sin) of pair i of sequence row m (per-axis tables in r)
+hipError_t rope_rows_launch(const Rope& r, float2* rows, int S, int npair, hipStream_t st);
 hipError_t rmsnorm_launch(int act, bool seq_input, const SeqIn& seq, const float* dense, const void* g, void* out,
                           int M, int D, float eps, hipStream_t st);
 hipError_t rmsnorm_fp8_launch(bool seq_input, const SeqIn& seq, const float* dense, const void* g, uint8_t* out,

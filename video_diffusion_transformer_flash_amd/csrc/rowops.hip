@@ -59,6 +59,16 @@ __global__ void rope_table_kernel(float2* tab, int n_t, int rt, int n_h, int rh,
     tab[e] = make_float2((float)cos(ang), (float)sin(ang));
 }
 
+// Per sequence row m, the (cos, sin) of every pair of head-local features:
+// rows[m][i] for pair i of band t, h or w at the row's coordinates (from the
+// per-axis tables); text rows get position 0 on every axis (identity).
+__global__ void rope_rows_kernel(Rope r, float2* rows, int S, int npair) {
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= S * npair) return;
+    const int m = e / npair, i = e - m * npair;
+    rows[e] = rope_cs(r, 2 * i, rope_coords(r, m));
+}
+
 // ----------------------------------------------------------------- RMSNorm
 template <typename T> DIT_DEV void ld4(const T* p, float v[4]);
 template <> DIT_DEV void ld4<float>(const float* p, float v[4]) {
@@ -288,6 +298,11 @@ hipError_t rope_tables_launch(float2* tab, int n_t, int rt, int n_h, int rh, int
                               hipStream_t st) {
     const int n = n_t * (rt / 2) + n_h * (rh / 2) + n_w * (rw / 2);
     hipLaunchKernelGGL(rope_table_kernel, dim3(nblk(n)), dim3(256), 0, st, tab, n_t, rt, n_h, rh, n_w, rw, base);
+    return hipGetLastError();
+}
+
+hipError_t rope_rows_launch(const Rope& r, float2* rows, int S, int npair, hipStream_t st) {
+    hipLaunchKernelGGL(rope_rows_kernel, dim3(nblk((long)S * npair)), dim3(256), 0, st, r, rows, S, npair);
     return hipGetLastError();
 }
 
