@@ -12,15 +12,17 @@ timed as a second line item.
 
 The bandwidth-bound kernels (gather of the kept rows, nearest-kept broadcast
 plus residual) are also timed alone on the same shapes with the 256 MB
-Infinity Cache flushed before every repetition (a 1 GiB write), which is the
-number their HBM roofline fraction is judged on.
+Infinity Cache and the L2s flushed before every repetition, which is the number
+their HBM roofline fraction is judged on. The flush reads a 1 GiB buffer: a
+write flush would leave up to ~290 MB of dirty lines whose write-back to HBM
+would then be charged to the kernel under test.
 
 Prints one JSON line (see the repository's bench contract).
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu] [--no-off] [--copy-calib]
 
---copy-calib adds three plain 1 GiB device copies after the timed region: the
-reference dispatches that scale rocprofv3's FETCH_SIZE / WRITE_SIZE counters
-to bytes (see TRAFFIC).
+--copy-calib adds three plain 1 GiB elementwise copies after the timed region:
+the reference dispatches that scale rocprofv3's FETCH_SIZE / WRITE_SIZE
+counters to bytes (see TRAFFIC).
 """
 from __future__ import annotations
 
@@ -40,7 +42,16 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # then WRITE_SIZE; KiB per dispatch), each divided by what the same counter
 # reads per byte of a plain 1 GiB copy. Valid only for the kernel source it was
 # taken on (sha256 of the listed files); otherwise reported as null.
-TRAFFIC = {}
+TRAFFIC = {
+    "gemm_gate_up": {"files": ['video_diffusion_transformer_flash_amd/csrc/gemm_mfma.hip', 'video_diffusion_transformer_flash_amd/csrc/epilogue.h', 'video_diffusion_transformer_flash_amd/csrc/common.h'], "sha": "5b623c1e60d5ea7c",
+                     "fetch_bytes": 2138072087, "write_bytes": 107118592,
+                     "copy_scale": {"FETCH_SIZE": 1.99992, "WRITE_SIZE": 1.0},
+                     "source": "profiles/gemm_gate_up_540p_compressed_hbm_traffic.md"},
+    "broadcast_residual": {"files": ['video_diffusion_transformer_flash_amd/csrc/rowops.hip', 'video_diffusion_transformer_flash_amd/csrc/common.h'], "sha": "4e3907b9c48de74c",
+                           "fetch_bytes": 206363631, "write_bytes": 131604480,
+                           "copy_scale": {"FETCH_SIZE": 1.99992, "WRITE_SIZE": 1.0},
+                           "source": "profiles/broadcast_residual_540p_compressed_hbm_traffic.md"},
+}
 
 
 def _src_sha(files):
@@ -146,8 +157,8 @@ def kernel_table(kern, flops, bytes_):
 
 
 def bandwidth_kernels(d, reps=10):
-    """Gather and broadcast alone on the workload's shapes, Infinity Cache
-    flushed (1 GiB write) before every repetition; median of reps."""
+    """Gather and broadcast alone on the workload's shapes, caches flushed
+    (1 GiB read) before every repetition; median of reps."""
     import torch
     import video_diffusion_transformer_flash_amd as V
     Hk, Wk = V.keep_dims(d.H, d.W, d.stride)
@@ -159,7 +170,7 @@ def bandwidth_kernels(d, reps=10):
     nk = V.nearest_kept_map(d.T, d.H, d.W, d.stride)
     xc = torch.empty(Nk, D, dtype=torch.bfloat16, device="cuda")
     out = torch.empty_like(x)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")   # 1 GiB
     fns = {"gather_kept": lambda: V.gather_kept(x, keep, out=xc),
            "broadcast_residual": lambda: V.broadcast_residual(x, delta, nk, out=out)}
     byts = {"gather_kept": 2 * Nk * D * 2, "broadcast_residual": (2 * Nv * 2 + Nk * 4) * D}
@@ -167,7 +178,7 @@ def bandwidth_kernels(d, reps=10):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for r in range(reps + 2):
         for name, fn in fns.items():
-            flush.fill_(r & 255)
+            flush.amax()                    # reads 1 GiB: evicts inputs, leaves nothing dirty
             e0.record()
             fn()
             e1.record()
@@ -184,12 +195,16 @@ def bandwidth_kernels(d, reps=10):
 
 
 def copy_calibration(nbytes=1 << 30, reps=3):
-    """Plain device copies of a known size (reference dispatches for the HBM counters)."""
+    """Plain elementwise copies of a known size (b = a * 1 over fp32, 16-byte
+    vector accesses like the library's kernels): the reference dispatches
+    that scale the HBM counters to bytes. (A same-dtype copy_ would go to the
+    runtime's blit kernel, whose wider requests the fetch counter reads
+    differently.)"""
     import torch
-    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
     for _ in range(reps):
-        b.copy_(a)
+        torch.mul(a, 1.0, out=b)
     torch.cuda.synchronize()
 
 
@@ -270,7 +285,7 @@ def main():
     bc = bw["broadcast_residual"]
     line["hbm_roofline"] = {"bound": "hbm", "kernel": "broadcast_residual", "achieved": bc["GB/s"],
                             "peak": PEAK_HBM, "unit": "GB/s", "frac": bc["frac"], "bytes_per_launch": bc["bytes"],
-                            "launch_ms": bc["ms"], "cache": "Infinity Cache flushed before each launch",
+                            "launch_ms": bc["ms"], "cache": "L2 and Infinity Cache flushed (1 GiB read) before each launch",
                             "traffic": traffic_for("broadcast_residual")}
     line["bandwidth_kernels"] = bw
     torch.cuda.empty_cache()

@@ -184,22 +184,41 @@ __global__ void amax_to_scale_kernel(float* p) {
 }
 
 // ----------------------------------------------------------------- gather / broadcast
-// out[j] = x[idx[j]], rows of `rowbytes` (multiple of 16)
-__global__ void gather_rows_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__ idx,
-                                   uint8_t* __restrict__ out, int n, int chunks) {
-    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (size_t)n * chunks) return;
-    const int j = (int)(i / chunks);
-    const int c = (int)(i - (size_t)j * chunks);
-    const int src = idx[j];
-    ((uint4*)out)[(size_t)j * chunks + c] = ((const uint4*)x)[(size_t)src * chunks + c];
+// out[j] = x[idx[j]], rows of `chunks` 16-byte chunks. A workgroup of 512
+// threads copies two consecutive output rows, 256 threads each (the source
+// row is then uniform per wave), up to four loads in flight per thread; the
+// copy is written non-temporally.
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_v;
+__global__ __launch_bounds__(512) void gather_rows_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__ idx,
+                                                          uint8_t* __restrict__ out, int n, int chunks) {
+    constexpr int U = 4;
+    const int j = blockIdx.x * 2 + (threadIdx.x >> 8);
+    if (j >= n) return;
+    const int t = threadIdx.x & 255;
+    const int src = __builtin_amdgcn_readfirstlane(idx[j]);
+    const uint4* xr = (const uint4*)x + (size_t)src * chunks;
+    u32x4_v* orow = (u32x4_v*)out + (size_t)j * chunks;
+    for (int c0 = t; c0 < chunks; c0 += U * 256) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (c0 + u * 256 < chunks) v[u] = xr[c0 + u * 256];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (c0 + u * 256 < chunks) {
+                const u32x4_v w = {v[u].x, v[u].y, v[u].z, v[u].w};
+                __builtin_nontemporal_store(w, orow + c0 + u * 256);
+            }
+    }
 }
 
-// out[p] = x[p] + delta[nk[p]]. One workgroup per video position p (so the
-// kept slot nk[p] is a scalar), 8 elements per 16/32-byte access, up to four
-// accesses in flight per thread; the output is written non-temporally (it is
-// not read again by this block).
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_v;
+// out[p] = x[p] + delta[nk[p]]. A workgroup of 512 threads takes two
+// consecutive video positions, 256 threads each (the kept slot nk[p] is then
+// uniform per wave), 8 elements per 16/32-byte access, up to four accesses in
+// flight per thread; the output is written non-temporally (it is not read
+// again by this block). Position pairs are dealt to XCDs in contiguous
+// ranges: raster neighbours, which share their kept slot's delta row, then
+// meet that row in the same L2.
 typedef __attribute__((ext_vector_type(4))) float f32x4_v;
 template <typename T>
 struct Chunk8;
@@ -233,18 +252,19 @@ struct Chunk8<float> {
 };
 
 template <typename T>
-__global__ __launch_bounds__(256) void broadcast_residual_kernel(const T* x, const float* __restrict__ delta,
+__global__ __launch_bounds__(512) void broadcast_residual_kernel(const T* x, const float* __restrict__ delta,
                                                                  const int32_t* __restrict__ nk, T* out, int n_video,
                                                                  int D) {
     // x and out may be the same buffer: every element is read, then written, by one thread
     constexpr int U = 4;
-    const int p = blockIdx.x;
+    const int p = xcd_remap(blockIdx.x, (n_video + 1) / 2) * 2 + (threadIdx.x >> 8);
+    if (p >= n_video) return;
     const int j = __builtin_amdgcn_readfirstlane(nk[p]);
     const int per_row = D / 8;
     const T* xr = x + (size_t)p * D;
     const float* dr = delta + (size_t)j * D;
     T* orow = out + (size_t)p * D;
-    for (int c0 = threadIdx.x; c0 < per_row; c0 += U * 256) {
+    for (int c0 = threadIdx.x & 255; c0 < per_row; c0 += U * 256) {
         Chunk8<T> xv[U];
         float4 d0[U], d1[U];
 #pragma unroll
@@ -377,19 +397,21 @@ hipError_t amax_to_scale_launch(float* p, hipStream_t st) {
 
 hipError_t gather_rows_launch(const void* x, const int32_t* idx, void* out, int n, size_t rowbytes, hipStream_t st) {
     const int chunks = (int)(rowbytes / 16);
-    hipLaunchKernelGGL(gather_rows_kernel, dim3(nblk((size_t)n * chunks)), dim3(256), 0, st, (const uint8_t*)x, idx,
-                       (uint8_t*)out, n, chunks);
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(gather_rows_kernel, dim3((n + 1) / 2), dim3(512), 0, st, (const uint8_t*)x, idx, (uint8_t*)out, n,
+                       chunks);
     return hipGetLastError();
 }
 
 hipError_t broadcast_residual_launch(bool bf16, const void* x, const float* delta, const int32_t* nk, void* out,
                                      int n_video, int D, hipStream_t st) {
+    if (n_video == 0) return hipSuccess;
     if (bf16)
-        hipLaunchKernelGGL(broadcast_residual_kernel<bf16_t>, dim3(n_video), dim3(256), 0, st, (const bf16_t*)x, delta,
-                           nk, (bf16_t*)out, n_video, D);
+        hipLaunchKernelGGL(broadcast_residual_kernel<bf16_t>, dim3((n_video + 1) / 2), dim3(512), 0, st,
+                           (const bf16_t*)x, delta, nk, (bf16_t*)out, n_video, D);
     else
-        hipLaunchKernelGGL(broadcast_residual_kernel<float>, dim3(n_video), dim3(256), 0, st, (const float*)x, delta,
-                           nk, (float*)out, n_video, D);
+        hipLaunchKernelGGL(broadcast_residual_kernel<float>, dim3((n_video + 1) / 2), dim3(512), 0, st,
+                           (const float*)x, delta, nk, (float*)out, n_video, D);
     return hipGetLastError();
 }
 
