@@ -194,6 +194,126 @@ def bandwidth_kernels(d, reps=10):
     return res
 
 
+def _gpu_block_inputs(d, seed, fp8=False):
+    """Seeded synthetic inputs generated on the device (timing only; the parity
+    tests use the host generator): activations N(0, 1); weights N(0, 1/fan_in);
+    gains 1 + N(0, 0.1); bf16, or e4m3 codes + scale for fp8 projections."""
+    import torch
+    import video_diffusion_transformer_flash_amd as V
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    D, I, F = d.d_model, d.inner, d.d_ffn
+
+    def normal(shape, std=1.0, mean=0.0):
+        return torch.randn(shape, generator=g, device="cuda", dtype=torch.float32) * std + mean
+
+    x = {"x_text": normal((d.n_text, D)).bfloat16(), "x_video": normal((d.T, d.H, d.W, D)).bfloat16(),
+         "x_audio": normal((d.n_audio, D)).bfloat16()}
+    shapes = {"wqkv": ((3 * I, D), D), "wo": ((D, I), I), "wgate": ((F, D), D), "wup": ((F, D), D),
+              "wdown": ((D, F), F)}
+    w = {"g1": normal((D,), 0.1 ** 0.5, 1.0).bfloat16(), "g2": normal((D,), 0.1 ** 0.5, 1.0).bfloat16()}
+    for k, (shape, fan_in) in shapes.items():
+        t = normal(shape, fan_in ** -0.5)
+        if fp8:
+            w[k], w["s_" + k] = V.quantize_fp8(t)
+        else:
+            w[k] = t.bfloat16()
+        del t
+    return x, w
+
+
+def sweep(steps=2, warmup=1):
+    """768p grid at T = 2, 8, 32 latent frames, compression on and off:
+    block latency and TFLOP/s (device-generated inputs of the configuration's
+    distributions)."""
+    import torch
+    import video_diffusion_transformer_flash_amd as V
+    from dit_synth import CONFIGS, SWEEP_FRAMES
+    res = []
+    for T in SWEEP_FRAMES:
+        d = CONFIGS["768p"].with_(name=f"768p_T{T}", T=T)
+        x, w = _gpu_block_inputs(d, 3000 + T)
+        dims = V.make_dims(d)
+        Hk, Wk = V.keep_dims(d.H, d.W, d.stride)
+        keep = V.keep_index(d.T, d.H, d.W, d.stride)
+        nk = V.nearest_kept_map(d.T, d.H, d.W, d.stride)
+        out = tuple(torch.empty_like(x[k]) for k in ("x_text", "x_video", "x_audio"))
+        for comp in (True, False):
+            ws = V.workspace(V.block_workspace_size(dims, comp))
+
+            def step():
+                V.block_forward(dims, x["x_text"], x["x_video"], x["x_audio"], w, comp, keep if comp else None,
+                                nk if comp else None, out=out, ws=ws)
+
+            ms, _ = time_steps(step, steps, warmup, trace=False)
+            S = d.n_text + d.n_audio + (d.T * Hk * Wk if comp else d.n_video)
+            tf = sum(block_flops(d, S).values()) / 1e12
+            res.append({"T": T, "compress": comp, "tokens": S, "ms": round(ms, 3), "tflop": round(tf, 3),
+                        "TFLOP/s": round(tf / (ms * 1e-3), 1), "frac_of_bf16_peak": round(tf / (ms * 1e-3) / PEAK_BF16, 4)})
+            del ws
+            torch.cuda.empty_cache()
+        del x, w, out
+        torch.cuda.empty_cache()
+    return res
+
+
+def stack_timing(reps=2):
+    """The Flash-shaped stack: 42 blocks with fp8 projections (layers 1-2 full,
+    3-28 compressed, 29-42 full) on the 540p grid, 3 flow-matching Euler
+    evaluations on the fixed schedule t_k = u/(u + s(1-u)), u = k/3 (s = 12
+    video, 3 audio). Reported against the mixed roofline: GEMM FLOPs at the fp8
+    peak plus attention FLOPs at the bf16 peak."""
+    import torch
+    import video_diffusion_transformer_flash_amd as V
+    from dit_synth import CONFIGS, FLASH_EVALS, FLASH_LAYERS
+    d = CONFIGS["stack"]
+    a, b, c = FLASH_LAYERS
+    flags = [0] * a + [1] * b + [0] * c
+    x, w0 = _gpu_block_inputs(d, 4000, fp8=True)
+    layers = [w0] + [_gpu_block_inputs(d.with_(T=1, H=1, W=1, n_text=1, n_audio=1), 4001 + l, fp8=True)[1]
+                     for l in range(1, len(flags))]
+    dims = V.make_dims(d)
+    keep = V.keep_index(d.T, d.H, d.W, d.stride)
+    nk = V.nearest_kept_map(d.T, d.H, d.W, d.stride)
+
+    def sched(n, s):
+        return [(k / n) / ((k / n) + s * (1 - k / n)) for k in range(n + 1)]
+
+    tv, ta = sched(FLASH_EVALS, 12.0), sched(FLASH_EVALS, 3.0)
+    ws = V.workspace(V.stack_workspace_size(dims, flags))
+    xv0, xa0 = x["x_video"].clone(), x["x_audio"].clone()
+
+    def run():
+        x["x_video"].copy_(xv0)
+        x["x_audio"].copy_(xa0)
+        V.stack_sample(dims, layers, flags, tv, ta, x["x_text"], x["x_video"], x["x_audio"], keep, nk, ws=ws)
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(reps):
+        e0.record()
+        run()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = min(ts)
+    Hk, Wk = V.keep_dims(d.H, d.W, d.stride)
+    S_on, S_off = d.n_text + d.n_audio + d.T * Hk * Wk, d.n_text + d.n_audio + d.n_video
+    f_on, f_off = block_flops(d, S_on), block_flops(d, S_off)
+    gemm = FLASH_EVALS * sum(v for fl in flags for k, v in (f_on if fl else f_off).items() if k != "attention")
+    att = FLASH_EVALS * sum((f_on if fl else f_off)["attention"] for fl in flags)
+    roof_ms = (gemm / (2 * PEAK_BF16 * 1e12) + att / (PEAK_BF16 * 1e12)) * 1e3
+    ok = bool(torch.isfinite(x["x_video"].float()).all() and torch.isfinite(x["x_audio"].float()).all())
+    del layers, w0, ws
+    torch.cuda.empty_cache()
+    return {"workload": "42 blocks (2 full, 26 compressed, 14 full), fp8 e4m3 projections with per-tensor scales, "
+                        "540p grid 6x34x60, 3 Euler evaluations", "ms": round(ms, 2), "reps": reps,
+            "tflop": round((gemm + att) / 1e12, 1), "TFLOP/s": round((gemm + att) / 1e12 / (ms * 1e-3), 1),
+            "mixed_roofline_ms": round(roof_ms, 1), "frac_of_mixed_roofline": round(roof_ms / ms, 4),
+            "outputs_finite": ok}
+
+
 def copy_calibration(nbytes=1 << 30, reps=3):
     """Plain elementwise copies of a known size (b = a * 1 over fp32, 16-byte
     vector accesses like the library's kernels): the reference dispatches
@@ -248,6 +368,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-off", action="store_true", help="skip the compression-off line item")
     ap.add_argument("--copy-calib", action="store_true", help="add 1 GiB reference copies (counter calibration)")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the 768p frame sweep")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 42-layer fp8 stack")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures the block on one GPU; the multi-GPU sharding is not part of this build "
@@ -301,6 +423,10 @@ def main():
                                 "kernels": kernel_table(kern2, f2, hbm_bytes(d2, S2, d2.n_video, 0))}
         line["on_off_speedup"] = round(ms2 / ms, 3)
         del host2
+    if not a.no_sweep:
+        line["sweep_768p"] = sweep()
+    if not a.no_stack:
+        line["stack"] = stack_timing()
     if not a.no_cpu:
         line["cpu_baseline"] = cpu_baseline(d, host, True)
     print(json.dumps(line), flush=True)

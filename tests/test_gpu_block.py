@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import oracle as O
-from dit_synth import CONFIGS, BlockDims
+from dit_synth import CONFIGS, SWEEP_FRAMES, BlockDims
 from helpers import FP8_MAX_BOUND, gpu_weights, inputs, oracle_weights, rel_err, rms_err, to_numpy, torch_act
 
 pytestmark = pytest.mark.gpu
@@ -124,10 +124,8 @@ def sampled(d, compress, n_video=96, seed=0):
     return {"text": st, "video": sv, "audio": sa}
 
 
-@pytest.mark.parametrize("name,compress", [("540p_on", True), ("540p_off", False), ("768p", True)])
-def test_full_size_sampled(name, compress):
-    d = CONFIGS[name]
-    print(f"block {name} compress={compress} (sampled rows)", flush=True)
+def check_sampled(d, compress):
+    print(f"block {d.name} compress={compress} (sampled rows)", flush=True)
     x, w = inputs(d)
     got, _ = run_gpu(d, x, w, compress)
     smp = sampled(d, compress)
@@ -140,3 +138,16 @@ def test_full_size_sampled(name, compress):
     assert err <= TOL[d.dtype]
     # every output finite
     assert all(np.all(np.isfinite(a)) for a in got)
+
+
+@pytest.mark.parametrize("name,compress", [("540p_on", True), ("540p_off", False), ("768p", True), ("768p", False)])
+def test_full_size_sampled(name, compress):
+    check_sampled(CONFIGS[name], compress)
+
+
+@pytest.mark.parametrize("T", SWEEP_FRAMES)
+@pytest.mark.parametrize("compress", [True, False])
+def test_sweep_768p_sampled(T, compress):
+    """The 768p grid at 2, 8 and 32 latent frames (sequence-length sweep;
+    2794 to 129668 tokens), sampled rows against the oracle."""
+    check_sampled(CONFIGS["768p"].with_(name=f"768p_T{T}", T=T), compress)
