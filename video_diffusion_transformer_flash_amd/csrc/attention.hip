@@ -73,6 +73,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
     bf16x8_v qf[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) qf[s] = *(const bf16x8_v*)(Qh + (size_t)(q0 + lrow) * DH + 16 * s + 8 * lhalf);
+    // Have them in registers here: left to itself the compiler sinks these
+    // loads below the first K/V fill, and its wait counting then makes every
+    // key tile's score MFMAs wait for the next tile's fills.
+    asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]), "v"(qf[7]));
 
     // Memory -> LDS fills (buffer_load ... lds, 16 bytes per lane). K: one
     // instruction writes 4 rows of 256 B; instruction i of wave w rows
@@ -147,6 +151,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
                     if (key >= S) sc[b][r] = -INFINITY;
                 }
         }
+        // V^T fragments of the whole tile, read now so that they land during the softmax arithmetic
+        bf16x8_v vf[4][4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) vf[ks][d] = *(const bf16x8_v*)(bV + vOff[ks] + d * 4096);
+        __builtin_amdgcn_sched_barrier(0);
         float tmax = sc[0][0];
 #pragma unroll
         for (int b = 0; b < 2; ++b)
@@ -189,10 +200,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
             const bf16x8_v pf =
                 __builtin_bit_cast(bf16x8_v, make_uint4(pk[b][j0], pk[b][j0 + 1], pk[b][j0 + 2], pk[b][j0 + 3]));
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const bf16x8_v vf = *(const bf16x8_v*)(bV + vOff[ks] + d * 4096);
-                o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[d], 0, 0, 0);
-            }
+            for (int d = 0; d < 4; ++d) o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks][d], pf, o[d], 0, 0, 0);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();

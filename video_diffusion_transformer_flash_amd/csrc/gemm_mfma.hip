@@ -10,12 +10,14 @@
 // Tiling: WGT x WGF waves (token groups x feature groups); a tile of BT
 // tokens x BF features, each wave BT/WGT x BF/WGF; a K step of RB bytes per
 // row (RB = 128: 64 bf16 / 128 fp8; RB = 64: half that). Operands go from
-// memory straight to LDS (buffer_load ... lds) through NS stages, one LDS
-// array per stage, one barrier per K step, with a 16-byte-chunk XOR swizzle so
-// that 16 lanes reading one chunk column of 16 consecutive rows hit 16
-// distinct bank groups of the 64-bank LDS. Fragment reads of the next MFMA
-// substep are issued under the current substep's MFMAs. Workgroup ids are
-// remapped so that neighbouring tiles share an XCD (L2).
+// memory straight to LDS (buffer_load ... lds) through NS token stages and
+// NSF weight stages (the weight rows, which miss the XCD's L2 more often, may
+// get a third stage), one LDS array per operand and stage, one barrier per K
+// step, with a 16-byte-chunk XOR swizzle so that 16 lanes reading one chunk
+// column of 16 consecutive rows hit 16 distinct bank groups of the 64-bank
+// LDS. Fragment reads of the next MFMA substep are issued under the current
+// substep's MFMAs. Workgroup ids are remapped so that neighbouring tiles share
+// an XCD (L2).
 #include "common.h"
 #include "epilogue.h"
 #include "kernels.h"
@@ -36,7 +38,7 @@ DIT_DEV int swz(int row, int chunk) {
     return chunk ^ ((row / G) & (CPR - 1));
 }
 
-template <int BT, int BF, int WGT, int WGF, int NS, int RB, int PF, int OCC, int SCHED, bool FP8, int MODE,
+template <int BT, int BF, int WGT, int WGF, int NS, int NSF, int RB, int PF, int OCC, int SCHED, bool FP8, int MODE,
           typename TOUT>
 __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const uint8_t* __restrict__ A,
                                                                    const uint8_t* __restrict__ W0,
@@ -57,24 +59,33 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
     constexpr int LDS_T = BT * RB, LDS_F = BF * RB;
     static_assert(WT % 32 == 0 && WF % 64 == 0 && BT % RPI == 0 && BF % RPI == 0 && RPI % 16 == 0, "tile");
     static_assert(SUB >= 1 && NS >= 2, "pipeline");
-    static_assert(PF == 0 || (PF == 1 && NS == 2 && BT == BF && 64 * NW == 2 * BT) || (PF == 2 && NS == 2),
-                  "prefetch modes run on two LDS stages");
 
-    // LDS: one array per pipeline stage (feature tile, then token tile). With
-    // separate arrays the compiler can tell that the memory -> LDS loads into
-    // one stage do not alias the LDS reads of another, and does not make those
-    // reads wait for the loads. Stage addresses are constants.
-    constexpr int SB = LDS_F + LDS_T;
-    __shared__ __attribute__((aligned(16))) uint8_t st0[SB];
-    __shared__ __attribute__((aligned(16))) uint8_t st1[SB];
-    __shared__ __attribute__((aligned(16))) uint8_t st2[NS > 2 ? SB : 16];
-    __shared__ __attribute__((aligned(16))) uint8_t st3[NS > 3 ? SB : 16];
-    auto stage = [&](auto bc) -> uint8_t* {
+    // LDS: one array per operand and pipeline stage (NS token stages, NSF
+    // weight stages). With separate arrays the compiler can tell that the
+    // memory -> LDS loads into one stage do not alias the LDS reads of
+    // another, and does not make those reads wait for the loads; every stage
+    // address is a constant.
+    __shared__ __attribute__((aligned(16))) uint8_t sT0[LDS_T];
+    __shared__ __attribute__((aligned(16))) uint8_t sT1[LDS_T];
+    __shared__ __attribute__((aligned(16))) uint8_t sT2[NS > 2 ? LDS_T : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t sT3[NS > 3 ? LDS_T : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t sF0[LDS_F];
+    __shared__ __attribute__((aligned(16))) uint8_t sF1[LDS_F];
+    __shared__ __attribute__((aligned(16))) uint8_t sF2[NSF > 2 ? LDS_F : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t sF3[NSF > 3 ? LDS_F : 16];
+    auto stT = [&](auto bc) -> uint8_t* {
         constexpr int B = decltype(bc)::value;
-        if constexpr (B == 0) return st0;
-        else if constexpr (B == 1) return st1;
-        else if constexpr (B == 2) return st2;
-        else return st3;
+        if constexpr (B == 0) return sT0;
+        else if constexpr (B == 1) return sT1;
+        else if constexpr (B == 2) return sT2;
+        else return sT3;
+    };
+    auto stF = [&](auto bc) -> uint8_t* {
+        constexpr int B = decltype(bc)::value;
+        if constexpr (B == 0) return sF0;
+        else if constexpr (B == 1) return sF1;
+        else if constexpr (B == 2) return sF2;
+        else return sF3;
     };
 
     const int tid = threadIdx.x;
@@ -106,7 +117,11 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
     // rows, so it is the same for every i).
     const int rw = RPW * wave + lane / CPR;
     const int cswz = swz<RB>(rw, lane % CPR) * 16;
-    // token rows past M read as zero: the bound check sees only the lane offset
+    // Token rows past M read as zero through the descriptor's bound. The
+    // per-step K offset goes in the scalar soffset, so the lane offsets are
+    // loop-invariant registers that no later instruction overwrites (a fresh
+    // address register per load made the compiler wait for the load before
+    // reusing it, which drained the deeper stages).
     const int tvalid = min(M - t0, BT);
     const __amdgpu_buffer_rsrc_t rsT = make_rsrc(A + (size_t)t0 * rowbytes, tvalid * rowbytes);
     int voT[BT / RPI];
@@ -123,13 +138,16 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
     const int voF = (lane / CPR) * rowbytes + cswz;   // lane part; the wave's row goes in soffset
     const int nk = K / BK;
 
-    auto issue = [&](int kt, auto bufc) {
+    auto issueT = [&](int kt, auto bufc) {
         const int koff = kt * RB;
-        LDSPTR lt = (LDSPTR)(stage(bufc) + LDS_F + wave * 1024);
-        LDSPTR lf = (LDSPTR)(stage(bufc) + wave * 1024);
+        LDSPTR lt = (LDSPTR)(stT(bufc) + wave * 1024);
 #pragma unroll
         for (int i = 0; i < BT / RPI; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsT, lt + i * RPI * RB, 16, voT[i] + koff, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsT, lt + i * RPI * RB, 16, voT[i], koff, 0, 0);
+    };
+    auto issueF = [&](int kt, auto bufc) {
+        const int koff = kt * RB;
+        LDSPTR lf = (LDSPTR)(stF(bufc) + wave * 1024);
 #pragma unroll
         for (int i = 0; i < BF / RPI; ++i) {
             const int rowr = RPI * i + RPW * wave;         // first of this wave's rows (uniform)
@@ -137,10 +155,10 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
                 // 32-row blocks of the tile alternate gate / up rows of the same
                 // ffn features: block b holds gate (b even) or up rows b/2*32 ..
                 const int blk = rowr / 32;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds((blk & 1) ? rsF1 : rsF0, lf + i * RPI * RB, 16, voF + koff,
-                                                         ((blk >> 1) * 32 + rowr % 32) * rowbytes, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds((blk & 1) ? rsF1 : rsF0, lf + i * RPI * RB, 16, voF,
+                                                         ((blk >> 1) * 32 + rowr % 32) * rowbytes + koff, 0, 0);
             } else {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsF0, lf + i * RPI * RB, 16, voF + koff, rowr * rowbytes, 0,
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsF0, lf + i * RPI * RB, 16, voF, rowr * rowbytes + koff, 0,
                                                          0);
             }
         }
@@ -157,56 +175,35 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
         const int koff = kt * RB;
 #pragma unroll
         for (int i = 0; i < NPT; ++i)
-            pre[SET][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsT, voT[i] + koff, 0, 0));
+            pre[SET][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsT, voT[i], koff, 0));
 #pragma unroll
         for (int i = 0; i < NPF; ++i) {
             const int rowr = RPI * i + RPW * wave;
             if constexpr (MODE == EPI_SWIGLU) {
                 const int blk = rowr / 32;
                 pre[SET][NPT + i] = __builtin_bit_cast(
-                    uint4, __builtin_amdgcn_raw_buffer_load_b128((blk & 1) ? rsF1 : rsF0, voF + koff,
-                                                                 ((blk >> 1) * 32 + rowr % 32) * rowbytes, 0));
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128((blk & 1) ? rsF1 : rsF0, voF,
+                                                                 ((blk >> 1) * 32 + rowr % 32) * rowbytes + koff, 0));
             } else {
                 pre[SET][NPT + i] = __builtin_bit_cast(
-                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rsF0, voF + koff, rowr * rowbytes, 0));
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rsF0, voF, rowr * rowbytes + koff, 0));
             }
         }
     };
     auto lwrite = [&](auto setc, auto bufc) {
         constexpr int SET = decltype(setc)::value;
-        uint8_t* lt = stage(bufc) + LDS_F + wave * 1024 + lane * 16;
-        uint8_t* lf = stage(bufc) + wave * 1024 + lane * 16;
+        uint8_t* lt = stT(bufc) + wave * 1024 + lane * 16;
+        uint8_t* lf = stF(bufc) + wave * 1024 + lane * 16;
 #pragma unroll
         for (int i = 0; i < NPT; ++i) *(uint4*)(lt + i * RPI * RB) = pre[SET][i];
 #pragma unroll
         for (int i = 0; i < NPF; ++i) *(uint4*)(lf + i * RPI * RB) = pre[SET][NPT + i];
     };
-    // vmcnt immediate allowing the most recent step's register fetches to stay in flight
-    constexpr int WAIT_PF = ((NPT + NPF) & 15) | (7 << 4) | (15 << 8) | (((NPT + NPF) >> 4) << 14);
-    constexpr int WAIT_TOUCH = 2 | (7 << 4) | (15 << 8);
-    static_assert(NPT + NPF < 64, "vmcnt range");
-
-    // L2 touch (PF = 1): two dword loads per wave and step cover every
-    // 64-byte half line of a step's token and feature rows (lane pair 2 r,
-    // 2 r + 1 takes row r); issued two steps ahead, they bring the lines that
-    // missed the XCD's L2 in early, so that the direct loads one step ahead
-    // find them there. The loaded words only feed a sink value, folded in a
-    // step later (when the explicit waits have covered them) and stored by a
-    // branch that never runs; the compiler cannot drop the loads.
-    const int tg = (wave * 64 + lane) >> 1, th = (lane & 1) * 64;
-    uint32_t tk[2][2] = {{0u, 0u}, {0u, 0u}}, tsink = 0u;
-    auto touch = [&](int kt, auto setc) {
-        constexpr int SET = decltype(setc)::value;
-        const int koff = kt * RB;
-        tk[SET][0] = __builtin_amdgcn_raw_buffer_load_b32(rsT, tg * rowbytes + th + koff, 0, 0);
-        if constexpr (MODE == EPI_SWIGLU) {
-            // waves of the first half touch gate rows, the rest up rows
-            const bool up = wave >= NW / 2;
-            tk[SET][1] = __builtin_amdgcn_raw_buffer_load_b32(up ? rsF1 : rsF0,
-                                                              (tg - (up ? BF / 2 : 0)) * rowbytes + th + koff, 0, 0);
-        } else {
-            tk[SET][1] = __builtin_amdgcn_raw_buffer_load_b32(rsF0, tg * rowbytes + th + koff, 0, 0);
-        }
+    // vmcnt immediates (gfx9 encoding, expcnt / lgkmcnt left at their maxima)
+    auto vmwait = [](auto nc) {
+        constexpr int n = decltype(nc)::value;
+        static_assert(n < 64, "vmcnt range");
+        __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
     };
 
     // Per-lane LDS byte offsets of the operand fragments: fragment (s, block)
@@ -214,7 +211,7 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
     // A lane's rows differ by multiples of 32 between blocks, so its swizzle
     // term is the same for all of them and a block is a constant 32 * RB
     // further: one VGPR per (s, r), blocks and stages as immediate offsets.
-    const int rowF0 = (wf * WF + lrow) * RB, rowT0 = LDS_F + (wt * WT + lrow) * RB;
+    const int rowF0 = (wf * WF + lrow) * RB, rowT0 = (wt * WT + lrow) * RB;
     uint32_t aC[SUB][NR];
 #pragma unroll
     for (int s = 0; s < SUB; ++s)
@@ -232,12 +229,12 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
     // two fragment register sets: substep s computes from one while s+1 loads into the other
     uint4 fF[2][NBF][NR], fT[2][NBT][NR];
 
-    auto load_frags = [&](auto setc, auto sc, auto bufc) {
+    auto load_frags = [&](auto setc, auto sc, auto tbc, auto fbc) {
         constexpr int SET = decltype(setc)::value, S = decltype(sc)::value;
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            const uint8_t* pF = stage(bufc) + rowF0 + aC[S][r];
-            const uint8_t* pT = stage(bufc) + rowT0 + aC[S][r];
+            const uint8_t* pF = stF(fbc) + rowF0 + aC[S][r];
+            const uint8_t* pT = stT(tbc) + rowT0 + aC[S][r];
 #pragma unroll
             for (int b = 0; b < NBF; ++b) fF[SET][b][r] = *(const uint4*)(pF + b * 32 * RB);
 #pragma unroll
@@ -267,7 +264,7 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
 
     // Instruction order inside a substep (SCHED 1: the next substep's
     // fragment reads first, then the MFMAs; SCHED 2: reads interleaved one
-    // per MFMA; 0: left to the compiler, which places the reads late).
+    // per MFMA; 0: left to the compiler).
     constexpr int NRD = NR * (NBF + NBT), NMF = NBT * NBF;
     auto order_substep = [&]() {
         if constexpr (SCHED == 1) {
@@ -282,95 +279,110 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
         }
     };
 
-    // vmcnt immediate (gfx9 encoding, expcnt / lgkmcnt left at their maxima)
-    constexpr int LPS = BT / RPI + BF / RPI;      // memory -> LDS loads per step per wave
-    constexpr int VM_KEEP = LPS * (NS - 2);        // loads of later steps left in flight
-    static_assert(VM_KEEP < 64, "vmcnt range");
-    constexpr int WAIT_KEEP = (VM_KEEP & 15) | (7 << 4) | (15 << 8) | ((VM_KEEP >> 4) << 14);
+    // Pipelines. Direct loads (PF = 0): step j's token rows go to token stage
+    // j % NS and its weight rows to weight stage j % NSF; at step kt the loads
+    // of token step kt + NS - 1 and weight step kt + NSF - 1 are issued (token
+    // first), into the stages freed by the previous step. With NS = NSF the
+    // loads of the NS - 2 later steps may stay in flight at the end of a
+    // step; with NS = 2, NSF = 3 the weight loads of step kt + 2 may.
+    static_assert(PF == 0 || (PF == 2 && NS == 2 && NSF == 2), "register prefetch runs on two stages");
+    static_assert(NSF == NS || (NS == 2 && NSF == 3 && PF == 0), "uneven stages: two token, three weight");
+    constexpr int LOOP = (NS == NSF) ? NS : 6;    // steps per loop iteration (stage indices repeat)
 
-    // One K step on LDS stage BUF: the fragments of substep 0 are already in
-    // register set P, the loads for the next NS - 2 steps are in flight. Issue
-    // the loads of step kt + NS - 1 into the stage freed by the previous step;
-    // substeps 0..SUB-2 load the next substep's fragments while their MFMAs
-    // run; the last substep's fragments are in registers before the barrier,
-    // so after it the next step's first fragments load while the last MFMAs
-    // run. Substep s of the step computes from set (P + s) mod 2.
-    auto kstep = [&](auto bufc, auto pc, int kt) {
-        constexpr int BUF = decltype(bufc)::value, P = decltype(pc)::value;
-        if constexpr (PF <= 1)
-            if (kt + NS - 1 < nk) issue(kt + NS - 1, std::integral_constant<int, (BUF + NS - 1) % NS>{});
-        if constexpr (PF == 1)
-            if (kt + 2 < nk) touch(kt + 2, std::integral_constant<int, BUF>{});
+    // One K step on token stage TB and weight stage FB: the fragments of
+    // substep 0 are already in register set P. Substeps 0..SUB-2 load the
+    // next substep's fragments while their MFMAs run; the last substep's
+    // fragments are in registers before the barrier, so after it the next
+    // step's first fragments load while the last MFMAs run. Substep s
+    // computes from set (P + s) mod 2.
+    auto kstep = [&](auto tbc, auto fbc, auto pc, int kt) {
+        constexpr int TB = decltype(tbc)::value, FB = decltype(fbc)::value, P = decltype(pc)::value;
+        if constexpr (PF == 0 && NS == NSF) {
+            if (kt + NS - 1 < nk) issueT(kt + NS - 1, std::integral_constant<int, (TB + NS - 1) % NS>{});
+            if (kt + NSF - 1 < nk) issueF(kt + NSF - 1, std::integral_constant<int, (FB + NSF - 1) % NSF>{});
+        } else if constexpr (PF == 0) {
+            // uneven stages, branch-free: past the last step the fills repeat
+            // step nk - 1 into stages that are not read again
+            issueT(min(kt + 1, nk - 1), std::integral_constant<int, (TB + 1) % 2>{});
+            issueF(min(kt + 2, nk - 1), std::integral_constant<int, (FB + 2) % 3>{});
+        }
         static_for<SUB - 1>([&](auto s) {
-            load_frags(std::integral_constant<int, (P + s + 1) & 1>{}, std::integral_constant<int, s + 1>{}, bufc);
+            load_frags(std::integral_constant<int, (P + s + 1) & 1>{}, std::integral_constant<int, s + 1>{}, tbc,
+                       fbc);
             mfmas(std::integral_constant<int, (P + s) & 1>{});
             order_substep();
             __builtin_amdgcn_sched_barrier(0);   // keep later fragment loads out of this substep
         });
         if constexpr (PF == 0) {
-            // step kt + 1's LDS fills (this wave's) have landed; then everyone's
-            if (kt + NS - 1 < nk) __builtin_amdgcn_s_waitcnt(WAIT_KEEP);
-            else __builtin_amdgcn_s_waitcnt(0);
-        } else if constexpr (PF == 1) {
-            // step kt + 1's fills have landed; step kt + 2's two touches may not have
-            if (kt + 2 < nk) __builtin_amdgcn_s_waitcnt(WAIT_TOUCH);
-            else __builtin_amdgcn_s_waitcnt(0);
-            tsink ^= tk[(BUF + 1) % 2][0] ^ tk[(BUF + 1) % 2][1];   // touches of the previous step
+            // this wave's fills of step kt + 1 have landed (then, after the barrier, everyone's)
+            if constexpr (NS == NSF) {
+                if (kt + NS - 1 < nk) vmwait(std::integral_constant<int, (NPT + NPF) * (NS - 2)>{});
+                else vmwait(std::integral_constant<int, 0>{});
+            } else {
+                vmwait(std::integral_constant<int, NPF>{});   // the weight fills of step kt + 2 may stay in flight
+            }
         } else {
             // step kt + 1's registers (fetched two steps ago) go to the free
             // stage; that set then fetches step kt + 3
             if (kt + 1 < nk) {
-                if (kt + 2 < nk) __builtin_amdgcn_s_waitcnt(WAIT_PF);
-                else __builtin_amdgcn_s_waitcnt(0);
-                lwrite(std::integral_constant<int, (BUF + 1) % 2>{}, std::integral_constant<int, (BUF + 1) % 2>{});
-                if (kt + 3 < nk) gload(kt + 3, std::integral_constant<int, (BUF + 1) % 2>{});
+                if (kt + 2 < nk) vmwait(std::integral_constant<int, NPT + NPF>{});
+                else vmwait(std::integral_constant<int, 0>{});
+                lwrite(std::integral_constant<int, (TB + 1) % 2>{}, std::integral_constant<int, (TB + 1) % 2>{});
+                if (kt + 3 < nk) gload(kt + 3, std::integral_constant<int, (TB + 1) % 2>{});
             }
         }
-        lds_barrier();                   // nobody reads stage BUF any more
-        if (kt + 1 < nk) load_frags(std::integral_constant<int, (P + SUB) & 1>{}, std::integral_constant<int, 0>{},
-                                    std::integral_constant<int, (BUF + 1) % NS>{});
+        lds_barrier();                   // nobody reads stages TB / FB any more
+        if (NS != NSF || kt + 1 < nk)    // (uneven stages: after the last step these reads are unused)
+            load_frags(std::integral_constant<int, (P + SUB) & 1>{}, std::integral_constant<int, 0>{},
+                       std::integral_constant<int, (TB + 1) % NS>{}, std::integral_constant<int, (FB + 1) % NSF>{});
         mfmas(std::integral_constant<int, (P + SUB - 1) & 1>{});
         order_substep();
         __builtin_amdgcn_sched_barrier(0);
     };
 
+    using I0 = std::integral_constant<int, 0>;
     if constexpr (PF == 0) {
-        static_for<NS - 1>([&](auto b) {
-            if (b < nk) issue(b, b);
-        });
-        if (NS - 1 <= nk) __builtin_amdgcn_s_waitcnt(WAIT_KEEP);
-        else __builtin_amdgcn_s_waitcnt(0);
-    } else if constexpr (PF == 1) {
-        issue(0, std::integral_constant<int, 0>{});
-        if (1 < nk) {
-            touch(1, std::integral_constant<int, 1>{});
-            __builtin_amdgcn_s_waitcnt(WAIT_TOUCH);
+        if constexpr (NS == NSF) {
+            static_for<NS - 1>([&](auto b) {
+                if (b < nk) {
+                    issueT(b, b);
+                    issueF(b, b);
+                }
+            });
+            if (NS - 1 <= nk) vmwait(std::integral_constant<int, (NPT + NPF) * (NS - 2)>{});
+            else vmwait(I0{});
         } else {
-            __builtin_amdgcn_s_waitcnt(0);
+            issueT(0, I0{});
+            issueF(0, I0{});
+            issueF(min(1, nk - 1), std::integral_constant<int, 1>{});
+            vmwait(std::integral_constant<int, NPF>{});
         }
     } else {
-        gload(0, std::integral_constant<int, 0>{});
+        gload(0, I0{});
         if (1 < nk) {
             gload(1, std::integral_constant<int, 1>{});
-            __builtin_amdgcn_s_waitcnt(WAIT_PF);
+            vmwait(std::integral_constant<int, NPT + NPF>{});
         } else {
-            __builtin_amdgcn_s_waitcnt(0);
+            vmwait(I0{});
         }
-        lwrite(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-        if (2 < nk) gload(2, std::integral_constant<int, 0>{});
+        lwrite(I0{}, I0{});
+        if (2 < nk) gload(2, I0{});
     }
     lds_barrier();
-    load_frags(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-    // NS steps per iteration; NS * SUB even, so every iteration starts on set 0
-    static_assert((NS * SUB) % 2 == 0, "register set parity");
-    for (int kt = 0; kt < nk; kt += NS) {
-        static_for<NS>([&](auto b) {
-            if (kt + b < nk) kstep(b, std::integral_constant<int, (b * SUB) & 1>{}, kt + b);
+    load_frags(I0{}, I0{}, I0{}, I0{});
+    // LOOP steps per iteration; LOOP * SUB even, so every iteration starts on set 0
+    static_assert((LOOP * SUB) % 2 == 0, "register set parity");
+    for (int kt = 0; kt < nk; kt += LOOP) {
+        static_for<LOOP>([&](auto b) {
+            if (kt + b < nk)
+                kstep(std::integral_constant<int, b % NS>{}, std::integral_constant<int, b % NSF>{},
+                      std::integral_constant<int, (b * SUB) & 1>{}, kt + b);
         });
     }
-
-    if constexpr (PF == 1) {
-        if (M < 0) *(volatile uint32_t*)ep.u_amax = tsink ^ tk[0][0] ^ tk[0][1] ^ tk[1][0] ^ tk[1][1];   // never
+    if constexpr (NS != NSF) {
+        // the repeated fills past the last step must land before the epilogue reuses the LDS
+        vmwait(I0{});
+        lds_barrier();
     }
 
     // ---------------------------------------------------------------- epilogue
@@ -384,8 +396,10 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
     // wave has passed the last step's barrier, after which nobody reads it.
     static_assert(WF == 64, "a wave's rows hold 64 outputs");
     constexpr int RS = 64 * 4 + 16;
-    static_assert((NW / 2) * 32 * RS <= SB, "epilogue slices fit in two stages");
-    uint8_t* wl = ((wave & 1) ? st1 : st0) + (wave >> 1) * 32 * RS;
+    // wave w: a slice of the first token or weight stage (w mod 4), (w / 4) slices in
+    static_assert(NW <= 8 && ((NW + 3) / 4) * 32 * RS <= (LDS_T < LDS_F ? LDS_T : LDS_F), "epilogue slices");
+    const int ws4 = wave & 3;
+    uint8_t* wl = (ws4 == 0 ? sT0 : ws4 == 1 ? sT1 : ws4 == 2 ? sF0 : sF1) + (wave >> 2) * 32 * RS;
     float scb[NBF];
     if constexpr (MODE == EPI_SWIGLU) {
         const float sg = epi_scale(ep.amax_a, ep.s_w), su = epi_scale(ep.amax_a, ep.s_w2);
@@ -469,12 +483,12 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
 #endif  // device pass only: the host pass keeps just the launch stub
 }
 
-template <int BT, int BF, int WGT, int WGF, int NS, int RB, int PF, int OCC, int SCHED, bool FP8, int MODE>
+template <int BT, int BF, int WGT, int WGF, int NS, int NSF, int RB, int PF, int OCC, int SCHED, bool FP8, int MODE>
 hipError_t launch_t(const void* A, const void* W0, const void* W1, int M, int N, int K, const EpiParams& ep,
                     hipStream_t st) {
-    static_assert(NS * (BT + BF) * RB <= 160 * 1024, "LDS");   // NS stages of each operand tile
+    static_assert((NS * BT + NSF * BF) * RB <= 160 * 1024, "LDS");   // NS token and NSF weight stages
     const int tiles = ((M + BT - 1) / BT) * (N / BF);
-    hipLaunchKernelGGL((gemm_mfma_kernel<BT, BF, WGT, WGF, NS, RB, PF, OCC, SCHED, FP8, MODE, bf16_t>), dim3(tiles), dim3(64 * WGT * WGF), 0,
+    hipLaunchKernelGGL((gemm_mfma_kernel<BT, BF, WGT, WGF, NS, NSF, RB, PF, OCC, SCHED, FP8, MODE, bf16_t>), dim3(tiles), dim3(64 * WGT * WGF), 0,
                        st, (const uint8_t*)A, (const uint8_t*)W0, (const uint8_t*)W1, M, N, K, ep);
     return hipGetLastError();
 }
@@ -484,8 +498,8 @@ hipError_t dispatch(const void* A, const void* W0, const void* W1, int M, int N,
                     hipStream_t st) {
     // big tiles when there are enough of them to fill 256 CUs several times
     const long t256 = (long)((M + 255) / 256) * (N / 256);
-    if (N % 256 == 0 && t256 >= 512) return launch_t<256, 256, 2, 4, 2, 128, 0, 2, 0, FP8, MODE>(A, W0, W1, M, N, K, ep, st);
-    return launch_t<128, 128, 2, 2, 2, 128, 2, 2, 0, FP8, MODE>(A, W0, W1, M, N, K, ep, st);
+    if (N % 256 == 0 && t256 >= 512) return launch_t<256, 256, 2, 4, 2, 3, 128, 0, 2, 0, FP8, MODE>(A, W0, W1, M, N, K, ep, st);
+    return launch_t<128, 128, 2, 2, 2, 3, 128, 0, 2, 0, FP8, MODE>(A, W0, W1, M, N, K, ep, st);
 }
 
 }  // namespace detail
