@@ -138,16 +138,28 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
     const int voF = (lane / CPR) * rowbytes + cswz;   // lane part; the wave's row goes in soffset
     const int nk = K / BK;
 
+    // The LDS base of a fill goes through an empty register move, so the fill
+    // carries no array provenance: the compiler then counts it with the LDS
+    // writes it cannot place and does not make reads of the named stage arrays
+    // wait for it (its pairing of reads with earlier fills made some steps wait
+    // for fills of later stages). Every read of a stage follows this wave's
+    // explicit vmcnt wait for its fills and the barrier after it; at the IR
+    // level the fill still writes unknown LDS, so no LDS access moves across it.
+    auto untracked = [](uint8_t* p) {
+        uint32_t a = (uint32_t)(uintptr_t)(LDSPTR)p;
+        asm volatile("" : "+s"(a));
+        return (LDSPTR)(uintptr_t)a;
+    };
     auto issueT = [&](int kt, auto bufc) {
         const int koff = kt * RB;
-        LDSPTR lt = (LDSPTR)(stT(bufc) + wave * 1024);
+        LDSPTR lt = untracked(stT(bufc) + wave * 1024);
 #pragma unroll
         for (int i = 0; i < BT / RPI; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsT, lt + i * RPI * RB, 16, voT[i], koff, 0, 0);
     };
     auto issueF = [&](int kt, auto bufc) {
         const int koff = kt * RB;
-        LDSPTR lf = (LDSPTR)(stF(bufc) + wave * 1024);
+        LDSPTR lf = untracked(stF(bufc) + wave * 1024);
 #pragma unroll
         for (int i = 0; i < BF / RPI; ++i) {
             const int rowr = RPI * i + RPW * wave;         // first of this wave's rows (uniform)
