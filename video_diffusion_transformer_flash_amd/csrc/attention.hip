@@ -36,66 +36,94 @@ DIT_DEV int swzV(int row, int c) { return c ^ ((row >> 1) & 7); }    // 16-byte 
 // consecutive keys, matching one 16-byte read of a V^T row.
 DIT_DEV int rho(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
-                                                           const bf16_t* __restrict__ Vt, bf16_t* __restrict__ O,
-                                                           int S, int Sp, int nh, float c, float* o_amax) {
+// NW waves x 32 queries per workgroup, K / V^T tiles through NST LDS stages.
+template <int NW, int NST>
+__global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void attn_bf16_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ Vt, bf16_t* __restrict__ O,
+    int S, int Sp, int nh, float c, float* o_amax) {
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int DH = 128;
-    // one LDS array per stage and operand: the memory -> LDS loads into one
-    // stage then do not alias, for the compiler, the reads of the other, and
-    // every LDS address is a per-lane offset plus a constant
+    constexpr int QB = QW * NW;           // queries per workgroup
+    constexpr int LPT = 2 * (16 / NW);    // memory -> LDS loads per wave and key tile (K, then V^T)
+    static_assert(NW == 4 || NW == 8, "waves");
+    static_assert(NST == 2 || NST == 3, "stages");
+    // one LDS array per stage and operand: every fragment read is a per-lane
+    // offset plus a constant
     __shared__ __attribute__((aligned(16))) uint8_t sK0[KT * DH * 2];
     __shared__ __attribute__((aligned(16))) uint8_t sK1[KT * DH * 2];
+    __shared__ __attribute__((aligned(16))) uint8_t sK2[NST > 2 ? KT * DH * 2 : 16];
     __shared__ __attribute__((aligned(16))) uint8_t sV0[DH * KT * 2];
     __shared__ __attribute__((aligned(16))) uint8_t sV1[DH * KT * 2];
+    __shared__ __attribute__((aligned(16))) uint8_t sV2[NST > 2 ? DH * KT * 2 : 16];
     auto stK = [&](auto bc) -> uint8_t* {
         if constexpr (decltype(bc)::value == 0) return sK0;
-        else return sK1;
+        else if constexpr (decltype(bc)::value == 1) return sK1;
+        else return sK2;
     };
     auto stV = [&](auto bc) -> uint8_t* {
         if constexpr (decltype(bc)::value == 0) return sV0;
-        else return sV1;
+        else if constexpr (decltype(bc)::value == 1) return sV1;
+        else return sV2;
     };
 
-    const int nq = (S + 127) / 128;
+    const int nq = (S + QB - 1) / QB;
     const int blk = xcd_remap(blockIdx.x, nq * nh);
     const int head = blk / nq;
     const int qt = blk - head * nq;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lrow = lane & 31, lhalf = lane >> 5;
-    const int q0 = qt * 128 + wave * QW;
+    const int q0 = qt * QB + wave * QW;
 
     const bf16_t* Qh = Q + (size_t)head * Sp * DH;
     const bf16_t* Kh = K + (size_t)head * Sp * DH;
     const bf16_t* Vh = Vt + (size_t)head * DH * Sp;
 
-    // Q^T operand fragments for the 8 dh steps of 16
+    // Q^T operand fragments for the 8 dh steps of 16; query rows past the
+    // padded Sp rows read as zero through the descriptor's bound
+    const __amdgpu_buffer_rsrc_t rsQ = make_rsrc(Qh, Sp * DH * 2);
     bf16x8_v qf[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = *(const bf16x8_v*)(Qh + (size_t)(q0 + lrow) * DH + 16 * s + 8 * lhalf);
+    for (int s = 0; s < 8; ++s)
+        qf[s] = __builtin_bit_cast(bf16x8_v, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rsQ, ((q0 + lrow) * DH + 16 * s + 8 * lhalf) * 2, 0, 0));
     // Have them in registers here: left to itself the compiler sinks these
     // loads below the first K/V fill, and its wait counting then makes every
-    // key tile's score MFMAs wait for the next tile's fills.
+    // key tile's score MFMAs wait for later tiles' fills.
     asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]), "v"(qf[7]));
 
     // Memory -> LDS fills (buffer_load ... lds, 16 bytes per lane). K: one
     // instruction writes 4 rows of 256 B; instruction i of wave w rows
-    // 16 i + 4 w + L/16. V^T: 8 rows of 128 B; rows 32 i + 8 w + L/8. The
-    // swizzle is applied by fetching logical chunk (slot ^ swz(row)).
+    // 4 NW i + 4 w + L/16. V^T: 8 rows of 128 B; rows 8 NW i + 8 w + L/8. The
+    // swizzle is applied by fetching logical chunk (slot ^ swz(row)); its row
+    // term is the same for every i. The LDS base of a fill goes through an
+    // empty register move, so that the compiler does not pair the fill with
+    // reads of other stages and wait for it: each wave waits for its own
+    // fills explicitly before the barrier that precedes their reads.
     const __amdgpu_buffer_rsrc_t rsK = make_rsrc(Kh, Sp * DH * 2);
     const __amdgpu_buffer_rsrc_t rsV = make_rsrc(Vh, Sp * DH * 2);
     const int krow = 4 * wave + (lane >> 4);
     const int voK = krow * 256 + swzK(krow, lane & 15) * 16;
     const int vrow = 8 * wave + (lane >> 3);
     const int voV = vrow * Sp * 2 + swzV(vrow, lane & 7) * 16;
+    auto untracked = [](uint8_t* p) {
+        uint32_t a = (uint32_t)(uintptr_t)(LDSPTR)p;
+        asm volatile("" : "+s"(a));
+        return (LDSPTR)(uintptr_t)a;
+    };
     auto issue = [&](int kt, auto bc) {
-        LDSPTR lk = (LDSPTR)(stK(bc) + wave * 1024);
-        LDSPTR lv = (LDSPTR)(stV(bc) + wave * 1024);
+        LDSPTR lk = untracked(stK(bc) + wave * 1024);
+        LDSPTR lv = untracked(stV(bc) + wave * 1024);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, lk + i * 4096, 16, voK, kt * KT * 256 + i * 16 * 256, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, lv + i * 4096, 16, voV, kt * KT * 2 + i * 32 * Sp * 2, 0, 0);
+        for (int i = 0; i < 16 / NW; ++i) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, lk + i * NW * 1024, 16, voK, kt * KT * 256 + i * 4 * NW * 256,
+                                                     0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, lv + i * NW * 1024, 16, voV,
+                                                     kt * KT * 2 + i * 8 * NW * Sp * 2, 0, 0);
         }
+    };
+    auto vmwait = [](auto nc) {
+        constexpr int n = decltype(nc)::value;
+        __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
     };
 
     // Per-lane LDS offsets. K fragment (block b, dh step s): row b 32 + rho(lrow),
@@ -121,8 +149,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
 
     const int nkt = (S + KT - 1) / KT;
 
+    // Key tile kt on stage BC. The fills of tile kt + NST - 1 go out first
+    // (past the last tile they repeat tile nkt - 1 into a stage that is not
+    // read again: the step stays free of branches); at the end this wave's
+    // fills of tile kt + 1 have landed (those of tile kt + 2 may not), then
+    // the barrier: stage BC is free and tile kt + 1 complete for everyone.
     auto tile = [&](int kt, auto bc) {
-        if (kt + 1 < nkt) issue(kt + 1, std::integral_constant<int, 1 - decltype(bc)::value>{});
+        constexpr int BC = decltype(bc)::value;
+        issue(min(kt + NST - 1, nkt - 1), std::integral_constant<int, (BC + NST - 1) % NST>{});
         const uint8_t* bK = stK(bc);
         const uint8_t* bV = stV(bc);
 
@@ -133,13 +167,20 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) sc[b][r] = 0.f;
+        // all 16 K fragments of the tile are read first, so that only the
+        // first MFMA waits for LDS
+        bf16x8_v kf[8][2];
 #pragma unroll
         for (int s = 0; s < 8; ++s)
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const bf16x8_v kf = *(const bf16x8_v*)(bK + kOff[s] + b * 8192);
-                sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sc[b], 0, 0, 0);
-            }
+            for (int b = 0; b < 2; ++b) kf[s][b] = *(const bf16x8_v*)(bK + kOff[s] + b * 8192);
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s][b], qf[s], sc[b], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);   // the 16 LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);   // then the 16 MFMAs
+        __builtin_amdgcn_sched_barrier(0);
         // mask keys >= S (only in the last tile)
         const int k0 = kt * KT;
         if (k0 + KT > S) {
@@ -202,17 +243,20 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
 #pragma unroll
             for (int d = 0; d < 4; ++d) o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks][d], pf, o[d], 0, 0, 0);
         }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        vmwait(std::integral_constant<int, LPT * (NST - 2)>{});
+        lds_barrier();
     };
 
     issue(0, std::integral_constant<int, 0>{});
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int kt = 0; kt < nkt; kt += 2) {
-        tile(kt, std::integral_constant<int, 0>{});
-        if (kt + 1 < nkt) tile(kt + 1, std::integral_constant<int, 1>{});
+    if constexpr (NST == 3) issue(min(1, nkt - 1), std::integral_constant<int, 1>{});
+    vmwait(std::integral_constant<int, LPT * (NST - 2)>{});
+    lds_barrier();
+    for (int kt = 0; kt < nkt; kt += NST) {
+        static_for<NST>([&](auto b) {
+            if (kt + b < nkt) tile(kt + b, b);
+        });
     }
+    vmwait(std::integral_constant<int, 0>{});   // the repeated fills past the last tile
 
     const float ltot = lrun + __shfl_xor(lrun, 32, 64);
     const float inv = 1.f / ltot;
@@ -344,9 +388,10 @@ using namespace detail;
 hipError_t attention_bf16(const void* Q, const void* K, const void* Vt, void* O, int S, int Sp, int nh, int dh,
                           float c, float* o_amax, hipStream_t st) {
     if (dh != 128) return hipErrorInvalidValue;
-    const int nq = (S + 127) / 128;
-    hipLaunchKernelGGL(attn_bf16_kernel, dim3(nq * nh), dim3(256), 0, st, (const bf16_t*)Q, (const bf16_t*)K,
-                       (const bf16_t*)Vt, (bf16_t*)O, S, Sp, nh, c, o_amax);
+    constexpr int NW = 4, NST = 2;
+    const int nq = (S + QW * NW - 1) / (QW * NW);
+    hipLaunchKernelGGL((attn_bf16_kernel<NW, NST>), dim3(nq * nh), dim3(64 * NW), 0, st, (const bf16_t*)Q,
+                       (const bf16_t*)K, (const bf16_t*)Vt, (bf16_t*)O, S, Sp, nh, c, o_amax);
     return hipGetLastError();
 }
 

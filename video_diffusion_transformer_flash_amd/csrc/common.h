@@ -1,6 +1,8 @@
 // Shared device/host helpers of the gfx950 Flash DiT library (internal).
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -132,6 +134,16 @@ DIT_DEV float2 rope_cs(const Rope& r, int d, int3 c) {
     if (d < r.rh) return r.tab_h[c.y * (r.rh >> 1) + (d >> 1)];
     d -= r.rh;
     return r.tab_w[c.z * (r.rw >> 1) + (d >> 1)];
+}
+
+// Compile-time loop: f(integral_constant<int, i>) for i = 0 .. N-1, so that
+// register arrays are only ever indexed by constants.
+template <int N, int I = 0, class F>
+DIT_DEV void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
 }
 
 // Workgroup barrier for LDS pipelines fed by memory -> LDS loads: waits for

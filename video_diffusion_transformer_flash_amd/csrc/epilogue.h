@@ -237,7 +237,7 @@ DIT_DEV float epi8_swiglu(const EpiParams& p, int m, int f0, const float g[8], c
     if (m >= p.M) return 0.f;
     float o[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = g[i] / (1.f + __expf(-g[i])) * up[i];
+    for (int i = 0; i < 8; ++i) o[i] = g[i] * __builtin_amdgcn_rcpf(1.f + __expf(-g[i])) * up[i];   // rcp: 1 ulp
     store8<T>((T*)p.u + (size_t)m * p.F + f0, o);
     float mx = 0.f;
     if (p.u_amax) {
@@ -271,16 +271,6 @@ DIT_DEV void epi8_down(const EpiParams& p, int m, int n0, const float v[8]) {
         }
     } else {
         store8<T>((T*)o.ya + (size_t)(m - nt - nv) * p.D + n0, y);
-    }
-}
-
-// Compile-time loop: f(integral_constant<int, i>) for i = 0 .. N-1, so that
-// register arrays are only ever indexed by constants.
-template <int N, int I = 0, class F>
-DIT_DEV void static_for(F&& f) {
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for<N, I + 1>(f);
     }
 }
 

@@ -408,10 +408,18 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
     // wave has passed the last step's barrier, after which nobody reads it.
     static_assert(WF == 64, "a wave's rows hold 64 outputs");
     constexpr int RS = 64 * 4 + 16;
-    // wave w: a slice of the first token or weight stage (w mod 4), (w / 4) slices in
-    static_assert(NW <= 8 && ((NW + 3) / 4) * 32 * RS <= (LDS_T < LDS_F ? LDS_T : LDS_F), "epilogue slices");
-    const int ws4 = wave & 3;
-    uint8_t* wl = (ws4 == 0 ? sT0 : ws4 == 1 ? sT1 : ws4 == 2 ? sF0 : sF1) + (wave >> 2) * 32 * RS;
+    // wave slices packed into the stage arrays in order sT0, sT1, sF0, sF1, sF2
+    constexpr int SL = 32 * RS, capT = LDS_T / SL, capF = LDS_F / SL;
+    static_assert(2 * capT + (NSF > 2 ? 3 : 2) * capF >= NW, "epilogue slices");
+    uint8_t* wl;
+    {
+        int w = wave;
+        if (w < capT) wl = sT0 + w * SL;
+        else if ((w -= capT) < capT) wl = sT1 + w * SL;
+        else if ((w -= capT) < capF) wl = sF0 + w * SL;
+        else if ((w -= capF) < capF) wl = sF1 + w * SL;
+        else wl = sF2 + (w - capF) * SL;
+    }
     float scb[NBF];
     if constexpr (MODE == EPI_SWIGLU) {
         const float sg = epi_scale(ep.amax_a, ep.s_w), su = epi_scale(ep.amax_a, ep.s_w2);
