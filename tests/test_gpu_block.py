@@ -27,6 +27,13 @@ SMALL_FP8 = SMALL_BF16.with_(name="small_fp8", dtype="fp8", seed=6)
 # 1/sqrt(width), so this is the fp8 block at the width the stack runs at
 WIDE_FP8 = BlockDims("wide_fp8", T=2, H=6, W=10, n_text=16, n_audio=8, dtype="fp8", seed=8, d_model=5376, n_heads=56,
                      head_dim=128, d_ffn=14336, rope=(32, 48, 48))
+# 9 token x 4 feature tiles of 256 x 256 in the O and down projections when
+# uncompressed: fewer tiles than compute units, so those projections run
+# entirely as K slices plus the slice-sum pass (compressed: 3 token tiles,
+# too few to split, the plain path)
+SPLIT_BF16 = BlockDims("split_bf16", d_model=1024, n_heads=8, head_dim=128, d_ffn=2048, T=2, H=32, W=32, n_text=16,
+                       n_audio=8, rope=(32, 48, 48), dtype="bf16", seed=9)
+SPLIT_FP8 = SPLIT_BF16.with_(name="split_fp8", dtype="fp8", seed=10)
 
 
 def run_gpu(d, x, w, compress, stride=None):
@@ -80,6 +87,12 @@ def test_small_fp8(compress):
 @pytest.mark.parametrize("compress", [False, True])
 def test_wide_fp8(compress):
     check_full(WIDE_FP8, compress)
+
+
+@pytest.mark.parametrize("d", [SPLIT_BF16, SPLIT_FP8], ids=lambda d: d.name)
+@pytest.mark.parametrize("compress", [False, True])
+def test_k_split_tail(d, compress):
+    check_full(d, compress)
 
 
 @pytest.mark.parametrize("name", ["tiny", "small_bf16"])

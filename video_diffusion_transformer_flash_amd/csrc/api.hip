@@ -44,7 +44,7 @@ TraceState g_tr;
 
 inline void trace(const char* name, hipStream_t st) {
     if (g_tr.n < g_tr.cap) {
-        hipEventRecord(g_tr.ev[g_tr.n], st);
+        (void)hipEventRecord(g_tr.ev[g_tr.n], st);
         g_tr.name[g_tr.n] = name;
         ++g_tr.n;
     }
@@ -95,7 +95,7 @@ int validate_dims(const dit_dims* d) {
 // ------------------------------------------------------------------ workspace plan
 struct Plan {
     int S, Sp, nv_seq;
-    size_t tab, rrows, n, rinv, q, k, vt, o, o8, h, u, u8, delta, sc, total;
+    size_t tab, rrows, n, rinv, q, k, vt, o, o8, h, u, u8, delta, part, part_bytes, sc, total;
     int ntab_t;
 };
 
@@ -128,6 +128,11 @@ Plan make_plan(const dit_dims& d, int nv_seq, bool delta) {
     p.u = take((size_t)p.S * F * (fp8 ? 4 : es));   // fp8: fp32 u, quantised from full precision
     p.u8 = fp8 ? take((size_t)p.S * F) : 0;
     p.delta = delta ? take((size_t)nv_seq * D * 4) : 0;
+    // fp32 partial tiles of the O and down projections' K-split tails
+    p.part_bytes = d.act_dtype == DIT_F32 ? 0
+                                          : std::max(gemm_split_bytes(fp8, EPI_RESID, p.S, (int)D, (int)I),
+                                                     gemm_split_bytes(fp8, EPI_DOWN, p.S, (int)D, (int)F));
+    p.part = p.part_bytes ? take(p.part_bytes) : 0;
     p.sc = take(16 * sizeof(float));
     p.total = off;
     return p;
@@ -185,6 +190,8 @@ int run_block(const dit_dims& d, const dit_block_weights& w, const SeqIn& in, co
     ep.hres = h;
     ep.out = out;
     ep.refin = refin;
+    ep.part = P.part_bytes ? (float*)(ws + P.part) : nullptr;
+    ep.part_bytes = P.part_bytes;
 
     // 1-2. RMSNorm1 + QKV (+ rotary)
     if (fp8) {
@@ -288,7 +295,7 @@ int32_t dit_last_hip_error(void) { return g_last_hip; }
 
 int32_t dit_trace_enable(int32_t capacity) {
     if (capacity < 0) return DIT_EINVAL;
-    for (hipEvent_t e : g_tr.ev) hipEventDestroy(e);
+    for (hipEvent_t e : g_tr.ev) (void)hipEventDestroy(e);
     g_tr.ev.clear();
     g_tr.name.clear();
     g_tr.n = 0;

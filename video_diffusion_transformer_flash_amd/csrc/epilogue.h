@@ -47,6 +47,10 @@ struct EpiParams {
     const float* hres;
     SeqOut out;
     SeqIn refin;            // reference rows for delta (video segment only)
+    // RESID / DOWN: fp32 partial tiles of K-split tail tiles (nullptr or too
+    // small: no split)
+    float* part;
+    size_t part_bytes;
 };
 
 template <typename T> DIT_DEV void store4(T* p, const float v[4]);

@@ -18,6 +18,15 @@
 // LDS. Fragment reads of the next MFMA substep are issued under the current
 // substep's MFMAs. Workgroup ids are remapped so that neighbouring tiles share
 // an XCD (L2).
+//
+// K-split tail: when the tiles fill the compute units a whole number of
+// times plus a small remainder, the remainder tiles are cut along K into
+// `splits` slices that run as separate workgroups beside the whole tiles; each
+// writes its fp32 slice sum to a partial buffer, and a second kernel adds the
+// slices in a fixed order and runs the epilogue. The last round then takes a
+// fraction of a tile's time instead of a whole one.
+#include <atomic>
+
 #include "common.h"
 #include "epilogue.h"
 #include "kernels.h"
@@ -38,12 +47,27 @@ DIT_DEV int swz(int row, int chunk) {
     return chunk ^ ((row / G) & (CPR - 1));
 }
 
+// First token and first output feature of tile `tile`: GM consecutive token
+// tiles share one weight tile, so neighbouring tiles on an XCD reuse it in L2.
+template <int BT, int BF>
+DIT_DEV void tile_origin(int tile, int M, int N, int& t0, int& f0) {
+    constexpr int GM = 4;
+    const int ntt = (M + BT - 1) / BT;
+    const int ntf = N / BF;
+    const int group = tile / (GM * ntf);
+    const int first_t = group * GM;
+    const int gsz = min(ntt - first_t, GM);
+    const int in_g = tile - group * GM * ntf;
+    t0 = (first_t + in_g % gsz) * BT;
+    f0 = (in_g / gsz) * BF;
+}
+
 template <int BT, int BF, int WGT, int WGF, int NS, int NSF, int RB, int PF, int OCC, int SCHED, bool FP8, int MODE,
           typename TOUT>
 __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const uint8_t* __restrict__ A,
                                                                    const uint8_t* __restrict__ W0,
                                                                    const uint8_t* __restrict__ W1, int M, int N, int K,
-                                                                   EpiParams ep) {
+                                                                   int nfull, int splits, EpiParams ep) {
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int NW = WGT * WGF;                 // waves
     constexpr int WT = BT / WGT, WF = BF / WGF;   // per-wave tile
@@ -93,18 +117,25 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keep it scalar
     const int wt = wave % WGT, wf = wave / WGT;
 
-    // tile coordinates: XCD-aware, grouped along tokens (GM token tiles share W)
-    const int ntt = (M + BT - 1) / BT;
-    const int ntf = N / BF;
-    const int ntiles = ntt * ntf;
-    const int tile = xcd_remap(blockIdx.x, ntiles);
-    constexpr int GM = 4;
-    const int group = tile / (GM * ntf);
-    const int first_t = group * GM;
-    const int gsz = min(ntt - first_t, GM);
-    const int in_g = tile - group * GM * ntf;
-    const int t0 = (first_t + in_g % gsz) * BT;
-    const int f0 = (in_g / gsz) * BF;
+    // Tile coordinates, XCD-aware. Workgroups [0, nfull) take whole tiles;
+    // the rest are (tail tile, K slice) units, unit u = slice * ntail + tile,
+    // writing their sums to partial slot tile * splits + slice.
+    const int ntiles = ((M + BT - 1) / BT) * (N / BF);
+    int tile, nk = K / BK, kb = 0;
+    float* pslot = nullptr;
+    if ((int)blockIdx.x < nfull) {
+        tile = xcd_remap(blockIdx.x, nfull);
+    } else {
+        const int ntail = ntiles - nfull;
+        const int u = xcd_remap(blockIdx.x - nfull, ntail * splits);
+        const int r = u % ntail, slice = u / ntail;
+        tile = nfull + r;
+        nk /= splits;
+        kb = slice * nk;
+        pslot = ep.part + (size_t)(r * splits + slice) * BT * BF;
+    }
+    int t0, f0;
+    tile_origin<BT, BF>(tile, M, N, t0, f0);
 
     const int rowbytes = K * ESZ;
     const int lrow = lane & 31, lhalf = lane >> 5;
@@ -122,21 +153,21 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
     // loop-invariant registers that no later instruction overwrites (a fresh
     // address register per load made the compiler wait for the load before
     // reusing it, which drained the deeper stages).
+    // (a K slice starts kb steps into every row: the bases move by kb RB bytes)
     const int tvalid = min(M - t0, BT);
-    const __amdgpu_buffer_rsrc_t rsT = make_rsrc(A + (size_t)t0 * rowbytes, tvalid * rowbytes);
+    const __amdgpu_buffer_rsrc_t rsT = make_rsrc(A + (size_t)t0 * rowbytes + kb * RB, tvalid * rowbytes);
     int voT[BT / RPI];
 #pragma unroll
     for (int i = 0; i < BT / RPI; ++i) voT[i] = (RPI * i + rw) * rowbytes + cswz;
     __amdgpu_buffer_rsrc_t rsF0, rsF1;
     if constexpr (MODE == EPI_SWIGLU) {
-        rsF0 = make_rsrc(W0 + (size_t)(f0 / 2) * rowbytes, (BF / 2) * rowbytes);
-        rsF1 = make_rsrc(W1 + (size_t)(f0 / 2) * rowbytes, (BF / 2) * rowbytes);
+        rsF0 = make_rsrc(W0 + (size_t)(f0 / 2) * rowbytes + kb * RB, (BF / 2) * rowbytes);
+        rsF1 = make_rsrc(W1 + (size_t)(f0 / 2) * rowbytes + kb * RB, (BF / 2) * rowbytes);
     } else {
-        rsF0 = make_rsrc(W0 + (size_t)f0 * rowbytes, BF * rowbytes);
+        rsF0 = make_rsrc(W0 + (size_t)f0 * rowbytes + kb * RB, BF * rowbytes);
         rsF1 = rsF0;
     }
     const int voF = (lane / CPR) * rowbytes + cswz;   // lane part; the wave's row goes in soffset
-    const int nk = K / BK;
 
     // The LDS base of a fill goes through an empty register move, so the fill
     // carries no array provenance: the compiler then counts it with the LDS
@@ -489,7 +520,8 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
                 const int r = (lane >> 3) + 8 * i, c0 = (lane & 7) * 8;
                 float v[8];
                 row8(r, c0, v);
-                if constexpr (MODE == EPI_RESID) epi8_resid<TOUT>(ep, mb + r, fw + c0, v);
+                if (pslot) store8<float>(pslot + (size_t)(mb - t0 + r) * BF + (fw - f0 + c0), v);
+                else if constexpr (MODE == EPI_RESID) epi8_resid<TOUT>(ep, mb + r, fw + c0, v);
                 else epi8_down<TOUT>(ep, mb + r, fw + c0, v);
             }
         }
@@ -503,19 +535,102 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
 #endif  // device pass only: the host pass keeps just the launch stub
 }
 
+// K-split tail, second pass: one thread per 8 consecutive outputs of a tail
+// tile row; the slices are added in slice order, then the RESID / DOWN
+// epilogue runs on the sum.
+template <int MODE, int BT, int BF>
+__global__ __launch_bounds__(256) void split_reduce_kernel(int M, int N, int nfull, int splits, EpiParams ep) {
+    constexpr int TPR = BF / 8, RPB = 256 / TPR;   // threads per row, rows per block
+    static_assert(BT % RPB == 0, "rows");
+    const int r = blockIdx.x / (BT / RPB);
+    const int row = (blockIdx.x % (BT / RPB)) * RPB + threadIdx.x / TPR;
+    const int c0 = (threadIdx.x % TPR) * 8;
+    int t0, f0;
+    tile_origin<BT, BF>(nfull + r, M, N, t0, f0);
+    if (t0 + row >= M) return;
+    const float* p = ep.part + ((size_t)r * splits * BT + row) * BF + c0;
+    float v[8], x[8];
+    load8<float>(p, v);
+    for (int k = 1; k < splits; ++k) {
+        load8<float>(p + (size_t)k * BT * BF, x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] += x[i];
+    }
+    if constexpr (MODE == EPI_RESID) epi8_resid<bf16_t>(ep, t0 + row, f0 + c0, v);
+    else epi8_down<bf16_t>(ep, t0 + row, f0 + c0, v);
+}
+
+// Split of the tail: whole tiles fill `cus` compute units `nfull / cus`
+// times; the remaining tiles run as K slices, `splits` per tile, at most one
+// unit per compute unit, each slice at least 4 K steps.
+struct SplitPlan {
+    int nfull = 0, splits = 1;
+    size_t bytes = 0;
+};
+constexpr int SPLIT_BT = 256, SPLIT_BF = 256;
+
+SplitPlan split_plan(bool fp8, int mode, int M, int N, int K, int cus) {
+    SplitPlan p;
+    if ((mode != EPI_RESID && mode != EPI_DOWN) || N % SPLIT_BF || cus <= 0 || M <= 0) return p;
+    const long tiles = (long)((M + SPLIT_BT - 1) / SPLIT_BT) * (N / SPLIT_BF);
+    if (tiles < 32) return p;
+    const long nfull = tiles / cus * cus, tail = tiles - nfull;
+    if (tail == 0) return p;
+    const int nk = K / (fp8 ? 128 : 64);
+    int s = (int)std::min<long>(8, cus / tail);
+    while (s > 1 && (nk % s || nk / s < 4)) --s;
+    if (s < 2) return p;
+    p.nfull = (int)nfull;
+    p.splits = s;
+    p.bytes = (size_t)tail * s * SPLIT_BT * SPLIT_BF * sizeof(float);
+    return p;
+}
+
+// compute units of the current device (cached per device; 256 when it cannot be read)
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) {
+        (void)hipGetLastError();
+        c = 256;
+    }
+    cache[dev].store(c, std::memory_order_relaxed);
+    return c;
+}
+
 template <int BT, int BF, int WGT, int WGF, int NS, int NSF, int RB, int PF, int OCC, int SCHED, bool FP8, int MODE>
 hipError_t launch_t(const void* A, const void* W0, const void* W1, int M, int N, int K, const EpiParams& ep,
-                    hipStream_t st) {
+                    hipStream_t st, const SplitPlan& sp = SplitPlan{}) {
     static_assert((NS * BT + NSF * BF) * RB <= 160 * 1024, "LDS");   // NS token and NSF weight stages
     const int tiles = ((M + BT - 1) / BT) * (N / BF);
-    hipLaunchKernelGGL((gemm_mfma_kernel<BT, BF, WGT, WGF, NS, NSF, RB, PF, OCC, SCHED, FP8, MODE, bf16_t>), dim3(tiles), dim3(64 * WGT * WGF), 0,
-                       st, (const uint8_t*)A, (const uint8_t*)W0, (const uint8_t*)W1, M, N, K, ep);
+    const int nfull = sp.splits > 1 ? sp.nfull : tiles;
+    const int grid = nfull + (tiles - nfull) * sp.splits;
+    hipLaunchKernelGGL((gemm_mfma_kernel<BT, BF, WGT, WGF, NS, NSF, RB, PF, OCC, SCHED, FP8, MODE, bf16_t>),
+                       dim3(grid), dim3(64 * WGT * WGF), 0, st, (const uint8_t*)A, (const uint8_t*)W0,
+                       (const uint8_t*)W1, M, N, K, nfull, sp.splits, ep);
+    if constexpr ((MODE == EPI_RESID || MODE == EPI_DOWN) && BT == SPLIT_BT && BF == SPLIT_BF) {
+        if (sp.splits > 1) {
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL((split_reduce_kernel<MODE, BT, BF>), dim3((tiles - nfull) * (BT / (256 / (BF / 8)))),
+                               dim3(256), 0, st, M, N, nfull, sp.splits, ep);
+        }
+    }
     return hipGetLastError();
 }
 
 template <bool FP8, int MODE>
 hipError_t dispatch(const void* A, const void* W0, const void* W1, int M, int N, int K, const EpiParams& ep,
                     hipStream_t st) {
+    if constexpr (MODE == EPI_RESID || MODE == EPI_DOWN) {
+        // 256 x 256 tiles with a K-split tail when the partial buffer holds it
+        const SplitPlan sp = split_plan(FP8, MODE, M, N, K, device_cus());
+        if (sp.splits > 1 && ep.part && sp.bytes <= ep.part_bytes)
+            return launch_t<256, 256, 2, 4, 2, 3, 128, 0, 2, 0, FP8, MODE>(A, W0, W1, M, N, K, ep, st, sp);
+    }
     // big tiles when there are enough of them to fill 256 CUs several times
     const long t256 = (long)((M + 255) / 256) * (N / 256);
     if (N % 256 == 0 && t256 >= 512) return launch_t<256, 256, 2, 4, 2, 3, 128, 0, 2, 0, FP8, MODE>(A, W0, W1, M, N, K, ep, st);
@@ -524,6 +639,10 @@ hipError_t dispatch(const void* A, const void* W0, const void* W1, int M, int N,
 
 }  // namespace detail
 using namespace detail;
+
+size_t gemm_split_bytes(bool fp8, int mode, int M, int N, int K) {
+    return split_plan(fp8, mode, M, N, K, device_cus()).bytes;
+}
 
 // N: output features (for SWIGLU: 2 * F, gate and up interleaved per tile)
 hipError_t gemm_mfma(bool fp8, int mode, const void* A, const void* W0, const void* W1, int M, int N, int K,

@@ -30,6 +30,9 @@ hipError_t euler_launch(bool bf16, void* x, const void* v, size_t n, float dt, h
 
 hipError_t gemm_mfma(bool fp8, int mode, const void* A, const void* W0, const void* W1, int M, int N, int K,
                      const EpiParams& ep, hipStream_t st);
+// bytes of fp32 partial tiles gemm_mfma uses for a K-split tail (0: none);
+// the current device's compute-unit count decides it
+size_t gemm_split_bytes(bool fp8, int mode, int M, int N, int K);
 hipError_t gemm_f32(int mode, const void* A, const void* W0, const void* W1, int M, int N, int K, const EpiParams& ep,
                     hipStream_t st);
 
