@@ -35,6 +35,13 @@ DIT_DEV int swzV(int row, int c) { return c ^ ((row >> 1) & 7); }    // 16-byte 
 // swapped) so that each lane's eight P values of a 16-key step are 8
 // consecutive keys, matching one 16-byte read of a V^T row.
 DIT_DEV int rho(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+// lanes l and l ^ 32 exchange through v_permlane32_swap (no LDS round trip):
+// the swap of x with itself leaves (low half, high half) of x in the two results
+DIT_DEV void swap32(float x, float& lo, float& hi) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+}
 
 // NW waves x 32 queries per workgroup, K / V^T tiles through NST LDS stages.
 template <int NW, int NST>
@@ -204,7 +211,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void attn_bf16_kernel(
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sc[b][r]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        {
+            float a, b;
+            swap32(tmax, a, b);
+            tmax = fmaxf(a, b);
+        }
         const float mnew = fmaxf(mrun, tmax);
         const float alpha = __builtin_amdgcn_exp2f((mrun - mnew) * c);
         mrun = mnew;
@@ -258,7 +269,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void attn_bf16_kernel(
     }
     vmwait(std::integral_constant<int, 0>{});   // the repeated fills past the last tile
 
-    const float ltot = lrun + __shfl_xor(lrun, 32, 64);
+    float l0, l1;
+    swap32(lrun, l0, l1);
+    const float ltot = l0 + l1;
     const float inv = 1.f / ltot;
     const int q = q0 + lrow;
     float mx = 0.f;

@@ -51,7 +51,7 @@ DIT_DEV int swz(int row, int chunk) {
 // tiles share one weight tile, so neighbouring tiles on an XCD reuse it in L2.
 template <int BT, int BF>
 DIT_DEV void tile_origin(int tile, int M, int N, int& t0, int& f0) {
-    constexpr int GM = 4;
+    constexpr int GM = 16;
     const int ntt = (M + BT - 1) / BT;
     const int ntf = N / BF;
     const int group = tile / (GM * ntf);
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
     constexpr int RPI = RPW * NW;                 // rows per round of instructions
     constexpr int LDS_T = BT * RB, LDS_F = BF * RB;
     static_assert(WT % 32 == 0 && WF % 64 == 0 && BT % RPI == 0 && BF % RPI == 0 && RPI % 16 == 0, "tile");
-    static_assert(SUB >= 1 && NS >= 2, "pipeline");
+    static_assert(SUB >= 1 && NS >= 2 && NS <= 4 && NSF <= 4, "pipeline");
 
     // LDS: one array per operand and pipeline stage (NS token stages, NSF
     // weight stages). With separate arrays the compiler can tell that the
@@ -439,17 +439,25 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
     // wave has passed the last step's barrier, after which nobody reads it.
     static_assert(WF == 64, "a wave's rows hold 64 outputs");
     constexpr int RS = 64 * 4 + 16;
-    // wave slices packed into the stage arrays in order sT0, sT1, sF0, sF1, sF2
+    // wave slices packed into the stage arrays in order sT0.., sF0..
     constexpr int SL = 32 * RS, capT = LDS_T / SL, capF = LDS_F / SL;
-    static_assert(2 * capT + (NSF > 2 ? 3 : 2) * capF >= NW, "epilogue slices");
-    uint8_t* wl;
+    static_assert(NS * capT + NSF * capF >= NW, "epilogue slices");
+    uint8_t* wl = nullptr;
     {
         int w = wave;
-        if (w < capT) wl = sT0 + w * SL;
-        else if ((w -= capT) < capT) wl = sT1 + w * SL;
-        else if ((w -= capT) < capF) wl = sF0 + w * SL;
-        else if ((w -= capF) < capF) wl = sF1 + w * SL;
-        else wl = sF2 + (w - capF) * SL;
+        auto take = [&](uint8_t* arr, int cap) {
+            if (wl) return;
+            if (w < cap) wl = arr + w * SL;
+            else w -= cap;
+        };
+        take(sT0, capT);
+        take(sT1, capT);
+        if constexpr (NS > 2) take(sT2, capT);
+        if constexpr (NS > 3) take(sT3, capT);
+        take(sF0, capF);
+        take(sF1, capF);
+        if constexpr (NSF > 2) take(sF2, capF);
+        if constexpr (NSF > 3) take(sF3, capF);
     }
     float scb[NBF];
     if constexpr (MODE == EPI_SWIGLU) {
