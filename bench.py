@@ -43,13 +43,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # reads per byte of a plain 1 GiB copy. Valid only for the kernel source it was
 # taken on (sha256 of the listed files); otherwise reported as null.
 TRAFFIC = {
-    "gemm_gate_up": {"files": ['video_diffusion_transformer_flash_amd/csrc/gemm_mfma.hip', 'video_diffusion_transformer_flash_amd/csrc/epilogue.h', 'video_diffusion_transformer_flash_amd/csrc/common.h'], "sha": "5b623c1e60d5ea7c",
-                     "fetch_bytes": 2138072087, "write_bytes": 107118592,
-                     "copy_scale": {"FETCH_SIZE": 1.99992, "WRITE_SIZE": 1.0},
+    "gemm_gate_up": {"files": ['video_diffusion_transformer_flash_amd/csrc/gemm_mfma.hip', 'video_diffusion_transformer_flash_amd/csrc/epilogue.h', 'video_diffusion_transformer_flash_amd/csrc/common.h'], "sha": "82580fd1367c3622",
+                     "fetch_bytes": 2919885376, "write_bytes": 107118592,
+                     "copy_scale": {"FETCH_SIZE": 1.99994, "WRITE_SIZE": 1.0},
                      "source": "profiles/gemm_gate_up_540p_compressed_hbm_traffic.md"},
-    "broadcast_residual": {"files": ['video_diffusion_transformer_flash_amd/csrc/rowops.hip', 'video_diffusion_transformer_flash_amd/csrc/common.h'], "sha": "4e3907b9c48de74c",
-                           "fetch_bytes": 206363631, "write_bytes": 131604480,
-                           "copy_scale": {"FETCH_SIZE": 1.99992, "WRITE_SIZE": 1.0},
+    "broadcast_residual": {"files": ['video_diffusion_transformer_flash_amd/csrc/rowops.hip', 'video_diffusion_transformer_flash_amd/csrc/common.h'], "sha": "ae731ca96373fb0c",
+                           "fetch_bytes": 206361936, "write_bytes": 131604480,
+                           "copy_scale": {"FETCH_SIZE": 1.99994, "WRITE_SIZE": 1.0},
                            "source": "profiles/broadcast_residual_540p_compressed_hbm_traffic.md"},
 }
 
