@@ -298,6 +298,283 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void attn_bf16_kernel(
 #endif  // device pass only: the host pass keeps just the launch stub
 }
 
+// Software-pipelined bf16 kernel (same tiling, fragment layouts and numerics
+// as attn_bf16_kernel): iteration t issues the score MFMAs of key tile t next
+// to the rescale of O, then the P V MFMAs of tile t - 1 next to the softmax of
+// tile t, so that each wave's own instruction stream keeps its SIMD's matrix
+// core and VALU busy together instead of alternating between them. K and V^T
+// tiles sit one tile apart in LDS: iteration t fills K(t + 1) and V^T(t) while
+// it reads K(t) and V^T(t - 1), two stages per operand as before.
+template <int NW>
+__global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void attn_bf16_pipe_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ Vt, bf16_t* __restrict__ O,
+    int S, int Sp, int nh, float c, float* o_amax) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    static_assert(NW == 4 || NW == 8, "waves");
+    constexpr int DH = 128, QB = QW * NW;
+    __shared__ __attribute__((aligned(16))) uint8_t sK0[KT * DH * 2];
+    __shared__ __attribute__((aligned(16))) uint8_t sK1[KT * DH * 2];
+    __shared__ __attribute__((aligned(16))) uint8_t sV0[DH * KT * 2];
+    __shared__ __attribute__((aligned(16))) uint8_t sV1[DH * KT * 2];
+    // stage bases; the stage index is a compile-time constant in the main
+    // loop and a run-time value (t % 2) in the last iterations
+    auto stK = [&](int bc) -> uint8_t* { return bc ? sK1 : sK0; };
+    auto stV = [&](int bc) -> uint8_t* { return bc ? sV1 : sV0; };
+
+    const int nq = (S + QB - 1) / QB;
+    const int blk = xcd_remap(blockIdx.x, nq * nh);
+    const int head = blk / nq;
+    const int qt = blk - head * nq;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lrow = lane & 31, lhalf = lane >> 5;
+    const int q0 = qt * QB + wave * QW;
+
+    const bf16_t* Qh = Q + (size_t)head * Sp * DH;
+    const bf16_t* Kh = K + (size_t)head * Sp * DH;
+    const bf16_t* Vh = Vt + (size_t)head * DH * Sp;
+
+    const __amdgpu_buffer_rsrc_t rsQ = make_rsrc(Qh, Sp * DH * 2);
+    bf16x8_v qf[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+        qf[s] = __builtin_bit_cast(bf16x8_v, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rsQ, ((q0 + lrow) * DH + 16 * s + 8 * lhalf) * 2, 0, 0));
+    asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]), "v"(qf[7]));
+
+    const __amdgpu_buffer_rsrc_t rsK = make_rsrc(Kh, Sp * DH * 2);
+    const __amdgpu_buffer_rsrc_t rsV = make_rsrc(Vh, Sp * DH * 2);
+    const int krow = 4 * wave + (lane >> 4);
+    const int voK = krow * 256 + swzK(krow, lane & 15) * 16;
+    const int vrow = 8 * wave + (lane >> 3);
+    const int voV = vrow * Sp * 2 + swzV(vrow, lane & 7) * 16;
+    auto untracked = [](uint8_t* p) {
+        uint32_t a = (uint32_t)(uintptr_t)(LDSPTR)p;
+        asm volatile("" : "+s"(a));
+        return (LDSPTR)(uintptr_t)a;
+    };
+    auto fillK = [&](int kt, auto bc) {
+        LDSPTR lk = untracked(stK(bc) + wave * 1024);
+#pragma unroll
+        for (int i = 0; i < 16 / NW; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, lk + i * NW * 1024, 16, voK, kt * KT * 256 + i * 4 * NW * 256,
+                                                     0, 0);
+    };
+    auto fillV = [&](int kt, auto bc) {
+        LDSPTR lv = untracked(stV(bc) + wave * 1024);
+#pragma unroll
+        for (int i = 0; i < 16 / NW; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, lv + i * NW * 1024, 16, voV,
+                                                     kt * KT * 2 + i * 8 * NW * Sp * 2, 0, 0);
+    };
+    auto vmwait0 = []() { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); };
+
+    int kOff[8], vOff[4];
+    {
+        const int kr = rho(lrow);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) kOff[s] = kr * 256 + swzK(kr, 2 * s + lhalf) * 16;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) vOff[ks] = lrow * 128 + swzV(lrow, 2 * ks + lhalf) * 16;
+    }
+
+    f32x16 o[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
+    float mrun = -INFINITY, lrun = 0.f;   // lrun: this lane's half of the row sum
+    float alpha = 1.f;                     // O rescale owed before the next P V product
+    uint32_t pk[2][8];                     // P of the previous tile, bf16 pairs
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pk[b][j] = 0u;
+    const bf16x2_v ones = {(__bf16)1.f, (__bf16)1.f};
+    const int nkt = (S + KT - 1) / KT;
+
+    // Iteration t on K stage KB = t % 2 (V^T(t - 1) is in stage KB ^ 1).
+    // QK: tile t exists (t < nkt); PV: tile t - 1 exists (t >= 1); MASK: tile
+    // t is the last one and keys >= S are masked.
+    auto step = [&](int t, auto kbc, auto qkc, auto pvc, auto maskc) {
+        const int KB = kbc;
+        constexpr bool QK = decltype(qkc)::value, PV = decltype(pvc)::value, MASK = decltype(maskc)::value;
+        if constexpr (QK) {
+            // V^T(t) goes to stage KB (V^T(t - 2) was read last iteration);
+            // K(t + 1) to stage KB ^ 1 (past the last tile it repeats the
+            // last tile into a stage that is not read again)
+            fillV(t, KB);
+            fillK(min(t + 1, nkt - 1), KB ^ 1);
+        }
+        // The two phases are written slot by slot, one MFMA per slot with the
+        // VALU work and LDS reads that should issue beside it; the fences keep
+        // the compiler from regrouping them (it otherwise issues all MFMAs of a
+        // phase back to back and the VALU work after them).
+        auto fence = []() { __builtin_amdgcn_sched_barrier(0); };
+        // ---- phase A: S(t) = K(t) Q^T on the matrix core, O *= alpha on the VALU
+        f32x16 sc[2];
+        bf16x8_v kf[8][2];
+        const uint8_t* bK = stK(KB);
+        if constexpr (QK) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sc[b][r] = 0.f;
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) kf[s][b] = *(const bf16x8_v*)(bK + kOff[s] + b * 8192);
+        }
+        fence();
+        static_for<16>([&](auto ic) {
+            constexpr int i = ic, s = i / 2, b = i % 2;
+            if constexpr (QK) sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s][b], qf[s], sc[b], 0, 0, 0);
+            if constexpr (PV) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[i / 4][(i % 4) * 4 + r] *= alpha;
+            }
+            if constexpr (QK && s < 4) kf[s + 4][b] = *(const bf16x8_v*)(bK + kOff[s + 4] + b * 8192);
+            fence();
+        });
+        // ---- phase B: O^T += V^T(t - 1) P^T(t - 1) on the matrix core, softmax of S(t) on the VALU
+        const uint8_t* bV = stV(KB ^ 1);
+        bf16x8_v vf[4][4];
+        auto vread = [&](int ks, int d) { vf[ks][d] = *(const bf16x8_v*)(bV + vOff[ks] + d * 4096); };
+        if constexpr (PV) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) vread(ks, d);
+        }
+        fence();
+        float t0 = 0.f, t1 = 0.f, mc = 0.f, psum = 0.f;
+        uint32_t pn[2][8];   // P of tile t
+        auto pair = [&](int p) {
+            const int b = p >> 3, j = p & 7;
+            pn[b][j] = pack_bf2(__builtin_amdgcn_exp2f(fmaf(sc[b][2 * j], c, mc)),
+                                __builtin_amdgcn_exp2f(fmaf(sc[b][2 * j + 1], c, mc)));
+            psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, pn[b][j]), ones, psum, false);
+        };
+        static_for<16>([&](auto jc) {
+            constexpr int j = jc, ks = j / 4, d = j % 4;
+            if constexpr (PV) {
+                const int b = ks >> 1, j0 = 4 * (ks & 1);
+                const bf16x8_v pf = __builtin_bit_cast(
+                    bf16x8_v, make_uint4(pk[b][j0], pk[b][j0 + 1], pk[b][j0 + 2], pk[b][j0 + 3]));
+                o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks][d], pf, o[d], 0, 0, 0);
+                if constexpr (j == 0 || j == 1) { vread(2, 2 * j); vread(2, 2 * j + 1); }
+                if constexpr (j == 6 || j == 7) { vread(3, 2 * (j - 6)); vread(3, 2 * (j - 6) + 1); }
+            }
+            if constexpr (QK) {
+                if constexpr (j == 1 && MASK) {
+                    // register r of block b holds key 32 b + rho(8 (r / 4) + 4 h + r % 4)
+                    // = 32 b + 16 (r / 8) + 8 h + 4 ((r / 4) % 2) + r % 4 of the tile
+                    const int lim = S - t * KT - 8 * lhalf;
+#pragma unroll
+                    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            if (32 * bb + 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3) >= lim) sc[bb][r] = -INFINITY;
+                }
+                if constexpr (j == 2) {
+                    t0 = fmaxf(sc[0][0], sc[0][1]);
+                    t1 = fmaxf(sc[1][0], sc[1][1]);
+#pragma unroll
+                    for (int r = 2; r < 8; ++r) {
+                        t0 = fmaxf(t0, sc[0][r]);
+                        t1 = fmaxf(t1, sc[1][r]);
+                    }
+                }
+                if constexpr (j == 3) {
+#pragma unroll
+                    for (int r = 8; r < 16; ++r) {
+                        t0 = fmaxf(t0, sc[0][r]);
+                        t1 = fmaxf(t1, sc[1][r]);
+                    }
+                }
+                if constexpr (j == 4) {
+                    float a, bb;
+                    swap32(fmaxf(t0, t1), a, bb);
+                    const float mnew = fmaxf(mrun, fmaxf(a, bb));
+                    alpha = __builtin_amdgcn_exp2f((mrun - mnew) * c);
+                    mrun = mnew;
+                    mc = -mnew * c;
+                }
+                // the 16 exp pairs over slots 5..15: two in slots 5..9, one after
+                if constexpr (j >= 5 && j <= 9) { pair(2 * (j - 5)); pair(2 * (j - 5) + 1); }
+                if constexpr (j >= 10) pair(j);
+            }
+            fence();
+        });
+        if constexpr (QK) {
+            lrun = lrun * alpha + psum;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) pk[b][j] = pn[b][j];
+        }
+        if constexpr (QK) {
+            // this wave's fills have landed, then everyone's; stages KB (K)
+            // and KB ^ 1 (V^T) are free
+            vmwait0();
+            lds_barrier();
+        }
+    };
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+
+    fillK(0, 0);
+    vmwait0();
+    lds_barrier();
+    int t = 1;
+    if (nkt == 1) {
+        step(0, B0{}, T_{}, F_{}, T_{});
+    } else {
+        step(0, B0{}, T_{}, F_{}, F_{});
+        for (; t + 2 < nkt; t += 2) {
+            step(t, B1{}, T_{}, T_{}, F_{});
+            step(t + 1, B0{}, T_{}, T_{}, F_{});
+        }
+        // t is odd; one or two tiles remain, the last one masked
+        if (t + 2 == nkt) {
+            step(t, B1{}, T_{}, T_{}, F_{});
+            ++t;
+        }
+        step(t, t & 1, T_{}, T_{}, T_{});
+        ++t;
+    }
+    step(t, t & 1, F_{}, T_{}, F_{});   // the last P V (t = nkt)
+    vmwait0();   // the repeated K fill of the last iteration
+
+    float l0, l1;
+    swap32(lrun, l0, l1);
+    const float inv = 1.f / (l0 + l1);
+    const int q = q0 + lrow;
+    float mx = 0.f;
+    if (q < S) {
+        bf16_t* orow = O + (size_t)q * nh * DH + head * DH;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float v0 = o[d][4 * g] * inv, v1 = o[d][4 * g + 1] * inv;
+                float v2 = o[d][4 * g + 2] * inv, v3 = o[d][4 * g + 3] * inv;
+                uint2 w = make_uint2(pack_bf2(v0, v1), pack_bf2(v2, v3));
+                *(uint2*)(orow + d * 32 + 8 * g + 4 * lhalf) = w;
+                if (o_amax) {
+                    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(bf2f(f2bf(v0))), fabsf(bf2f(f2bf(v1)))),
+                                         fmaxf(fabsf(bf2f(f2bf(v2))), fabsf(bf2f(f2bf(v3))))));
+                }
+            }
+    }
+    if (o_amax) {
+        mx = wave_max(mx);
+        if (lane == 0) atomic_max_nonneg(o_amax, mx);
+    }
+#endif  // device pass only: the host pass keeps just the launch stub
+}
+
 // fp32 attention: one thread per query, 64 queries of one head per block,
 // key tiles of 32 in LDS; fp32 online softmax.
 template <int DH>
@@ -401,9 +678,9 @@ using namespace detail;
 hipError_t attention_bf16(const void* Q, const void* K, const void* Vt, void* O, int S, int Sp, int nh, int dh,
                           float c, float* o_amax, hipStream_t st) {
     if (dh != 128) return hipErrorInvalidValue;
-    constexpr int NW = 4, NST = 2;
+    constexpr int NW = 4;
     const int nq = (S + QW * NW - 1) / (QW * NW);
-    hipLaunchKernelGGL((attn_bf16_kernel<NW, NST>), dim3(nq * nh), dim3(64 * NW), 0, st, (const bf16_t*)Q,
+    hipLaunchKernelGGL((attn_bf16_pipe_kernel<NW>), dim3(nq * nh), dim3(64 * NW), 0, st, (const bf16_t*)Q,
                        (const bf16_t*)K, (const bf16_t*)Vt, (bf16_t*)O, S, Sp, nh, c, o_amax);
     return hipGetLastError();
 }
