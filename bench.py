@@ -185,11 +185,30 @@ def bandwidth_kernels(d, reps=10):
             torch.cuda.synchronize()
             if r >= 2:
                 times[name].append(e0.elapsed_time(e1))
+    # reference: torch's own device copy moving the same bytes (half read, half
+    # written) under the same flush
+    cref = {}
+    for name, nb in byts.items():
+        a = torch.ones(nb // 4, dtype=torch.bfloat16, device="cuda")
+        b = torch.empty_like(a)
+        ts = []
+        for r in range(reps + 2):
+            flush.amax()
+            e0.record()
+            b.copy_(a)
+            e1.record()
+            torch.cuda.synchronize()
+            if r >= 2:
+                ts.append(e0.elapsed_time(e1))
+        cref[name] = sorted(ts)[len(ts) // 2]
+        del a, b
     res = {}
     for name, ts in times.items():
         ms = sorted(ts)[len(ts) // 2]
         gbs = byts[name] / (ms * 1e-3) / 1e9
-        res[name] = {"ms": round(ms, 4), "bytes": byts[name], "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM, 4)}
+        cgbs = byts[name] / (cref[name] * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 4), "bytes": byts[name], "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM, 4),
+                     "torch_copy_same_bytes_GB/s": round(cgbs, 1)}
     del flush
     return res
 
