@@ -95,50 +95,59 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(SeqIn seq, const float* __
                                                       const TG* __restrict__ g, TO* __restrict__ out,
                                                       float* __restrict__ rinv, float* __restrict__ amax, int M,
                                                       int D, float eps) {
-    const int lane = threadIdx.x & 63;
-    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (m >= M) return;
-    const TI* x = SEQ ? seq_row<TI>(seq, m, D) : (const TI*)(dense + (size_t)m * D);
-    float r;
-    if (MODE == 2) {
-        r = rinv[m];
-    } else {
-        float ss = 0.f;
-        for (int c = lane * 4; c < D; c += 256) {
-            float v[4];
-            ld4<TI>(x + c, v);
-            ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
-        }
-        ss = wave_sum(ss);
-        r = 1.f / sqrtf(ss / (float)D + eps);
-    }
+    // one wave per row; the stats pass (MODE 1) takes RPW rows per wave and
+    // makes one atomic per workgroup (one per row serialised thousands of
+    // atomics on the single amax word)
+    constexpr int RPW = MODE == 1 ? 4 : 1;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     float mx = 0.f;
-    float qs = 1.f;
-    if (MODE == 2) {
-        const float a = *amax;
-        qs = a > 0.f ? 448.f / a : 1.f;
-    }
-    for (int c = lane * 4; c < D; c += 256) {
-        float v[4], gv[4];
-        ld4<TI>(x + c, v);
-        ld4<TG>(g + c, gv);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = v[i] * r * gv[i];
-        if constexpr (MODE == 0) {
-            st4<TO>(out + (size_t)m * D + c, v);
-        } else if constexpr (MODE == 1) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(v[i]));
+    for (int i = 0; i < RPW; ++i) {
+        const int m = (blockIdx.x * RPW + i) * 4 + wave;
+        if (m >= M) break;
+        const TI* x = SEQ ? seq_row<TI>(seq, m, D) : (const TI*)(dense + (size_t)m * D);
+        float r;
+        if (MODE == 2) {
+            r = rinv[m];
         } else {
-            uint32_t w = f32_to_e4m3(v[0] * qs) | (f32_to_e4m3(v[1] * qs) << 8) | (f32_to_e4m3(v[2] * qs) << 16) |
-                         (f32_to_e4m3(v[3] * qs) << 24);
-            *(uint32_t*)((uint8_t*)out + (size_t)m * D + c) = w;
+            float ss = 0.f;
+            for (int c = lane * 4; c < D; c += 256) {
+                float v[4];
+                ld4<TI>(x + c, v);
+                ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+            }
+            ss = wave_sum(ss);
+            r = 1.f / sqrtf(ss / (float)D + eps);
         }
+        float qs = 1.f;
+        if (MODE == 2) {
+            const float a = *amax;
+            qs = a > 0.f ? 448.f / a : 1.f;
+        }
+        for (int c = lane * 4; c < D; c += 256) {
+            float v[4], gv[4];
+            ld4<TI>(x + c, v);
+            ld4<TG>(g + c, gv);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[k] = v[k] * r * gv[k];
+            if constexpr (MODE == 0) {
+                st4<TO>(out + (size_t)m * D + c, v);
+            } else if constexpr (MODE == 1) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) mx = fmaxf(mx, fabsf(v[k]));
+            } else {
+                uint32_t w = f32_to_e4m3(v[0] * qs) | (f32_to_e4m3(v[1] * qs) << 8) | (f32_to_e4m3(v[2] * qs) << 16) |
+                             (f32_to_e4m3(v[3] * qs) << 24);
+                *(uint32_t*)((uint8_t*)out + (size_t)m * D + c) = w;
+            }
+        }
+        if (MODE == 1 && lane == 0) rinv[m] = r;
     }
-    if (MODE == 1) {
-        if (lane == 0) rinv[m] = r;
+    if constexpr (MODE == 1) {
+        __shared__ float wmax[4];
         mx = wave_max(mx);
-        if (lane == 0) atomic_max_nonneg(amax, mx);
+        if (lane == 0) wmax[wave] = mx;
+        __syncthreads();
+        if (threadIdx.x == 0) atomic_max_nonneg(amax, fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
     }
 }
 
@@ -350,15 +359,15 @@ hipError_t rmsnorm_launch(int act, bool seq_input, const SeqIn& seq, const float
 // bf16 activations, fp8 output: stats pass (rinv, amax) then quantise pass
 hipError_t rmsnorm_fp8_launch(bool seq_input, const SeqIn& seq, const float* dense, const void* g, uint8_t* out,
                               float* rinv, float* amax, int M, int D, float eps, hipStream_t st) {
-    const dim3 grid(nblk(M, 4)), block(256);
+    const dim3 grid(nblk(M, 4)), gstat(nblk(M, 16)), block(256);   // stats: 4 rows per wave
     hipLaunchKernelGGL(fill_kernel, dim3(1), dim3(64), 0, st, amax, 1, 0.f);
     if (seq_input) {
-        hipLaunchKernelGGL((rmsnorm_kernel<bf16_t, bf16_t, uint8_t, true, 1>), grid, block, 0, st, seq, dense,
+        hipLaunchKernelGGL((rmsnorm_kernel<bf16_t, bf16_t, uint8_t, true, 1>), gstat, block, 0, st, seq, dense,
                            (const bf16_t*)g, out, rinv, amax, M, D, eps);
         hipLaunchKernelGGL((rmsnorm_kernel<bf16_t, bf16_t, uint8_t, true, 2>), grid, block, 0, st, seq, dense,
                            (const bf16_t*)g, out, rinv, amax, M, D, eps);
     } else {
-        hipLaunchKernelGGL((rmsnorm_kernel<float, bf16_t, uint8_t, false, 1>), grid, block, 0, st, seq, dense,
+        hipLaunchKernelGGL((rmsnorm_kernel<float, bf16_t, uint8_t, false, 1>), gstat, block, 0, st, seq, dense,
                            (const bf16_t*)g, out, rinv, amax, M, D, eps);
         hipLaunchKernelGGL((rmsnorm_kernel<float, bf16_t, uint8_t, false, 2>), grid, block, 0, st, seq, dense,
                            (const bf16_t*)g, out, rinv, amax, M, D, eps);
