@@ -43,263 +43,7 @@ DIT_DEV void swap32(float x, float& lo, float& hi) {
     hi = __uint_as_float(r[1]);
 }
 
-// NW waves x 32 queries per workgroup, K / V^T tiles through NST LDS stages.
-template <int NW, int NST>
-__global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void attn_bf16_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ Vt, bf16_t* __restrict__ O,
-    int S, int Sp, int nh, float c, float* o_amax) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    constexpr int DH = 128;
-    constexpr int QB = QW * NW;           // queries per workgroup
-    constexpr int LPT = 2 * (16 / NW);    // memory -> LDS loads per wave and key tile (K, then V^T)
-    static_assert(NW == 4 || NW == 8, "waves");
-    static_assert(NST == 2 || NST == 3, "stages");
-    // one LDS array per stage and operand: every fragment read is a per-lane
-    // offset plus a constant
-    __shared__ __attribute__((aligned(16))) uint8_t sK0[KT * DH * 2];
-    __shared__ __attribute__((aligned(16))) uint8_t sK1[KT * DH * 2];
-    __shared__ __attribute__((aligned(16))) uint8_t sK2[NST > 2 ? KT * DH * 2 : 16];
-    __shared__ __attribute__((aligned(16))) uint8_t sV0[DH * KT * 2];
-    __shared__ __attribute__((aligned(16))) uint8_t sV1[DH * KT * 2];
-    __shared__ __attribute__((aligned(16))) uint8_t sV2[NST > 2 ? DH * KT * 2 : 16];
-    auto stK = [&](auto bc) -> uint8_t* {
-        if constexpr (decltype(bc)::value == 0) return sK0;
-        else if constexpr (decltype(bc)::value == 1) return sK1;
-        else return sK2;
-    };
-    auto stV = [&](auto bc) -> uint8_t* {
-        if constexpr (decltype(bc)::value == 0) return sV0;
-        else if constexpr (decltype(bc)::value == 1) return sV1;
-        else return sV2;
-    };
-
-    const int nq = (S + QB - 1) / QB;
-    const int blk = xcd_remap(blockIdx.x, nq * nh);
-    const int head = blk / nq;
-    const int qt = blk - head * nq;
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lrow = lane & 31, lhalf = lane >> 5;
-    const int q0 = qt * QB + wave * QW;
-
-    const bf16_t* Qh = Q + (size_t)head * Sp * DH;
-    const bf16_t* Kh = K + (size_t)head * Sp * DH;
-    const bf16_t* Vh = Vt + (size_t)head * DH * Sp;
-
-    // Q^T operand fragments for the 8 dh steps of 16; query rows past the
-    // padded Sp rows read as zero through the descriptor's bound
-    const __amdgpu_buffer_rsrc_t rsQ = make_rsrc(Qh, Sp * DH * 2);
-    bf16x8_v qf[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-        qf[s] = __builtin_bit_cast(bf16x8_v, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 rsQ, ((q0 + lrow) * DH + 16 * s + 8 * lhalf) * 2, 0, 0));
-    // Have them in registers here: left to itself the compiler sinks these
-    // loads below the first K/V fill, and its wait counting then makes every
-    // key tile's score MFMAs wait for later tiles' fills.
-    asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]), "v"(qf[7]));
-
-    // Memory -> LDS fills (buffer_load ... lds, 16 bytes per lane). K: one
-    // instruction writes 4 rows of 256 B; instruction i of wave w rows
-    // 4 NW i + 4 w + L/16. V^T: 8 rows of 128 B; rows 8 NW i + 8 w + L/8. The
-    // swizzle is applied by fetching logical chunk (slot ^ swz(row)); its row
-    // term is the same for every i. The LDS base of a fill goes through an
-    // empty register move, so that the compiler does not pair the fill with
-    // reads of other stages and wait for it: each wave waits for its own
-    // fills explicitly before the barrier that precedes their reads.
-    const __amdgpu_buffer_rsrc_t rsK = make_rsrc(Kh, Sp * DH * 2);
-    const __amdgpu_buffer_rsrc_t rsV = make_rsrc(Vh, Sp * DH * 2);
-    const int krow = 4 * wave + (lane >> 4);
-    const int voK = krow * 256 + swzK(krow, lane & 15) * 16;
-    const int vrow = 8 * wave + (lane >> 3);
-    const int voV = vrow * Sp * 2 + swzV(vrow, lane & 7) * 16;
-    auto untracked = [](uint8_t* p) {
-        uint32_t a = (uint32_t)(uintptr_t)(LDSPTR)p;
-        asm volatile("" : "+s"(a));
-        return (LDSPTR)(uintptr_t)a;
-    };
-    auto issue = [&](int kt, auto bc) {
-        LDSPTR lk = untracked(stK(bc) + wave * 1024);
-        LDSPTR lv = untracked(stV(bc) + wave * 1024);
-#pragma unroll
-        for (int i = 0; i < 16 / NW; ++i) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, lk + i * NW * 1024, 16, voK, kt * KT * 256 + i * 4 * NW * 256,
-                                                     0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, lv + i * NW * 1024, 16, voV,
-                                                     kt * KT * 2 + i * 8 * NW * Sp * 2, 0, 0);
-        }
-    };
-    auto vmwait = [](auto nc) {
-        constexpr int n = decltype(nc)::value;
-        __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
-    };
-
-    // Per-lane LDS offsets. K fragment (block b, dh step s): row b 32 + rho(lrow),
-    // chunk 2 s + h; the swizzle term depends on row & 15 = rho(lrow) & 15 only,
-    // so block b is a constant 8192 bytes further. V^T fragment (dh block d,
-    // key step ks): row d 32 + lrow, chunk 2 ks + h; block d is 4096 further.
-    int kOff[8], vOff[4];
-    {
-        const int kr = rho(lrow);
-#pragma unroll
-        for (int s = 0; s < 8; ++s) kOff[s] = kr * 256 + swzK(kr, 2 * s + lhalf) * 16;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) vOff[ks] = lrow * 128 + swzV(lrow, 2 * ks + lhalf) * 16;
-    }
-
-    f32x16 o[4];
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
-    float mrun = -INFINITY, lrun = 0.f;   // lrun: this lane's half of the row sum
-    const bf16x2_v ones = {(__bf16)1.f, (__bf16)1.f};
-
-    const int nkt = (S + KT - 1) / KT;
-
-    // Key tile kt on stage BC. The fills of tile kt + NST - 1 go out first
-    // (past the last tile they repeat tile nkt - 1 into a stage that is not
-    // read again: the step stays free of branches); at the end this wave's
-    // fills of tile kt + 1 have landed (those of tile kt + 2 may not), then
-    // the barrier: stage BC is free and tile kt + 1 complete for everyone.
-    auto tile = [&](int kt, auto bc) {
-        constexpr int BC = decltype(bc)::value;
-        issue(min(kt + NST - 1, nkt - 1), std::integral_constant<int, (BC + NST - 1) % NST>{});
-        const uint8_t* bK = stK(bc);
-        const uint8_t* bV = stV(bc);
-
-        // scores S^T for 2 blocks of 32 keys (row i of block b is key 32 b + rho(i))
-        // (the two blocks interleave, so no MFMA waits on the one before it)
-        f32x16 sc[2];
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sc[b][r] = 0.f;
-        // all 16 K fragments of the tile are read first, so that only the
-        // first MFMA waits for LDS
-        bf16x8_v kf[8][2];
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-#pragma unroll
-            for (int b = 0; b < 2; ++b) kf[s][b] = *(const bf16x8_v*)(bK + kOff[s] + b * 8192);
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-#pragma unroll
-            for (int b = 0; b < 2; ++b) sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s][b], qf[s], sc[b], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);   // the 16 LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);   // then the 16 MFMAs
-        __builtin_amdgcn_sched_barrier(0);
-        // mask keys >= S (only in the last tile)
-        const int k0 = kt * KT;
-        if (k0 + KT > S) {
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + b * 32 + rho(8 * (r >> 2) + 4 * lhalf + (r & 3));
-                    if (key >= S) sc[b][r] = -INFINITY;
-                }
-        }
-        // V^T fragments of the whole tile, read now so that they land during the softmax arithmetic
-        bf16x8_v vf[4][4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int d = 0; d < 4; ++d) vf[ks][d] = *(const bf16x8_v*)(bV + vOff[ks] + d * 4096);
-        __builtin_amdgcn_sched_barrier(0);
-        float tmax = sc[0][0];
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sc[b][r]);
-        {
-            float a, b;
-            swap32(tmax, a, b);
-            tmax = fmaxf(a, b);
-        }
-        const float mnew = fmaxf(mrun, tmax);
-        const float alpha = __builtin_amdgcn_exp2f((mrun - mnew) * c);
-        mrun = mnew;
-        const float mc = -mnew * c;
-        // P = exp2(c s - c m), rounded to bf16 once: the packed values feed both
-        // the P V product and the row sum (dot product with (1, 1)), so the
-        // normaliser sums exactly the weights that multiplied V
-        uint32_t pk[2][8];
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                pk[b][j] = pack_bf2(__builtin_amdgcn_exp2f(fmaf(sc[b][2 * j], c, mc)),
-                                    __builtin_amdgcn_exp2f(fmaf(sc[b][2 * j + 1], c, mc)));
-        float psum = 0.f;
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, pk[b][j]), ones, psum, false);
-        lrun = lrun * alpha + psum;
-        if (__ballot(alpha != 1.f)) {
-#pragma unroll
-            for (int d = 0; d < 4; ++d)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
-        }
-        // O^T += V^T P^T. P^T key step ks = registers 8 (ks % 2) .. +7 of block
-        // ks / 2, i.e. keys 16 ks + 8 h + 0..7 for lane half h; the A operand
-        // lane (dh row, half h) reads the same keys of V^T
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int b = ks >> 1, j0 = 4 * (ks & 1);
-            const bf16x8_v pf =
-                __builtin_bit_cast(bf16x8_v, make_uint4(pk[b][j0], pk[b][j0 + 1], pk[b][j0 + 2], pk[b][j0 + 3]));
-#pragma unroll
-            for (int d = 0; d < 4; ++d) o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks][d], pf, o[d], 0, 0, 0);
-        }
-        vmwait(std::integral_constant<int, LPT * (NST - 2)>{});
-        lds_barrier();
-    };
-
-    issue(0, std::integral_constant<int, 0>{});
-    if constexpr (NST == 3) issue(min(1, nkt - 1), std::integral_constant<int, 1>{});
-    vmwait(std::integral_constant<int, LPT * (NST - 2)>{});
-    lds_barrier();
-    for (int kt = 0; kt < nkt; kt += NST) {
-        static_for<NST>([&](auto b) {
-            if (kt + b < nkt) tile(kt + b, b);
-        });
-    }
-    vmwait(std::integral_constant<int, 0>{});   // the repeated fills past the last tile
-
-    float l0, l1;
-    swap32(lrun, l0, l1);
-    const float ltot = l0 + l1;
-    const float inv = 1.f / ltot;
-    const int q = q0 + lrow;
-    float mx = 0.f;
-    if (q < S) {
-        bf16_t* orow = O + (size_t)q * nh * DH + head * DH;
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                float v0 = o[d][4 * g] * inv, v1 = o[d][4 * g + 1] * inv;
-                float v2 = o[d][4 * g + 2] * inv, v3 = o[d][4 * g + 3] * inv;
-                uint2 w = make_uint2(pack_bf2(v0, v1), pack_bf2(v2, v3));
-                *(uint2*)(orow + d * 32 + 8 * g + 4 * lhalf) = w;
-                if (o_amax) {
-                    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(bf2f(f2bf(v0))), fabsf(bf2f(f2bf(v1)))),
-                                         fmaxf(fabsf(bf2f(f2bf(v2))), fabsf(bf2f(f2bf(v3))))));
-                }
-            }
-    }
-    if (o_amax) {
-        mx = wave_max(mx);
-        if (lane == 0) atomic_max_nonneg(o_amax, mx);
-    }
-#endif  // device pass only: the host pass keeps just the launch stub
-}
-
-// Software-pipelined bf16 kernel (same tiling, fragment layouts and numerics
-// as attn_bf16_kernel): iteration t issues the score MFMAs of key tile t next
+// Software pipelining: iteration t issues the score MFMAs of key tile t next
 // to the rescale of O, then the P V MFMAs of tile t - 1 next to the softmax of
 // tile t, so that each wave's own instruction stream keeps its SIMD's matrix
 // core and VALU busy together instead of alternating between them. K and V^T
@@ -569,8 +313,17 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void attn_bf16_pipe_ker
             }
     }
     if (o_amax) {
+        // one atomic per workgroup
+        __shared__ float wmax[NW];
         mx = wave_max(mx);
-        if (lane == 0) atomic_max_nonneg(o_amax, mx);
+        if (lane == 0) wmax[wave] = mx;
+        __syncthreads();
+        if (tid == 0) {
+            float m = wmax[0];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) m = fmaxf(m, wmax[w]);
+            atomic_max_nonneg(o_amax, m);
+        }
     }
 #endif  // device pass only: the host pass keeps just the launch stub
 }

@@ -536,8 +536,19 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
     });
     if constexpr (MODE == EPI_SWIGLU) {
         if (ep.u_amax) {
+            // one atomic per workgroup; the wave maxima go to the tail of sT0,
+            // past the epilogue slices packed into it
+            static_assert(LDS_T - capT * SL >= NW * 4, "room for the wave maxima");
+            float* wmax = (float*)(sT0 + LDS_T - NW * 4);
             mx = wave_max(mx);
-            if (lane == 0) atomic_max_nonneg(ep.u_amax, mx);
+            if (lane == 0) wmax[wave] = mx;
+            __syncthreads();
+            if (tid == 0) {
+                float m = wmax[0];
+#pragma unroll
+                for (int w = 1; w < NW; ++w) m = fmaxf(m, wmax[w]);
+                atomic_max_nonneg(ep.u_amax, m);
+            }
         }
     }
 #endif  // device pass only: the host pass keeps just the launch stub
