@@ -25,7 +25,7 @@ import numpy as np
 from .configs import BlockDims, CONFIGS, FLASH_EVALS, FLASH_LAYERS, SWEEP_FRAMES, get_config  # noqa: F401
 
 # tensor ids inside one seed
-TID_X_TEXT, TID_X_VIDEO, TID_X_AUDIO = 0, 1, 2
+TID_X_TEXT, TID_X_VIDEO, TID_X_AUDIO, TID_X_CTRL = 0, 1, 2, 3
 TID_G1, TID_WQKV, TID_WO, TID_G2, TID_WGATE, TID_WUP, TID_WDOWN = 10, 11, 12, 13, 14, 15, 16
 WEIGHT_NAMES = ("g1", "wqkv", "wo", "g2", "wgate", "wup", "wdown")
 
@@ -83,14 +83,18 @@ def _fmt(x, dtype):
 
 
 def activations(d: BlockDims, seed: int, dtype: str = None) -> dict:
-    """x_text [Nt, D], x_video [T, H, W, D], x_audio [Na, D] as fp32 arrays
-    (bf16-exact values when the configuration is bf16 or fp8)."""
+    """x_text [Nt, D], x_video [T, H, W, D], x_audio [Na, D] (and x_ctrl
+    [n_ctrl, H, W, D] when the configuration has control frames) as fp32
+    arrays (bf16-exact values when the configuration is bf16 or fp8)."""
     dtype = dtype or d.dtype
-    return {
+    out = {
         "x_text": _fmt(_normal(seed, TID_X_TEXT, (d.n_text, d.d_model)), dtype),
         "x_video": _fmt(_normal(seed, TID_X_VIDEO, (d.T, d.H, d.W, d.d_model)), dtype),
         "x_audio": _fmt(_normal(seed, TID_X_AUDIO, (d.n_audio, d.d_model)), dtype),
     }
+    if getattr(d, "n_ctrl", 0):
+        out["x_ctrl"] = _fmt(_normal(seed, TID_X_CTRL, (d.n_ctrl, d.H, d.W, d.d_model)), dtype)
+    return out
 
 
 def weights(d: BlockDims, seed: int, dtype: str = None, layer: int = None) -> dict:

@@ -28,6 +28,8 @@ class BlockDims:
     rope_base: float = 10000.0
     eps: float = 1e-6
     stride: int = 2
+    n_ctrl: int = 0        # control frames at the video's spatial grid (0: none)
+    ctrl_offset: int = 0   # target time minus control time (> 0 with control frames)
 
     @property
     def inner(self) -> int:
@@ -36,6 +38,10 @@ class BlockDims:
     @property
     def n_video(self) -> int:
         return self.T * self.H * self.W
+
+    @property
+    def n_ctrl_tokens(self) -> int:
+        return self.n_ctrl * self.H * self.W
 
     def with_(self, **kw) -> "BlockDims":
         return replace(self, **kw)

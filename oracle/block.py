@@ -25,7 +25,19 @@ the reasons in the design notes):
     coordinates), audio token j rotates only its t band by position j, text
     does not rotate;
   * "the update" of a kept token is y - X (attention plus feed-forward);
-  * sequence order [text | video (t, h, w raster) | audio].
+  * sequence order [text | video (t, h, w raster) | control | audio].
+
+Control frames (tokendh.com article, backbone section: a reference's time
+coordinate sits a fixed positive constant before the target's; PaperDaily
+review, section 1: aligned control frames and targets keep a stable positive
+time offset, one-to-one in position but never at the same time). Readings:
+x_ctrl [Tc, H, W, D] holds control frames on the video's spatial grid; control
+frame k has coordinates (k, h, w) and rotates all three bands; with a
+control offset c the video tokens use (t + c, h, w) and audio token j the
+t-position j + c (every time position moves together, so the logits among
+video and audio tokens do not change); control tokens are never compressed;
+their block outputs are returned, and the sampler re-feeds the control frames
+every evaluation, like text.
 """
 from __future__ import annotations
 
@@ -86,19 +98,27 @@ def swiglu(n2: np.ndarray, wgate: np.ndarray, wup: np.ndarray, lowbit: bool = Fa
     return silu(n2 @ wgate.T) * (n2 @ wup.T)
 
 
-def token_coords(d, compressed: bool, stride: int = None):
-    """Per token of the joint sequence: coordinates [S, 3] and kind [S]."""
+def grid_coords(T: int, H: int, W: int) -> np.ndarray:
+    """(t, h, w) of every position of a [T, H, W] grid in raster order."""
+    t, h, w = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    return np.stack([t.ravel(), h.ravel(), w.ravel()], axis=1).astype(np.int64)
+
+
+def token_coords(d, compressed: bool, stride: int = None, t_shift: int = 0):
+    """Per token of the joint sequence: coordinates [S, 3] and kind [S].
+    t_shift moves every time position (video, control, audio) by a constant."""
     s = d.stride if stride is None else stride
+    nc, c = getattr(d, "n_ctrl", 0), getattr(d, "ctrl_offset", 0)
     text = np.zeros((d.n_text, 3), dtype=np.int64)
-    if compressed:
-        video = cmp.kept_coords(d.T, d.H, d.W, s)
-    else:
-        t, h, w = np.meshgrid(np.arange(d.T), np.arange(d.H), np.arange(d.W), indexing="ij")
-        video = np.stack([t.ravel(), h.ravel(), w.ravel()], axis=1).astype(np.int64)
+    video = cmp.kept_coords(d.T, d.H, d.W, s) if compressed else grid_coords(d.T, d.H, d.W)
+    video = video.copy()
+    video[:, 0] += c + t_shift
+    ctrl = grid_coords(nc, d.H, d.W)
+    ctrl[:, 0] += t_shift
     audio = np.zeros((d.n_audio, 3), dtype=np.int64)
-    audio[:, 0] = np.arange(d.n_audio)
-    coords = np.concatenate([text, video, audio], axis=0)
-    kinds = np.concatenate([np.full(d.n_text, KIND_TEXT), np.full(len(video), KIND_VIDEO),
+    audio[:, 0] = np.arange(d.n_audio) + c + t_shift
+    coords = np.concatenate([text, video, ctrl, audio], axis=0)
+    kinds = np.concatenate([np.full(d.n_text, KIND_TEXT), np.full(len(video) + len(ctrl), KIND_VIDEO),
                             np.full(d.n_audio, KIND_AUDIO)]).astype(np.int64)
     return coords, kinds
 
@@ -176,46 +196,58 @@ def block_core(X: np.ndarray, coords: np.ndarray, kinds: np.ndarray, w: BlockWei
 
 
 def block_forward(x_text, x_video, x_audio, w: BlockWeights, d, compress: bool, stride: int = None,
-                  sample: dict = None):
+                  sample: dict = None, x_ctrl=None, t_shift: int = 0):
     """The full block on the three inputs (x_video [T, H, W, D]).
 
-    Returns (y_text [Nt, D], y_video [T, H, W, D], y_audio [Na, D]).
+    Returns (y_text [Nt, D], y_video [T, H, W, D], y_audio [Na, D]), and
+    y_ctrl [Tc, H, W, D] as a fourth element when x_ctrl is given.
     With compress=True the joint sequence holds only the kept video tokens;
     text and audio outputs come from the block, and every video position gets
     x + (update of its nearest kept slot).
 
     sample = {"text": idx, "video": flat positions, "audio": idx} evaluates only
-    those outputs (returned flat, in the same three-tuple form)."""
+    those outputs (returned flat, in the same three-tuple form; no control
+    frames)."""
     s = d.stride if stride is None else stride
     D = d.d_model
+    nc = getattr(d, "n_ctrl", 0)
+    if (x_ctrl is None) != (nc == 0):
+        raise ValueError("x_ctrl must be given exactly when the configuration has control frames")
+    if nc and getattr(d, "ctrl_offset", 0) < 1:
+        raise ValueError("control frames need a positive time offset")
     xt = np.asarray(x_text, dtype=np.float64).reshape(d.n_text, D)
     xv = np.asarray(x_video, dtype=np.float64).reshape(d.n_video, D)
     xa = np.asarray(x_audio, dtype=np.float64).reshape(d.n_audio, D)
-    coords, kinds = token_coords(d, compress, s)
+    xc = np.asarray(x_ctrl, dtype=np.float64).reshape(nc * d.H * d.W, D) if nc else np.zeros((0, D))
+    coords, kinds = token_coords(d, compress, s, t_shift)
     if compress:
         keep = cmp.keep_index(d.T, d.H, d.W, s)
         nk = cmp.nearest_kept_map(d.T, d.H, d.W, s)
         xv_seq = xv[keep]
     else:
         xv_seq = xv
-    nvs = len(xv_seq)
-    X = np.concatenate([xt, xv_seq, xa], axis=0)
+    nvs, ncs = len(xv_seq), len(xc)
+    X = np.concatenate([xt, xv_seq, xc, xa], axis=0)
 
     if sample is None:
         y = block_core(X, coords, kinds, w, d)
-        yt, yv_seq, ya = y[:d.n_text], y[d.n_text:d.n_text + nvs], y[d.n_text + nvs:]
+        yt, yv_seq = y[:d.n_text], y[d.n_text:d.n_text + nvs]
+        yc, ya = y[d.n_text + nvs:d.n_text + nvs + ncs], y[d.n_text + nvs + ncs:]
         if compress:
             delta = yv_seq - xv_seq
             yv = xv + delta[nk]
         else:
             yv = yv_seq
-        return yt, yv.reshape(d.T, d.H, d.W, D), ya
+        out = (yt, yv.reshape(d.T, d.H, d.W, D), ya)
+        return out + (yc.reshape(nc, d.H, d.W, D),) if nc else out
+    if nc:
+        raise ValueError("row sampling is not available with control frames")
 
     st = np.asarray(sample.get("text", []), dtype=np.int64)
     sv = np.asarray(sample.get("video", []), dtype=np.int64)
     sa = np.asarray(sample.get("audio", []), dtype=np.int64)
     vslots = nk[sv] if compress else sv
-    rows = np.concatenate([st, d.n_text + vslots, d.n_text + nvs + sa]).astype(np.int64)
+    rows = np.concatenate([st, d.n_text + vslots, d.n_text + nvs + ncs + sa]).astype(np.int64)
     y = block_core(X, coords, kinds, w, d, rows=rows)
     yt, yv_rows, ya = y[:len(st)], y[len(st):len(st) + len(sv)], y[len(st) + len(sv):]
     if compress:

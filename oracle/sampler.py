@@ -36,11 +36,12 @@ def flash_layer_flags(n_full_head: int = 2, n_compressed: int = 26, n_full_tail:
     return np.asarray([0] * n_full_head + [1] * n_compressed + [0] * n_full_tail, dtype=np.uint8)
 
 
-def stack_sample(x_text, x_video, x_audio, layers, flags, t_video, t_audio, d):
+def stack_sample(x_text, x_video, x_audio, layers, flags, t_video, t_audio, d, x_ctrl=None):
     """Run len(t_video) - 1 evaluations of the layer stack with Euler updates.
 
     Every compressed layer is applied literally (gather the kept tokens,
     compute, broadcast the nearest-kept update onto the full features).
+    Control frames (x_ctrl) are re-fed unchanged every evaluation, like text.
     Returns the final (x_video, x_audio) in fp64."""
     t_video = np.asarray(t_video, dtype=np.float64)
     t_audio = t_video if t_audio is None else np.asarray(t_audio, dtype=np.float64)
@@ -48,9 +49,12 @@ def stack_sample(x_text, x_video, x_audio, layers, flags, t_video, t_audio, d):
     xv = np.asarray(x_video, dtype=np.float64)
     xa = np.asarray(x_audio, dtype=np.float64)
     for k in range(len(t_video) - 1):
-        zt, zv, za = xt, xv, xa
+        zt, zv, za, zc = xt, xv, xa, x_ctrl
         for w, c in zip(layers, flags):
-            zt, zv, za = block_forward(zt, zv, za, w, d, compress=bool(c))
+            if zc is None:
+                zt, zv, za = block_forward(zt, zv, za, w, d, compress=bool(c))
+            else:
+                zt, zv, za, zc = block_forward(zt, zv, za, w, d, compress=bool(c), x_ctrl=zc)
         xv = xv + (t_video[k + 1] - t_video[k]) * zv
         xa = xa + (t_audio[k + 1] - t_audio[k]) * za
     return xv, xa
