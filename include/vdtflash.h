@@ -79,6 +79,8 @@ typedef struct {
     int32_t stride;               /* compression stride (2 in the Flash layers; 1 keeps every token) */
     int32_t act_dtype;            /* dit_dtype of activations and gains */
     int32_t w_dtype;              /* dit_dtype of the projection weights */
+    int32_t n_ctrl;               /* control frames on the video's H x W grid (0: none; *_ctrl calls only) */
+    int32_t ctrl_offset;          /* target time minus control time, >= 1 with control frames */
 } dit_dims;
 
 /* One block's parameters (device pointers). Gains g1, g2 [D] have act_dtype;
@@ -134,6 +136,24 @@ int32_t dit_block_forward(const dit_dims* dims,
                           void* y_text, void* y_video, void* y_audio,
                           void* ws, size_t ws_bytes, void* stream);
 
+/* The same block with control frames [TDH-backbone] (a reference's time
+ * coordinate sits a fixed positive constant before the target's), [PD-1]
+ * (aligned control frames and targets keep a stable positive time offset).
+ * x_ctrl [n_ctrl][H][W][D] (act_dtype) joins the sequence after the video
+ * tokens: X = [x_text | video tokens | x_ctrl | x_audio]. Rotary coordinates:
+ * control frame k uses (k, h, w); video tokens use (t + ctrl_offset, h, w) and
+ * audio token j the t position j + ctrl_offset (every time position moves
+ * together, which leaves the logits among video and audio unchanged). Control
+ * tokens are never compressed; y_ctrl [n_ctrl][H][W][D] receives their rows of
+ * y (may alias x_ctrl). Needs n_ctrl >= 1 and ctrl_offset >= 1; everything
+ * else as dit_block_forward, whose dims must have n_ctrl == 0. */
+int32_t dit_block_forward_ctrl(const dit_dims* dims,
+                               const void* x_text, const void* x_video, const void* x_ctrl, const void* x_audio,
+                               const dit_block_weights* weights, int32_t compress_on,
+                               const int32_t* keep, const int32_t* nk,
+                               void* y_text, void* y_video, void* y_ctrl, void* y_audio,
+                               void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes for dit_stack_sample with these dims and layer flags. */
 int32_t dit_stack_workspace_size(const dit_dims* dims, const uint8_t* compressed_host, int32_t n_layers,
                                  size_t* bytes);
@@ -155,6 +175,16 @@ int32_t dit_stack_sample(const dit_dims* dims, const dit_block_weights* layers_h
                          const void* x_text, void* x_video, void* x_audio,
                          const int32_t* keep, const int32_t* nk,
                          void* ws, size_t ws_bytes, void* stream);
+
+/* The sampler with control frames (see dit_block_forward_ctrl): every layer
+ * runs on [x_text | x_video | x_ctrl | x_audio], and the control frames are
+ * re-fed unchanged each evaluation, like text. dims must have n_ctrl >= 1. */
+int32_t dit_stack_sample_ctrl(const dit_dims* dims, const dit_block_weights* layers_host, int32_t n_layers,
+                              const uint8_t* compressed_host, int32_t n_evals,
+                              const float* t_video_host, const float* t_audio_host,
+                              const void* x_text, void* x_video, const void* x_ctrl, void* x_audio,
+                              const int32_t* keep, const int32_t* nk,
+                              void* ws, size_t ws_bytes, void* stream);
 
 /* Per-tensor e4m3 quantisation of a weight tensor [PD-2] (low-bit
  * projections): amax = max |src|, dst = e4m3(saturate(src * (448 / amax))) with

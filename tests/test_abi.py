@@ -55,6 +55,9 @@ def _dims(**kw):
     (dict(act_dtype=_lib.DIT_F32), _lib.DIT_EUNSUPPORTED),       # f32 activations with bf16 weights
     (dict(w_dtype=7), _lib.DIT_EUNSUPPORTED),
     (dict(d_model=5376 + 64), _lib.DIT_EUNSUPPORTED),          # bf16 path wants multiples of 128
+    (dict(n_ctrl=1, ctrl_offset=0), _lib.DIT_EINVAL),          # control frames need a positive offset
+    (dict(n_ctrl=-1), _lib.DIT_EINVAL),
+    (dict(ctrl_offset=-2), _lib.DIT_EINVAL),
 ])
 def test_dims_rejected(bad, code):
     n = ctypes.c_size_t()
@@ -110,3 +113,32 @@ def test_workspace_grows_with_sequence():
     V.lib().dit_block_workspace_size(ctypes.byref(d), 1, ctypes.byref(a))
     V.lib().dit_block_workspace_size(ctypes.byref(d), 0, ctypes.byref(b))
     assert 0 < a.value < b.value
+
+
+def test_control_frame_entry_points_reject():
+    """The plain calls refuse dims with control frames, the *_ctrl calls dims
+    without them; a control workspace covers the extra rows."""
+    lib = V.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    ws = ctypes.c_void_p(1 << 24)
+    wf = _lib.BlockWeights(*([fake] * 7))
+    dc = _dims(n_ctrl=2, ctrl_offset=3)
+    st = lib.dit_block_forward(ctypes.byref(dc), fake, fake, fake, ctypes.byref(wf), 0, None, None, fake, fake, fake,
+                               ws, 1 << 40, None)
+    assert st == _lib.DIT_EINVAL
+    d0 = _dims()
+    st = lib.dit_block_forward_ctrl(ctypes.byref(d0), fake, fake, fake, fake, ctypes.byref(wf), 0, None, None, fake,
+                                    fake, fake, fake, ws, 1 << 40, None)
+    assert st == _lib.DIT_EINVAL
+    # missing control pointers
+    st = lib.dit_block_forward_ctrl(ctypes.byref(dc), fake, fake, None, fake, ctypes.byref(wf), 0, None, None, fake,
+                                    fake, None, fake, ws, 1 << 40, None)
+    assert st == _lib.DIT_EINVAL
+    assert lib.dit_stack_sample(ctypes.byref(dc), None, 0, None, 1, None, None, fake, fake, fake, None, None, ws,
+                                1 << 40, None) == _lib.DIT_EINVAL
+    assert lib.dit_stack_sample_ctrl(ctypes.byref(d0), None, 0, None, 1, None, None, fake, fake, fake, fake, None,
+                                     None, ws, 1 << 40, None) == _lib.DIT_EINVAL
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    lib.dit_block_workspace_size(ctypes.byref(d0), 1, ctypes.byref(a))
+    lib.dit_block_workspace_size(ctypes.byref(dc), 1, ctypes.byref(b))
+    assert b.value > a.value

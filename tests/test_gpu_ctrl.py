@@ -1,0 +1,98 @@
+"""GPU parity of the block and the sampler with control frames (a fixed
+positive time offset before the target frames) against the fp64 oracle, and
+the permutation equivalence with the plain block on the GPU itself.
+
+Bars as for the plain block: 1e-4 (fp32), 2e-2 (bf16) on max|err|/RMS; fp8:
+6e-2 on the RMS error and the e4m3 code-flip bound on the max error."""
+import numpy as np
+import pytest
+
+import oracle as O
+from dit_synth import BlockDims
+from helpers import FP8_MAX_BOUND, gpu_weights, inputs, oracle_weights, rel_err, rms_err, to_numpy, torch_act
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+V = pytest.importorskip("video_diffusion_transformer_flash_amd")
+
+TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 6e-2}
+
+CTRL_BF16 = BlockDims("ctrl_bf16", d_model=512, n_heads=4, head_dim=128, d_ffn=1024, T=2, H=9, W=15, n_text=16,
+                      n_audio=8, rope=(32, 48, 48), dtype="bf16", seed=11, n_ctrl=2, ctrl_offset=3)
+CTRL_F32 = BlockDims("ctrl_f32", d_model=256, n_heads=4, head_dim=64, d_ffn=704, T=2, H=9, W=15, n_text=16,
+                     n_audio=8, rope=(16, 24, 24), dtype="f32", seed=12, n_ctrl=1, ctrl_offset=2)
+CONFIGS = {"bf16": CTRL_BF16, "fp8": CTRL_BF16.with_(name="ctrl_fp8", dtype="fp8", seed=13), "f32": CTRL_F32}
+
+
+def run_gpu(d, x, w, compress):
+    dims = V.make_dims(d)
+    xt, xv, xa, xc = (torch_act(x[k], d.dtype) for k in ("x_text", "x_video", "x_audio", "x_ctrl"))
+    gw, _ = gpu_weights(w, d.dtype)
+    keep = V.keep_index(d.T, d.H, d.W, d.stride) if compress else None
+    nk = V.nearest_kept_map(d.T, d.H, d.W, d.stride) if compress else None
+    yt, yv, ya, yc = V.block_forward(dims, xt, xv, xa, gw, compress, keep, nk, x_ctrl=xc)
+    torch.cuda.synchronize()
+    return [to_numpy(yt), to_numpy(yv), to_numpy(ya), to_numpy(yc)]
+
+
+def check(got, ref, dtype):
+    err, rerr = rel_err(got, ref), rms_err(got, ref)
+    print(f"  max|err|/rms = {err:.3e}, rms err = {rerr:.3e} (bar {TOL[dtype]})")
+    assert np.all(np.isfinite(np.concatenate([g.ravel() for g in got])))
+    if dtype == "fp8":
+        assert rerr <= TOL["fp8"] and err <= FP8_MAX_BOUND
+    else:
+        assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("compress", [False, True])
+def test_ctrl_block_vs_oracle(dtype, compress):
+    d = CONFIGS[dtype]
+    print(f"ctrl block {d.name} compress={compress}", flush=True)
+    x, w = inputs(d)
+    got = run_gpu(d, x, w, compress)
+    ref = O.block_forward(x["x_text"], x["x_video"], x["x_audio"], oracle_weights(w, dtype), d, compress,
+                          x_ctrl=x["x_ctrl"])
+    check(got, list(ref), dtype)
+
+
+def test_ctrl_block_is_plain_block_over_control_then_video_on_gpu():
+    """Offset = number of control frames, no audio: the block with control
+    frames equals the plain block on the frames [control | video] (another
+    token order of the same sequence and coordinates)."""
+    d = CTRL_F32.with_(n_audio=0, n_ctrl=2, ctrl_offset=2)
+    x, w = inputs(d)
+    yt, yv, ya, yc = run_gpu(d, x, w, False)
+    dp = d.with_(T=d.n_ctrl + d.T, n_ctrl=0, ctrl_offset=0)
+    dims = V.make_dims(dp)
+    xv = torch_act(np.concatenate([x["x_ctrl"], x["x_video"]], axis=0), "f32")
+    xt, xa = torch_act(x["x_text"], "f32"), torch_act(x["x_audio"], "f32")
+    gw, _ = gpu_weights(w, "f32")
+    pt, pv, pa = V.block_forward(dims, xt, xv, xa, gw, False)
+    torch.cuda.synchronize()
+    pv = to_numpy(pv)
+    assert rel_err([yt, yc, yv], [to_numpy(pt), pv[:d.n_ctrl], pv[d.n_ctrl:]]) <= 1e-5
+
+
+def test_ctrl_stack_vs_oracle():
+    d = CTRL_BF16.with_(name="ctrl_stack", d_model=256, n_heads=2, d_ffn=512, seed=14)
+    flags = [0, 1, 1, 0]
+    tv, ta = O.flow_schedule(3, 12.0), O.flow_schedule(3, 3.0)
+    print(f"ctrl stack flags={flags}", flush=True)
+    x, _ = inputs(d)
+    layers = [inputs(d, layer=l)[1] for l in range(len(flags))]
+    dims = V.make_dims(d)
+    xt, xv, xa, xc = (torch_act(x[k], d.dtype) for k in ("x_text", "x_video", "x_audio", "x_ctrl"))
+    gl = [gpu_weights(lw, d.dtype)[0] for lw in layers]
+    keep, nk = V.keep_index(d.T, d.H, d.W), V.nearest_kept_map(d.T, d.H, d.W)
+    xc0 = to_numpy(xc).copy()
+    V.stack_sample(dims, gl, flags, tv, ta, xt, xv, xa, keep, nk, x_ctrl=xc)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_numpy(xc), xc0)   # control frames are inputs only
+    ref = O.stack_sample(x["x_text"], x["x_video"], x["x_audio"], [oracle_weights(lw, "bf16") for lw in layers], flags,
+                         tv.astype(np.float32), ta.astype(np.float32), d, x_ctrl=x["x_ctrl"])
+    err = rel_err([to_numpy(xv), to_numpy(xa)], list(ref))
+    print(f"  max|err|/rms = {err:.3e}")
+    assert err <= 6e-2

@@ -40,7 +40,8 @@ def make_dims(cfg, stride: int = None) -> Dims:
     return Dims(T=cfg.T, H=cfg.H, W=cfg.W, n_text=cfg.n_text, n_audio=cfg.n_audio, d_model=cfg.d_model,
                 n_heads=cfg.n_heads, head_dim=cfg.head_dim, d_ffn=cfg.d_ffn, rope_t=cfg.rope[0], rope_h=cfg.rope[1],
                 rope_w=cfg.rope[2], rope_base=cfg.rope_base, eps=cfg.eps,
-                stride=cfg.stride if stride is None else stride, act_dtype=_ACT[cfg.dtype], w_dtype=_WT[cfg.dtype])
+                stride=cfg.stride if stride is None else stride, act_dtype=_ACT[cfg.dtype], w_dtype=_WT[cfg.dtype],
+                n_ctrl=getattr(cfg, "n_ctrl", 0), ctrl_offset=getattr(cfg, "ctrl_offset", 0))
 
 
 def keep_dims(H: int, W: int, stride: int = 2):
@@ -82,19 +83,29 @@ def workspace(nbytes: int):
 
 
 def block_forward(dims: Dims, x_text, x_video, x_audio, weights: dict, compress: bool, keep=None, nk=None,
-                  out=None, ws=None):
-    """One block; returns (y_text, y_video, y_audio). `out` may be the inputs
-    themselves (in place)."""
+                  out=None, ws=None, x_ctrl=None):
+    """One block; returns (y_text, y_video, y_audio), and y_ctrl as a fourth
+    element when x_ctrl (control frames, dims.n_ctrl > 0) is given. `out` may
+    be the inputs themselves (in place)."""
     if out is None:
         out = (torch.empty_like(x_text), torch.empty_like(x_video), torch.empty_like(x_audio))
+        if x_ctrl is not None:
+            out = out + (torch.empty_like(x_ctrl),)
     need = block_workspace_size(dims, compress)
     if ws is None:
         ws = workspace(need)
     w = _weights_struct(weights)
-    st = lib().dit_block_forward(ctypes.byref(dims), _ptr(x_text), _ptr(x_video), _ptr(x_audio), ctypes.byref(w),
-                                 int(compress), _ptr(keep), _ptr(nk), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]),
-                                 _ptr(ws), ws.numel(), _stream())
-    check(st, "dit_block_forward")
+    if x_ctrl is None:
+        st = lib().dit_block_forward(ctypes.byref(dims), _ptr(x_text), _ptr(x_video), _ptr(x_audio), ctypes.byref(w),
+                                     int(compress), _ptr(keep), _ptr(nk), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]),
+                                     _ptr(ws), ws.numel(), _stream())
+        check(st, "dit_block_forward")
+    else:
+        st = lib().dit_block_forward_ctrl(ctypes.byref(dims), _ptr(x_text), _ptr(x_video), _ptr(x_ctrl),
+                                          _ptr(x_audio), ctypes.byref(w), int(compress), _ptr(keep), _ptr(nk),
+                                          _ptr(out[0]), _ptr(out[1]), _ptr(out[3]), _ptr(out[2]), _ptr(ws),
+                                          ws.numel(), _stream())
+        check(st, "dit_block_forward_ctrl")
     return out
 
 
@@ -107,8 +118,9 @@ def stack_workspace_size(dims: Dims, flags) -> int:
 
 
 def stack_sample(dims: Dims, layers: list, flags, t_video, t_audio, x_text, x_video, x_audio, keep=None, nk=None,
-                 ws=None):
-    """Flow-matching sampler; x_video and x_audio are updated in place."""
+                 ws=None, x_ctrl=None):
+    """Flow-matching sampler; x_video and x_audio are updated in place
+    (control frames x_ctrl, when given, are re-fed every evaluation)."""
     n = len(layers)
     arr = (BlockWeights * max(n, 1))(*[_weights_struct(w) for w in layers])
     fl = (ctypes.c_uint8 * max(n, 1))(*[int(f) for f in flags])
@@ -116,11 +128,18 @@ def stack_sample(dims: Dims, layers: list, flags, t_video, t_audio, x_text, x_vi
     ta = None if t_audio is None else (ctypes.c_float * len(t_audio))(*[float(t) for t in t_audio])
     if ws is None:
         ws = workspace(stack_workspace_size(dims, flags))
-    st = lib().dit_stack_sample(ctypes.byref(dims), arr, n, ctypes.cast(fl, ctypes.c_void_p), len(t_video) - 1,
-                                ctypes.cast(tv, ctypes.c_void_p),
-                                None if ta is None else ctypes.cast(ta, ctypes.c_void_p), _ptr(x_text),
-                                _ptr(x_video), _ptr(x_audio), _ptr(keep), _ptr(nk), _ptr(ws), ws.numel(), _stream())
-    check(st, "dit_stack_sample")
+    tac = None if ta is None else ctypes.cast(ta, ctypes.c_void_p)
+    if x_ctrl is None:
+        st = lib().dit_stack_sample(ctypes.byref(dims), arr, n, ctypes.cast(fl, ctypes.c_void_p), len(t_video) - 1,
+                                    ctypes.cast(tv, ctypes.c_void_p), tac, _ptr(x_text), _ptr(x_video),
+                                    _ptr(x_audio), _ptr(keep), _ptr(nk), _ptr(ws), ws.numel(), _stream())
+        check(st, "dit_stack_sample")
+    else:
+        st = lib().dit_stack_sample_ctrl(ctypes.byref(dims), arr, n, ctypes.cast(fl, ctypes.c_void_p),
+                                         len(t_video) - 1, ctypes.cast(tv, ctypes.c_void_p), tac, _ptr(x_text),
+                                         _ptr(x_video), _ptr(x_ctrl), _ptr(x_audio), _ptr(keep), _ptr(nk), _ptr(ws),
+                                         ws.numel(), _stream())
+        check(st, "dit_stack_sample_ctrl")
     return x_video, x_audio
 
 

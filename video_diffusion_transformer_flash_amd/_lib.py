@@ -18,7 +18,8 @@ class Dims(ctypes.Structure):
     _fields_ = [("T", c_i32), ("H", c_i32), ("W", c_i32), ("n_text", c_i32), ("n_audio", c_i32),
                 ("d_model", c_i32), ("n_heads", c_i32), ("head_dim", c_i32), ("d_ffn", c_i32),
                 ("rope_t", c_i32), ("rope_h", c_i32), ("rope_w", c_i32), ("rope_base", c_f32), ("eps", c_f32),
-                ("stride", c_i32), ("act_dtype", c_i32), ("w_dtype", c_i32)]
+                ("stride", c_i32), ("act_dtype", c_i32), ("w_dtype", c_i32), ("n_ctrl", c_i32),
+                ("ctrl_offset", c_i32)]
 
 
 class BlockWeights(ctypes.Structure):
@@ -35,9 +36,13 @@ SIGNATURES = {
     "dit_block_workspace_size": (c_i32, [ctypes.POINTER(Dims), c_i32, ctypes.POINTER(c_size)]),
     "dit_block_forward": (c_i32, [ctypes.POINTER(Dims), c_vp, c_vp, c_vp, ctypes.POINTER(BlockWeights), c_i32,
                                   c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "dit_block_forward_ctrl": (c_i32, [ctypes.POINTER(Dims), c_vp, c_vp, c_vp, c_vp, ctypes.POINTER(BlockWeights),
+                                       c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "dit_stack_workspace_size": (c_i32, [ctypes.POINTER(Dims), c_vp, c_i32, ctypes.POINTER(c_size)]),
     "dit_stack_sample": (c_i32, [ctypes.POINTER(Dims), ctypes.POINTER(BlockWeights), c_i32, c_vp, c_i32, c_vp, c_vp,
                                  c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "dit_stack_sample_ctrl": (c_i32, [ctypes.POINTER(Dims), ctypes.POINTER(BlockWeights), c_i32, c_vp, c_i32, c_vp,
+                                      c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "dit_quantize_fp8": (c_i32, [c_vp, c_i32, c_i64, c_vp, c_vp, c_vp]),
     "dit_gather_kept": (c_i32, [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "dit_broadcast_residual": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),

@@ -75,8 +75,10 @@ int validate_dims(const dit_dims* d) {
     if (d->rope_t < 0 || d->rope_h < 0 || d->rope_w < 0 || (d->rope_t | d->rope_h | d->rope_w) & 1) return DIT_EINVAL;
     if (d->rope_t + d->rope_h + d->rope_w != d->head_dim) return DIT_EINVAL;
     if (!(d->rope_base > 0.f) || !(d->eps >= 0.f)) return DIT_EINVAL;
+    if (d->n_ctrl < 0 || d->ctrl_offset < 0 || (d->n_ctrl > 0 && d->ctrl_offset < 1)) return DIT_EINVAL;
+    if (d->n_ctrl > (1 << 20) || d->ctrl_offset > (1 << 20)) return DIT_EINVAL;
     const long long nv = (long long)d->T * d->H * d->W;
-    const long long S = nv + d->n_text + d->n_audio;
+    const long long S = nv + (long long)d->n_ctrl * d->H * d->W + d->n_text + d->n_audio;
     if (S > (1LL << 30) || nv * d->d_model > (1LL << 40)) return DIT_EINVAL;
     const int a = d->act_dtype, w = d->w_dtype;
     const bool f32 = a == DIT_F32 && w == DIT_F32;
@@ -105,9 +107,10 @@ Plan make_plan(const dit_dims& d, int nv_seq, bool delta) {
     const size_t es = esize(d.act_dtype);
     const size_t D = d.d_model, I = (size_t)d.n_heads * d.head_dim, F = d.d_ffn;
     p.nv_seq = nv_seq;
-    p.S = d.n_text + nv_seq + d.n_audio;
+    p.S = d.n_text + nv_seq + d.n_ctrl * d.H * d.W + d.n_audio;
     p.Sp = (p.S + 127) / 128 * 128;
-    p.ntab_t = std::max(std::max(d.T, d.n_audio), 1);
+    // time positions: video t + off, control k, audio j + off
+    p.ntab_t = std::max(std::max(d.T + d.ctrl_offset, d.n_audio + d.ctrl_offset), std::max(d.n_ctrl, 1));
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t o = off;
@@ -160,7 +163,8 @@ int run_block(const dit_dims& d, const dit_block_weights& w, const SeqIn& in, co
     rope.vpos = vpos;
     rope.rt = d.rope_t; rope.rh = d.rope_h; rope.rw = d.rope_w;
     rope.H = d.H; rope.W = d.W;
-    rope.nt = in.nt; rope.nv = in.nv;
+    rope.nt = in.nt; rope.nv = in.nv; rope.nc = in.nc;
+    rope.toff = d.ctrl_offset;
     if (d.act_dtype != DIT_F32) {
         TR("rope_rows");
         HIPCHK(rope_rows_launch(rope, (float2*)(ws + P.rrows), P.S, d.head_dim / 2, st));
@@ -353,28 +357,32 @@ int32_t dit_block_workspace_size(const dit_dims* dims, int32_t compress_on, size
     return DIT_OK;
 }
 
-int32_t dit_block_forward(const dit_dims* dims, const void* x_text, const void* x_video, const void* x_audio,
-                          const dit_block_weights* weights, int32_t compress_on, const int32_t* keep,
-                          const int32_t* nk, void* y_text, void* y_video, void* y_audio, void* ws, size_t ws_bytes,
-                          void* stream) {
-    int r = validate_dims(dims);
-    if (r) return r;
+namespace {
+
+int block_forward_impl(const dit_dims* dims, const void* x_text, const void* x_video, const void* x_ctrl,
+                       const void* x_audio, const dit_block_weights* weights, int32_t compress_on, const int32_t* keep,
+                       const int32_t* nk, void* y_text, void* y_video, void* y_ctrl, void* y_audio, void* ws,
+                       size_t ws_bytes, void* stream) {
     const dit_dims& d = *dims;
+    int r;
     if ((r = check_weights(d, weights))) return r;
     if (!x_video || !y_video || !aligned16(x_video) || !aligned16(y_video)) return DIT_EINVAL;
     if (d.n_text > 0 && (!x_text || !y_text || !aligned16(x_text) || !aligned16(y_text))) return DIT_EINVAL;
     if (d.n_audio > 0 && (!x_audio || !y_audio || !aligned16(x_audio) || !aligned16(y_audio))) return DIT_EINVAL;
+    if (d.n_ctrl > 0 && (!x_ctrl || !y_ctrl || !aligned16(x_ctrl) || !aligned16(y_ctrl))) return DIT_EINVAL;
     if (compress_on && (!keep || !nk)) return DIT_EINVAL;
     if (!ws || ((uintptr_t)ws & 255)) return DIT_EINVAL;
     const int nv = d.T * d.H * d.W;
+    const int nc = d.n_ctrl * d.H * d.W;
     const int nkept = d.T * keep_count(d.H, d.stride) * keep_count(d.W, d.stride);
     const Plan P = make_plan(d, compress_on ? nkept : nv, compress_on != 0);
     if (ws_bytes < P.total) return DIT_EWORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     uint8_t* w8 = (uint8_t*)ws;
 
-    SeqIn in{x_text, x_video, x_audio, compress_on ? keep : nullptr, d.n_text, compress_on ? nkept : nv, d.n_audio};
-    SeqOut out{y_text, y_video, y_audio, compress_on ? (float*)(w8 + P.delta) : nullptr, nullptr, nullptr};
+    SeqIn in{x_text, x_video, x_ctrl, x_audio, compress_on ? keep : nullptr, d.n_text, compress_on ? nkept : nv, nc,
+             d.n_audio};
+    SeqOut out{y_text, y_video, y_ctrl, y_audio, compress_on ? (float*)(w8 + P.delta) : nullptr, nullptr, nullptr};
     r = run_block(d, *weights, in, compress_on ? keep : nullptr, out, in, w8, P, st);
     if (r) return r;
     if (compress_on) {
@@ -386,6 +394,30 @@ int32_t dit_block_forward(const dit_dims* dims, const void* x_text, const void* 
     return DIT_OK;
 }
 
+}  // namespace
+
+int32_t dit_block_forward(const dit_dims* dims, const void* x_text, const void* x_video, const void* x_audio,
+                          const dit_block_weights* weights, int32_t compress_on, const int32_t* keep,
+                          const int32_t* nk, void* y_text, void* y_video, void* y_audio, void* ws, size_t ws_bytes,
+                          void* stream) {
+    int r = validate_dims(dims);
+    if (r) return r;
+    if (dims->n_ctrl != 0) return DIT_EINVAL;
+    return block_forward_impl(dims, x_text, x_video, nullptr, x_audio, weights, compress_on, keep, nk, y_text, y_video,
+                              nullptr, y_audio, ws, ws_bytes, stream);
+}
+
+int32_t dit_block_forward_ctrl(const dit_dims* dims, const void* x_text, const void* x_video, const void* x_ctrl,
+                               const void* x_audio, const dit_block_weights* weights, int32_t compress_on,
+                               const int32_t* keep, const int32_t* nk, void* y_text, void* y_video, void* y_ctrl,
+                               void* y_audio, void* ws, size_t ws_bytes, void* stream) {
+    int r = validate_dims(dims);
+    if (r) return r;
+    if (dims->n_ctrl < 1) return DIT_EINVAL;
+    return block_forward_impl(dims, x_text, x_video, x_ctrl, x_audio, weights, compress_on, keep, nk, y_text, y_video,
+                              y_ctrl, y_audio, ws, ws_bytes, stream);
+}
+
 int32_t dit_stack_workspace_size(const dit_dims* dims, const uint8_t* compressed_host, int32_t n_layers,
                                  size_t* bytes) {
     int r = validate_dims(dims);
@@ -394,20 +426,22 @@ int32_t dit_stack_workspace_size(const dit_dims* dims, const uint8_t* compressed
     const dit_dims& d = *dims;
     const size_t es = esize(d.act_dtype);
     const int nv = d.T * d.H * d.W;
+    const int nc = d.n_ctrl * d.H * d.W;
     const int nkept = d.T * keep_count(d.H, d.stride) * keep_count(d.W, d.stride);
-    const size_t Soff = (size_t)d.n_text + nv + d.n_audio, Son = (size_t)d.n_text + nkept + d.n_audio;
+    const size_t Soff = (size_t)d.n_text + nv + nc + d.n_audio, Son = (size_t)d.n_text + nkept + nc + d.n_audio;
     const Plan Pf = make_plan(d, nv, false), Pc = make_plan(d, nkept, true);
     *bytes = align256(Soff * d.d_model * es) + align256(Son * d.d_model * es) + std::max(Pf.total, Pc.total);
     return DIT_OK;
 }
 
-int32_t dit_stack_sample(const dit_dims* dims, const dit_block_weights* layers_host, int32_t n_layers,
-                         const uint8_t* compressed_host, int32_t n_evals, const float* t_video_host,
-                         const float* t_audio_host, const void* x_text, void* x_video, void* x_audio,
-                         const int32_t* keep, const int32_t* nk, void* ws, size_t ws_bytes, void* stream) {
-    int r = validate_dims(dims);
-    if (r) return r;
+namespace {
+
+int stack_impl(const dit_dims* dims, const dit_block_weights* layers_host, int32_t n_layers,
+               const uint8_t* compressed_host, int32_t n_evals, const float* t_video_host,
+               const float* t_audio_host, const void* x_text, void* x_video, const void* x_ctrl, void* x_audio,
+               const int32_t* keep, const int32_t* nk, void* ws, size_t ws_bytes, void* stream) {
     const dit_dims& d = *dims;
+    int r;
     if (n_layers < 0 || n_evals < 0 || (n_layers > 0 && (!layers_host || !compressed_host))) return DIT_EINVAL;
     if (n_evals > 0 && !t_video_host) return DIT_EINVAL;
     bool any_c = false;
@@ -419,6 +453,7 @@ int32_t dit_stack_sample(const dit_dims* dims, const dit_block_weights* layers_h
     if (!x_video || !aligned16(x_video)) return DIT_EINVAL;
     if (d.n_text > 0 && (!x_text || !aligned16(x_text))) return DIT_EINVAL;
     if (d.n_audio > 0 && (!x_audio || !aligned16(x_audio))) return DIT_EINVAL;
+    if (d.n_ctrl > 0 && (!x_ctrl || !aligned16(x_ctrl))) return DIT_EINVAL;
     if (!ws || ((uintptr_t)ws & 255)) return DIT_EINVAL;
     size_t need = 0;
     dit_stack_workspace_size(dims, compressed_host, n_layers, &need);
@@ -429,9 +464,11 @@ int32_t dit_stack_sample(const dit_dims* dims, const dit_block_weights* layers_h
     const size_t es = esize(d.act_dtype);
     const bool bf = d.act_dtype == DIT_BF16;
     const size_t D = d.d_model;
+    const int nt = d.n_text, na = d.n_audio;
     const int nv = d.T * d.H * d.W;
+    const int nc = d.n_ctrl * d.H * d.W;
     const int nkept = d.T * keep_count(d.H, d.stride) * keep_count(d.W, d.stride);
-    const size_t Soff = (size_t)d.n_text + nv + d.n_audio, Son = (size_t)d.n_text + nkept + d.n_audio;
+    const size_t Soff = (size_t)nt + nv + nc + na, Son = (size_t)nt + nkept + nc + na;
     uint8_t* w8 = (uint8_t*)ws;
     uint8_t* Z = w8;
     uint8_t* Zc = Z + align256(Soff * D * es);
@@ -439,39 +476,44 @@ int32_t dit_stack_sample(const dit_dims* dims, const dit_block_weights* layers_h
     const Plan Pf = make_plan(d, nv, false), Pc = make_plan(d, nkept, true);
     float* delta = (float*)(bws + Pc.delta);
 
+    // full-resolution state [text | video | control | audio] and the packed
+    // compressed state [text | kept video | control | audio]
     void* Zt = Z;
-    void* Zv = Z + (size_t)d.n_text * D * es;
-    void* Za = Z + ((size_t)d.n_text + nv) * D * es;
+    void* Zv = Z + (size_t)nt * D * es;
+    void* Zk = Z + ((size_t)nt + nv) * D * es;
+    void* Za = Z + ((size_t)nt + nv + nc) * D * es;
     void* Zct = Zc;
-    void* Zcv = Zc + (size_t)d.n_text * D * es;
-    void* Zca = Zc + ((size_t)d.n_text + nkept) * D * es;
+    void* Zcv = Zc + (size_t)nt * D * es;
+    void* Zck = Zc + ((size_t)nt + nkept) * D * es;
+    void* Zca = Zc + ((size_t)nt + nkept + nc) * D * es;
+    const SeqIn state{Zt, Zv, Zk, Za, nullptr, nt, nv, nc, na};
 
     for (int ev = 0; ev < n_evals; ++ev) {
         // current full-resolution state: the inputs for the first layer, Z after
-        SeqIn cur{x_text, x_video, x_audio, nullptr, d.n_text, nv, d.n_audio};
+        SeqIn cur{x_text, x_video, x_ctrl, x_audio, nullptr, nt, nv, nc, na};
         int l = 0;
         while (l < n_layers) {
             if (!compressed_host[l]) {
-                SeqOut out{Zt, Zv, Za, nullptr, nullptr, nullptr};
+                SeqOut out{Zt, Zv, Zk, Za, nullptr, nullptr, nullptr};
                 if ((r = run_block(d, layers_host[l], cur, nullptr, out, cur, bws, Pf, st))) return r;
-                cur = SeqIn{Zt, Zv, Za, nullptr, d.n_text, nv, d.n_audio};
+                cur = state;
                 ++l;
                 continue;
             }
             int e = l;
             while (e < n_layers && compressed_host[e]) ++e;
             // span [l, e): gather on read at its start, broadcast the summed update at its end
-            const SeqIn start{cur.xt, cur.xv, cur.xa, keep, d.n_text, nkept, d.n_audio};
-            const SeqIn packed{Zct, Zcv, Zca, nullptr, d.n_text, nkept, d.n_audio};
+            const SeqIn start{cur.xt, cur.xv, cur.xc, cur.xa, keep, nt, nkept, nc, na};
+            const SeqIn packed{Zct, Zcv, Zck, Zca, nullptr, nt, nkept, nc, na};
             for (int i = l; i < e; ++i) {
                 const SeqIn& in = (i == l) ? start : packed;
-                SeqOut out = (i + 1 < e) ? SeqOut{Zct, Zcv, Zca, nullptr, nullptr, nullptr}
-                                         : SeqOut{Zt, nullptr, Za, delta, nullptr, nullptr};
+                SeqOut out = (i + 1 < e) ? SeqOut{Zct, Zcv, Zck, Zca, nullptr, nullptr, nullptr}
+                                         : SeqOut{Zt, nullptr, Zk, Za, delta, nullptr, nullptr};
                 if ((r = run_block(d, layers_host[i], in, keep, out, start, bws, Pc, st))) return r;
             }
             TR("broadcast_residual");
             HIPCHK(broadcast_residual_launch(bf, cur.xv, delta, nk, Zv, nv, (int)D, st));
-            cur = SeqIn{Zt, Zv, Za, nullptr, d.n_text, nv, d.n_audio};
+            cur = state;
             l = e;
         }
         const float dtv = (float)((double)t_video_host[ev + 1] - (double)t_video_host[ev]);
@@ -482,10 +524,35 @@ int32_t dit_stack_sample(const dit_dims* dims, const dit_block_weights* layers_h
         const void* va = n_layers ? (const void*)Za : (const void*)x_audio;
         TR("euler");
         HIPCHK(euler_launch(bf, x_video, vv, (size_t)nv * D, dtv, st));
-        if (d.n_audio > 0) HIPCHK(euler_launch(bf, x_audio, va, (size_t)d.n_audio * D, dta, st));
+        if (na > 0) HIPCHK(euler_launch(bf, x_audio, va, (size_t)na * D, dta, st));
     }
     TR("end");
     return DIT_OK;
+}
+
+}  // namespace
+
+int32_t dit_stack_sample(const dit_dims* dims, const dit_block_weights* layers_host, int32_t n_layers,
+                         const uint8_t* compressed_host, int32_t n_evals, const float* t_video_host,
+                         const float* t_audio_host, const void* x_text, void* x_video, void* x_audio,
+                         const int32_t* keep, const int32_t* nk, void* ws, size_t ws_bytes, void* stream) {
+    int r = validate_dims(dims);
+    if (r) return r;
+    if (dims->n_ctrl != 0) return DIT_EINVAL;
+    return stack_impl(dims, layers_host, n_layers, compressed_host, n_evals, t_video_host, t_audio_host, x_text,
+                      x_video, nullptr, x_audio, keep, nk, ws, ws_bytes, stream);
+}
+
+int32_t dit_stack_sample_ctrl(const dit_dims* dims, const dit_block_weights* layers_host, int32_t n_layers,
+                              const uint8_t* compressed_host, int32_t n_evals, const float* t_video_host,
+                              const float* t_audio_host, const void* x_text, void* x_video, const void* x_ctrl,
+                              void* x_audio, const int32_t* keep, const int32_t* nk, void* ws, size_t ws_bytes,
+                              void* stream) {
+    int r = validate_dims(dims);
+    if (r) return r;
+    if (dims->n_ctrl < 1) return DIT_EINVAL;
+    return stack_impl(dims, layers_host, n_layers, compressed_host, n_evals, t_video_host, t_audio_host, x_text,
+                      x_video, x_ctrl, x_audio, keep, nk, ws, ws_bytes, stream);
 }
 
 int32_t dit_quantize_fp8(const void* src, int32_t src_dtype, int64_t n, uint8_t* dst, float* scale, void* stream) {

@@ -67,14 +67,17 @@ DIT_DEV float wave_max(float v) {
 DIT_DEV void atomic_max_nonneg(float* addr, float x) { atomicMax((unsigned int*)addr, __float_as_uint(x)); }
 
 // ----------------------------------------------------------------- sequence layout
-// The joint sequence is [text | video tokens | audio]. Video tokens are either
-// every position of x_video (vidx == nullptr) or the rows listed in vidx.
+// The joint sequence is [text | video tokens | control | audio]. Video tokens
+// are either every position of x_video (vidx == nullptr) or the rows listed in
+// vidx; control tokens (nc of them, possibly none) are every position of the
+// control frames.
 struct SeqIn {
     const void* xt;
     const void* xv;
+    const void* xc;
     const void* xa;
     const int32_t* vidx;   // video token j -> row of xv (nullptr: j)
-    int nt, nv, na;
+    int nt, nv, nc, na;
 };
 
 // Output rows of the block. With delta != nullptr the video rows are not
@@ -83,6 +86,7 @@ struct SeqIn {
 struct SeqOut {
     void* yt;
     void* yv;
+    void* yc;
     void* ya;
     float* delta;
     const void* ref_v;
@@ -98,7 +102,8 @@ struct Rope {
     const float2* rows;    // per sequence row: (cos, sin) of all head_dim / 2 pairs (MFMA epilogue)
     int rt, rh, rw;
     int H, W;
-    int nt, nv;            // text / video token counts in the sequence
+    int nt, nv, nc;        // text / video / control token counts in the sequence
+    int toff;              // time offset of video and audio tokens (control frames before the target)
 };
 
 template <typename T>
@@ -109,22 +114,26 @@ DIT_DEV const T* seq_row(const SeqIn& s, int m, int D) {
         int r = s.vidx ? s.vidx[m] : m;
         return (const T*)s.xv + (size_t)r * D;
     }
-    return (const T*)s.xa + (size_t)(m - s.nv) * D;
+    m -= s.nv;
+    if (m < s.nc) return (const T*)s.xc + (size_t)m * D;
+    return (const T*)s.xa + (size_t)(m - s.nc) * D;
 }
 
-// coordinates (t, h, w) of sequence row m; text -> (0,0,0), audio j -> (j,0,0)
+// coordinates (t, h, w) of sequence row m: text -> (0,0,0); video ->
+// (t + toff, h, w); control frame k -> (k, h, w); audio j -> (j + toff, 0, 0)
 DIT_DEV int3 rope_coords(const Rope& r, int m) {
     if (m < r.nt) return make_int3(0, 0, 0);
     m -= r.nt;
-    if (m < r.nv) {
-        int p = r.vpos ? r.vpos[m] : m;
-        int hw = r.H * r.W;
-        int t = p / hw;
-        int rem = p - t * hw;
-        int h = rem / r.W;
-        return make_int3(t, h, rem - h * r.W);
+    const int hw = r.H * r.W;
+    if (m < r.nv || m - r.nv < r.nc) {
+        const bool video = m < r.nv;
+        const int p = video ? (r.vpos ? r.vpos[m] : m) : m - r.nv;
+        const int t = p / hw;
+        const int rem = p - t * hw;
+        const int h = rem / r.W;
+        return make_int3(t + (video ? r.toff : 0), h, rem - h * r.W);
     }
-    return make_int3(m - r.nv, 0, 0);
+    return make_int3(m - r.nv - r.nc + r.toff, 0, 0);
 }
 
 // (cos, sin) for head-local feature d (even member of its pair) at coords c

@@ -155,7 +155,7 @@ DIT_DEV void epi_down(const EpiParams& p, int m, int n0, float v[4], float sc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) y[i] += v[i] * sc;
     const SeqOut& o = p.out;
-    const int nt = p.xin.nt, nv = p.xin.nv;
+    const int nt = p.xin.nt, nv = p.xin.nv, nc = p.xin.nc;
     if (m < nt) {
         store4<T>((T*)o.yt + (size_t)m * p.D + n0, y);
     } else if (m < nt + nv) {
@@ -169,8 +169,10 @@ DIT_DEV void epi_down(const EpiParams& p, int m, int n0, float v[4], float sc) {
         } else {
             store4<T>((T*)o.yv + (size_t)j * p.D + n0, y);
         }
+    } else if (m < nt + nv + nc) {
+        store4<T>((T*)o.yc + (size_t)(m - nt - nv) * p.D + n0, y);
     } else {
-        store4<T>((T*)o.ya + (size_t)(m - nt - nv) * p.D + n0, y);
+        store4<T>((T*)o.ya + (size_t)(m - nt - nv - nc) * p.D + n0, y);
     }
 }
 
@@ -259,7 +261,7 @@ DIT_DEV void epi8_down(const EpiParams& p, int m, int n0, const float v[8]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] += v[i];
     const SeqOut& o = p.out;
-    const int nt = p.xin.nt, nv = p.xin.nv;
+    const int nt = p.xin.nt, nv = p.xin.nv, nc = p.xin.nc;
     if (m < nt) {
         store8<T>((T*)o.yt + (size_t)m * p.D + n0, y);
     } else if (m < nt + nv) {
@@ -273,8 +275,10 @@ DIT_DEV void epi8_down(const EpiParams& p, int m, int n0, const float v[8]) {
         } else {
             store8<T>((T*)o.yv + (size_t)j * p.D + n0, y);
         }
+    } else if (m < nt + nv + nc) {
+        store8<T>((T*)o.yc + (size_t)(m - nt - nv) * p.D + n0, y);
     } else {
-        store8<T>((T*)o.ya + (size_t)(m - nt - nv) * p.D + n0, y);
+        store8<T>((T*)o.ya + (size_t)(m - nt - nv - nc) * p.D + n0, y);
     }
 }
 
