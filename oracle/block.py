@@ -104,9 +104,10 @@ def grid_coords(T: int, H: int, W: int) -> np.ndarray:
     return np.stack([t.ravel(), h.ravel(), w.ravel()], axis=1).astype(np.int64)
 
 
-def token_coords(d, compressed: bool, stride: int = None, t_shift: int = 0):
+def token_coords(d, compressed: bool, stride: int = None, t_shift: int = 0, ctrl_idx=None):
     """Per token of the joint sequence: coordinates [S, 3] and kind [S].
-    t_shift moves every time position (video, control, audio) by a constant."""
+    t_shift moves every time position (video, control, audio) by a constant;
+    ctrl_idx selects control tokens by flat position in the control grid."""
     s = d.stride if stride is None else stride
     nc, c = getattr(d, "n_ctrl", 0), getattr(d, "ctrl_offset", 0)
     text = np.zeros((d.n_text, 3), dtype=np.int64)
@@ -114,6 +115,8 @@ def token_coords(d, compressed: bool, stride: int = None, t_shift: int = 0):
     video = video.copy()
     video[:, 0] += c + t_shift
     ctrl = grid_coords(nc, d.H, d.W)
+    if ctrl_idx is not None:
+        ctrl = ctrl[np.asarray(ctrl_idx, dtype=np.int64)]
     ctrl[:, 0] += t_shift
     audio = np.zeros((d.n_audio, 3), dtype=np.int64)
     audio[:, 0] = np.arange(d.n_audio) + c + t_shift
@@ -196,11 +199,14 @@ def block_core(X: np.ndarray, coords: np.ndarray, kinds: np.ndarray, w: BlockWei
 
 
 def block_forward(x_text, x_video, x_audio, w: BlockWeights, d, compress: bool, stride: int = None,
-                  sample: dict = None, x_ctrl=None, t_shift: int = 0):
+                  sample: dict = None, x_ctrl=None, t_shift: int = 0, ctrl_idx=None):
     """The full block on the three inputs (x_video [T, H, W, D]).
 
     Returns (y_text [Nt, D], y_video [T, H, W, D], y_audio [Na, D]), and
-    y_ctrl [Tc, H, W, D] as a fourth element when x_ctrl is given.
+    y_ctrl [Tc, H, W, D] as a fourth element when x_ctrl is given. With
+    ctrl_idx (flat positions in the [Tc, H, W] control grid, e.g. a bounded
+    long-video history) only those control tokens join the sequence, with
+    their own coordinates, and y_ctrl is [len(ctrl_idx), D] in that order.
     With compress=True the joint sequence holds only the kept video tokens;
     text and audio outputs come from the block, and every video position gets
     x + (update of its nearest kept slot).
@@ -219,7 +225,9 @@ def block_forward(x_text, x_video, x_audio, w: BlockWeights, d, compress: bool, 
     xv = np.asarray(x_video, dtype=np.float64).reshape(d.n_video, D)
     xa = np.asarray(x_audio, dtype=np.float64).reshape(d.n_audio, D)
     xc = np.asarray(x_ctrl, dtype=np.float64).reshape(nc * d.H * d.W, D) if nc else np.zeros((0, D))
-    coords, kinds = token_coords(d, compress, s, t_shift)
+    if ctrl_idx is not None:
+        xc = xc[np.asarray(ctrl_idx, dtype=np.int64)]
+    coords, kinds = token_coords(d, compress, s, t_shift, ctrl_idx)
     if compress:
         keep = cmp.keep_index(d.T, d.H, d.W, s)
         nk = cmp.nearest_kept_map(d.T, d.H, d.W, s)
@@ -239,7 +247,9 @@ def block_forward(x_text, x_video, x_audio, w: BlockWeights, d, compress: bool, 
         else:
             yv = yv_seq
         out = (yt, yv.reshape(d.T, d.H, d.W, D), ya)
-        return out + (yc.reshape(nc, d.H, d.W, D),) if nc else out
+        if not nc:
+            return out
+        return out + ((yc if ctrl_idx is not None else yc.reshape(nc, d.H, d.W, D)),)
     if nc:
         raise ValueError("row sampling is not available with control frames")
 

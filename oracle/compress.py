@@ -71,3 +71,32 @@ def kept_coords(T: int, H: int, W: int, s: int = 2) -> np.ndarray:
     tokens keep their original coordinates)."""
     kh, kw = keep_axis(H, s), keep_axis(W, s)
     return np.asarray([(t, h, w) for t in range(T) for h in kh for w in kw], dtype=np.int64).reshape(-1, 3)
+
+
+def history_frames(n_hist: int) -> list:
+    """Bounded long-video history (tokendh.com article, long-video section;
+    PaperDaily review, section 3): of the n_hist latent frames generated so
+    far (0 = the first), the first frame stays at full spatial resolution, the
+    two most recent are sampled at stride 2 and up to eight frames before them
+    at stride 4; frames in the middle beyond that are dropped (the first and
+    the most recent are kept). Returns [(frame, stride)] in frame order."""
+    if n_hist < 0:
+        raise ValueError("n_hist must be >= 0")
+    if n_hist == 0:
+        return []
+    recent = [f for f in (n_hist - 2, n_hist - 1) if f >= 1]
+    middle = list(range(max(1, n_hist - 2 - 8), n_hist - 2))
+    return [(0, 1)] + [(f, 4) for f in middle] + [(f, 2) for f in recent]
+
+
+def history_index(n_hist: int, H: int, W: int) -> np.ndarray:
+    """int32: flat positions f*H*W + h*W + w, in the [n_hist, H, W] grid of
+    the history latents, of the history tokens, frame by frame in raster
+    order. Reading: a frame at stride s keeps rows and columns that are
+    multiples of s (plain stride sampling, without the compression's extra
+    edge row and column: then the whole history holds exactly two full frames
+    of tokens when H and W are multiples of 4, the budget the pages state)."""
+    out = []
+    for f, s in history_frames(n_hist):
+        out += [f * H * W + h * W + w for h in range(0, H, s) for w in range(0, W, s)]
+    return np.asarray(out, dtype=np.int32)

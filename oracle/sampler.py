@@ -36,12 +36,20 @@ def flash_layer_flags(n_full_head: int = 2, n_compressed: int = 26, n_full_tail:
     return np.asarray([0] * n_full_head + [1] * n_compressed + [0] * n_full_tail, dtype=np.uint8)
 
 
-def stack_sample(x_text, x_video, x_audio, layers, flags, t_video, t_audio, d, x_ctrl=None):
+def _scatter_ctrl(rows, ctrl_idx, d):
+    """Packed control-token rows back into a [Tc, H, W, D] grid (other positions zero)."""
+    g = np.zeros((d.n_ctrl * d.H * d.W, d.d_model))
+    g[np.asarray(ctrl_idx, dtype=np.int64)] = rows
+    return g.reshape(d.n_ctrl, d.H, d.W, d.d_model)
+
+
+def stack_sample(x_text, x_video, x_audio, layers, flags, t_video, t_audio, d, x_ctrl=None, ctrl_idx=None):
     """Run len(t_video) - 1 evaluations of the layer stack with Euler updates.
 
     Every compressed layer is applied literally (gather the kept tokens,
     compute, broadcast the nearest-kept update onto the full features).
-    Control frames (x_ctrl) are re-fed unchanged every evaluation, like text.
+    Control frames (x_ctrl, optionally only the tokens at ctrl_idx) are
+    re-fed unchanged every evaluation, like text.
     Returns the final (x_video, x_audio) in fp64."""
     t_video = np.asarray(t_video, dtype=np.float64)
     t_audio = t_video if t_audio is None else np.asarray(t_audio, dtype=np.float64)
@@ -50,11 +58,17 @@ def stack_sample(x_text, x_video, x_audio, layers, flags, t_video, t_audio, d, x
     xa = np.asarray(x_audio, dtype=np.float64)
     for k in range(len(t_video) - 1):
         zt, zv, za, zc = xt, xv, xa, x_ctrl
+        first = True
         for w, c in zip(layers, flags):
             if zc is None:
                 zt, zv, za = block_forward(zt, zv, za, w, d, compress=bool(c))
-            else:
+            elif ctrl_idx is None:
                 zt, zv, za, zc = block_forward(zt, zv, za, w, d, compress=bool(c), x_ctrl=zc)
+            else:
+                # the selected tokens, packed after the first layer
+                zin = zc if first else _scatter_ctrl(zc, ctrl_idx, d)
+                zt, zv, za, zc = block_forward(zt, zv, za, w, d, compress=bool(c), x_ctrl=zin, ctrl_idx=ctrl_idx)
+            first = False
         xv = xv + (t_video[k + 1] - t_video[k]) * zv
         xa = xa + (t_audio[k + 1] - t_audio[k]) * za
     return xv, xa
