@@ -109,7 +109,23 @@ int32_t dit_keep_index(int32_t T, int32_t H, int32_t W, int32_t stride, int32_t*
  * ties to the lower index [TDH-training], [PD-2]. nk: int32 [T * H * W], device. */
 int32_t dit_nearest_kept_map(int32_t T, int32_t H, int32_t W, int32_t stride, int32_t* nk, void* stream);
 
-/* Workspace bytes for dit_block_forward with these dims (compress_on 0 / 1). */
+/* Bounded long-video history [TDH-long] (tokendh.com article, long-video
+ * section), [PD-3] (PaperDaily review, section 3): of the n_hist latent frames
+ * generated so far (frame 0 the first), frame 0 stays at full spatial
+ * resolution, the two most recent frames are sampled at stride 2 and up to
+ * eight frames right before them at stride 4; middle frames beyond that are
+ * dropped. A frame at stride s keeps the rows and columns that are multiples
+ * of s, so the history never holds more than two full frames of tokens when H
+ * and W are multiples of 4. dit_history_count writes the token count (host
+ * only); dit_history_index writes idx[j] = flat position f*H*W + h*W + w of
+ * history token j in the [n_hist][H][W] grid, frame by frame in raster order
+ * (device, int32 [count]); use it as ctrl_idx with the history latents as
+ * x_ctrl (n_ctrl = n_hist, ctrl_offset = n_hist for a chunk that follows). */
+int32_t dit_history_count(int32_t n_hist, int32_t H, int32_t W, int32_t* count);
+int32_t dit_history_index(int32_t n_hist, int32_t H, int32_t W, int32_t* idx, void* stream);
+
+/* Workspace bytes for dit_block_forward with these dims (compress_on 0 / 1);
+ * with control frames, for every control position (enough for any ctrl_idx). */
 int32_t dit_block_workspace_size(const dit_dims* dims, int32_t compress_on, size_t* bytes);
 
 /* One Flash DiT block [TDH-backbone], [TDH-training], [PD-2].
@@ -145,10 +161,16 @@ int32_t dit_block_forward(const dit_dims* dims,
  * audio token j the t position j + ctrl_offset (every time position moves
  * together, which leaves the logits among video and audio unchanged). Control
  * tokens are never compressed; y_ctrl [n_ctrl][H][W][D] receives their rows of
- * y (may alias x_ctrl). Needs n_ctrl >= 1 and ctrl_offset >= 1; everything
- * else as dit_block_forward, whose dims must have n_ctrl == 0. */
+ * y (may alias x_ctrl). With ctrl_idx (device int32 [n_ctrl_tok], flat
+ * positions in the [n_ctrl][H][W] grid, e.g. from dit_history_index) only
+ * those control tokens join the sequence, each with its own coordinates, and
+ * y_ctrl receives n_ctrl_tok rows [n_ctrl_tok][D] in that order (then it must
+ * not alias x_ctrl); ctrl_idx NULL: every position, n_ctrl_tok ignored.
+ * Needs n_ctrl >= 1 and ctrl_offset >= 1; everything else as
+ * dit_block_forward, whose dims must have n_ctrl == 0. */
 int32_t dit_block_forward_ctrl(const dit_dims* dims,
-                               const void* x_text, const void* x_video, const void* x_ctrl, const void* x_audio,
+                               const void* x_text, const void* x_video, const void* x_ctrl,
+                               const int32_t* ctrl_idx, int32_t n_ctrl_tok, const void* x_audio,
                                const dit_block_weights* weights, int32_t compress_on,
                                const int32_t* keep, const int32_t* nk,
                                void* y_text, void* y_video, void* y_ctrl, void* y_audio,
@@ -177,12 +199,14 @@ int32_t dit_stack_sample(const dit_dims* dims, const dit_block_weights* layers_h
                          void* ws, size_t ws_bytes, void* stream);
 
 /* The sampler with control frames (see dit_block_forward_ctrl): every layer
- * runs on [x_text | x_video | x_ctrl | x_audio], and the control frames are
- * re-fed unchanged each evaluation, like text. dims must have n_ctrl >= 1. */
+ * runs on [x_text | x_video | control tokens | x_audio], and the control
+ * tokens (all of x_ctrl, or those at ctrl_idx) are re-fed unchanged each
+ * evaluation, like text. dims must have n_ctrl >= 1. */
 int32_t dit_stack_sample_ctrl(const dit_dims* dims, const dit_block_weights* layers_host, int32_t n_layers,
                               const uint8_t* compressed_host, int32_t n_evals,
                               const float* t_video_host, const float* t_audio_host,
-                              const void* x_text, void* x_video, const void* x_ctrl, void* x_audio,
+                              const void* x_text, void* x_video, const void* x_ctrl,
+                              const int32_t* ctrl_idx, int32_t n_ctrl_tok, void* x_audio,
                               const int32_t* keep, const int32_t* nk,
                               void* ws, size_t ws_bytes, void* stream);
 

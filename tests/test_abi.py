@@ -127,18 +127,33 @@ def test_control_frame_entry_points_reject():
                                ws, 1 << 40, None)
     assert st == _lib.DIT_EINVAL
     d0 = _dims()
-    st = lib.dit_block_forward_ctrl(ctypes.byref(d0), fake, fake, fake, fake, ctypes.byref(wf), 0, None, None, fake,
-                                    fake, fake, fake, ws, 1 << 40, None)
+    st = lib.dit_block_forward_ctrl(ctypes.byref(d0), fake, fake, fake, None, 0, fake, ctypes.byref(wf), 0, None,
+                                    None, fake, fake, fake, fake, ws, 1 << 40, None)
     assert st == _lib.DIT_EINVAL
     # missing control pointers
-    st = lib.dit_block_forward_ctrl(ctypes.byref(dc), fake, fake, None, fake, ctypes.byref(wf), 0, None, None, fake,
-                                    fake, None, fake, ws, 1 << 40, None)
+    st = lib.dit_block_forward_ctrl(ctypes.byref(dc), fake, fake, None, None, 0, fake, ctypes.byref(wf), 0, None,
+                                    None, fake, fake, None, fake, ws, 1 << 40, None)
+    assert st == _lib.DIT_EINVAL
+    # a token list longer than the control grid
+    st = lib.dit_block_forward_ctrl(ctypes.byref(dc), fake, fake, fake, fake, 2 * 34 * 60 + 1, fake,
+                                    ctypes.byref(wf), 0, None, None, fake, fake, fake, fake, ws, 1 << 40, None)
     assert st == _lib.DIT_EINVAL
     assert lib.dit_stack_sample(ctypes.byref(dc), None, 0, None, 1, None, None, fake, fake, fake, None, None, ws,
                                 1 << 40, None) == _lib.DIT_EINVAL
-    assert lib.dit_stack_sample_ctrl(ctypes.byref(d0), None, 0, None, 1, None, None, fake, fake, fake, fake, None,
-                                     None, ws, 1 << 40, None) == _lib.DIT_EINVAL
+    assert lib.dit_stack_sample_ctrl(ctypes.byref(d0), None, 0, None, 1, None, None, fake, fake, fake, None, 0, fake,
+                                     None, None, ws, 1 << 40, None) == _lib.DIT_EINVAL
     a, b = ctypes.c_size_t(), ctypes.c_size_t()
     lib.dit_block_workspace_size(ctypes.byref(d0), 1, ctypes.byref(a))
     lib.dit_block_workspace_size(ctypes.byref(dc), 1, ctypes.byref(b))
     assert b.value > a.value
+
+
+def test_history_count_matches_oracle():
+    lib = V.lib()
+    n = ctypes.c_int32()
+    for nh in (0, 1, 2, 3, 4, 11, 12, 25):
+        for H, W in ((8, 12), (34, 60), (5, 7)):
+            assert lib.dit_history_count(nh, H, W, ctypes.byref(n)) == _lib.DIT_OK
+            assert n.value == len(O.history_index(nh, H, W))
+    assert lib.dit_history_count(-1, 4, 4, ctypes.byref(n)) == _lib.DIT_EINVAL
+    assert lib.dit_history_index(3, 0, 4, None, None) == _lib.DIT_EINVAL

@@ -96,3 +96,62 @@ def test_ctrl_stack_vs_oracle():
     err = rel_err([to_numpy(xv), to_numpy(xa)], list(ref))
     print(f"  max|err|/rms = {err:.3e}")
     assert err <= 6e-2
+
+
+# ---------------------------------------------------------------- bounded long-video history
+@pytest.mark.parametrize("n_hist,H,W", [(0, 4, 4), (1, 9, 15), (3, 9, 15), (12, 9, 15), (25, 34, 60), (40, 5, 7)])
+def test_history_index_bit_exact(n_hist, H, W):
+    got = V.history_index(n_hist, H, W)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), O.history_index(n_hist, H, W))
+
+
+HIST = CTRL_BF16.with_(name="hist_bf16", n_ctrl=12, ctrl_offset=12, seed=15)
+
+
+def run_gpu_hist(d, x, w, compress):
+    dims = V.make_dims(d)
+    xt, xv, xa, xc = (torch_act(x[k], d.dtype) for k in ("x_text", "x_video", "x_audio", "x_ctrl"))
+    gw, _ = gpu_weights(w, d.dtype)
+    keep = V.keep_index(d.T, d.H, d.W, d.stride) if compress else None
+    nk = V.nearest_kept_map(d.T, d.H, d.W, d.stride) if compress else None
+    idx = V.history_index(d.n_ctrl, d.H, d.W)
+    yt, yv, ya, yc = V.block_forward(dims, xt, xv, xa, gw, compress, keep, nk, x_ctrl=xc, ctrl_idx=idx)
+    torch.cuda.synchronize()
+    return [to_numpy(yt), to_numpy(yv), to_numpy(ya), to_numpy(yc)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("compress", [False, True])
+def test_history_block_vs_oracle(dtype, compress):
+    """A chunk of 2 frames after 12 history frames (first full, 8 at stride 4,
+    2 at stride 2), the history tokens read through their position list."""
+    d = HIST.with_(dtype=dtype)
+    print(f"history block {dtype} compress={compress}", flush=True)
+    x, w = inputs(d)
+    got = run_gpu_hist(d, x, w, compress)
+    ref = O.block_forward(x["x_text"], x["x_video"], x["x_audio"], oracle_weights(w, dtype), d, compress,
+                          x_ctrl=x["x_ctrl"], ctrl_idx=O.history_index(d.n_ctrl, d.H, d.W))
+    check(got, list(ref), dtype)
+
+
+def test_history_stack_vs_oracle():
+    d = HIST.with_(name="hist_stack", d_model=256, n_heads=2, d_ffn=512, n_ctrl=5, ctrl_offset=5, seed=16)
+    flags = [0, 1, 0]
+    tv = O.flow_schedule(3, 12.0)
+    print(f"history stack flags={flags}", flush=True)
+    x, _ = inputs(d)
+    layers = [inputs(d, layer=l)[1] for l in range(len(flags))]
+    dims = V.make_dims(d)
+    xt, xv, xa, xc = (torch_act(x[k], d.dtype) for k in ("x_text", "x_video", "x_audio", "x_ctrl"))
+    gl = [gpu_weights(lw, d.dtype)[0] for lw in layers]
+    keep, nk = V.keep_index(d.T, d.H, d.W), V.nearest_kept_map(d.T, d.H, d.W)
+    idx = V.history_index(d.n_ctrl, d.H, d.W)
+    V.stack_sample(dims, gl, flags, tv, None, xt, xv, xa, keep, nk, x_ctrl=xc, ctrl_idx=idx)
+    torch.cuda.synchronize()
+    ref = O.stack_sample(x["x_text"], x["x_video"], x["x_audio"], [oracle_weights(lw, "bf16") for lw in layers], flags,
+                         tv.astype(np.float32), None, d, x_ctrl=x["x_ctrl"],
+                         ctrl_idx=O.history_index(d.n_ctrl, d.H, d.W))
+    err = rel_err([to_numpy(xv), to_numpy(xa)], list(ref))
+    print(f"  max|err|/rms = {err:.3e}")
+    assert err <= 6e-2

@@ -65,6 +65,16 @@ def nearest_kept_map(T: int, H: int, W: int, stride: int = 2, out=None):
     return out
 
 
+def history_index(n_hist: int, H: int, W: int, out=None):
+    """Token positions of the bounded long-video history (int32, device)."""
+    n = ctypes.c_int32()
+    check(lib().dit_history_count(n_hist, H, W, ctypes.byref(n)), "dit_history_count")
+    if out is None:
+        out = torch.empty(n.value, dtype=torch.int32, device="cuda")
+    check(lib().dit_history_index(n_hist, H, W, _ptr(out), _stream()), "dit_history_index")
+    return out
+
+
 def block_workspace_size(dims: Dims, compress: bool) -> int:
     n = ctypes.c_size_t()
     check(lib().dit_block_workspace_size(ctypes.byref(dims), int(compress), ctypes.byref(n)),
@@ -83,14 +93,18 @@ def workspace(nbytes: int):
 
 
 def block_forward(dims: Dims, x_text, x_video, x_audio, weights: dict, compress: bool, keep=None, nk=None,
-                  out=None, ws=None, x_ctrl=None):
+                  out=None, ws=None, x_ctrl=None, ctrl_idx=None):
     """One block; returns (y_text, y_video, y_audio), and y_ctrl as a fourth
-    element when x_ctrl (control frames, dims.n_ctrl > 0) is given. `out` may
-    be the inputs themselves (in place)."""
+    element when x_ctrl (control frames, dims.n_ctrl > 0) is given; with
+    ctrl_idx (int32 positions in the control grid) only those control tokens
+    join and y_ctrl is [len(ctrl_idx), D]. `out` may be the inputs themselves
+    (in place)."""
     if out is None:
         out = (torch.empty_like(x_text), torch.empty_like(x_video), torch.empty_like(x_audio))
         if x_ctrl is not None:
-            out = out + (torch.empty_like(x_ctrl),)
+            yc = (torch.empty_like(x_ctrl) if ctrl_idx is None else
+                  torch.empty((ctrl_idx.numel(), x_ctrl.shape[-1]), dtype=x_ctrl.dtype, device=x_ctrl.device))
+            out = out + (yc,)
     need = block_workspace_size(dims, compress)
     if ws is None:
         ws = workspace(need)
@@ -102,6 +116,7 @@ def block_forward(dims: Dims, x_text, x_video, x_audio, weights: dict, compress:
         check(st, "dit_block_forward")
     else:
         st = lib().dit_block_forward_ctrl(ctypes.byref(dims), _ptr(x_text), _ptr(x_video), _ptr(x_ctrl),
+                                          _ptr(ctrl_idx), 0 if ctrl_idx is None else ctrl_idx.numel(),
                                           _ptr(x_audio), ctypes.byref(w), int(compress), _ptr(keep), _ptr(nk),
                                           _ptr(out[0]), _ptr(out[1]), _ptr(out[3]), _ptr(out[2]), _ptr(ws),
                                           ws.numel(), _stream())
@@ -118,7 +133,7 @@ def stack_workspace_size(dims: Dims, flags) -> int:
 
 
 def stack_sample(dims: Dims, layers: list, flags, t_video, t_audio, x_text, x_video, x_audio, keep=None, nk=None,
-                 ws=None, x_ctrl=None):
+                 ws=None, x_ctrl=None, ctrl_idx=None):
     """Flow-matching sampler; x_video and x_audio are updated in place
     (control frames x_ctrl, when given, are re-fed every evaluation)."""
     n = len(layers)
@@ -137,8 +152,9 @@ def stack_sample(dims: Dims, layers: list, flags, t_video, t_audio, x_text, x_vi
     else:
         st = lib().dit_stack_sample_ctrl(ctypes.byref(dims), arr, n, ctypes.cast(fl, ctypes.c_void_p),
                                          len(t_video) - 1, ctypes.cast(tv, ctypes.c_void_p), tac, _ptr(x_text),
-                                         _ptr(x_video), _ptr(x_ctrl), _ptr(x_audio), _ptr(keep), _ptr(nk), _ptr(ws),
-                                         ws.numel(), _stream())
+                                         _ptr(x_video), _ptr(x_ctrl), _ptr(ctrl_idx),
+                                         0 if ctrl_idx is None else ctrl_idx.numel(), _ptr(x_audio), _ptr(keep),
+                                         _ptr(nk), _ptr(ws), ws.numel(), _stream())
         check(st, "dit_stack_sample_ctrl")
     return x_video, x_audio
 

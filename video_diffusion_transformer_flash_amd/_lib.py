@@ -36,13 +36,16 @@ SIGNATURES = {
     "dit_block_workspace_size": (c_i32, [ctypes.POINTER(Dims), c_i32, ctypes.POINTER(c_size)]),
     "dit_block_forward": (c_i32, [ctypes.POINTER(Dims), c_vp, c_vp, c_vp, ctypes.POINTER(BlockWeights), c_i32,
                                   c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
-    "dit_block_forward_ctrl": (c_i32, [ctypes.POINTER(Dims), c_vp, c_vp, c_vp, c_vp, ctypes.POINTER(BlockWeights),
-                                       c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "dit_block_forward_ctrl": (c_i32, [ctypes.POINTER(Dims), c_vp, c_vp, c_vp, c_vp, c_i32, c_vp,
+                                       ctypes.POINTER(BlockWeights), c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                       c_size, c_vp]),
+    "dit_history_count": (c_i32, [c_i32, c_i32, c_i32, P_i32]),
+    "dit_history_index": (c_i32, [c_i32, c_i32, c_i32, c_vp, c_vp]),
     "dit_stack_workspace_size": (c_i32, [ctypes.POINTER(Dims), c_vp, c_i32, ctypes.POINTER(c_size)]),
     "dit_stack_sample": (c_i32, [ctypes.POINTER(Dims), ctypes.POINTER(BlockWeights), c_i32, c_vp, c_i32, c_vp, c_vp,
                                  c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "dit_stack_sample_ctrl": (c_i32, [ctypes.POINTER(Dims), ctypes.POINTER(BlockWeights), c_i32, c_vp, c_i32, c_vp,
-                                      c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+                                      c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "dit_quantize_fp8": (c_i32, [c_vp, c_i32, c_i64, c_vp, c_vp, c_vp]),
     "dit_gather_kept": (c_i32, [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "dit_broadcast_residual": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),

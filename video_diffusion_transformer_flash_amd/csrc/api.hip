@@ -101,13 +101,13 @@ struct Plan {
     int ntab_t;
 };
 
-Plan make_plan(const dit_dims& d, int nv_seq, bool delta) {
+Plan make_plan(const dit_dims& d, int nv_seq, bool delta, int nc) {
     Plan p{};
     const bool fp8 = d.w_dtype == DIT_FP8_E4M3;
     const size_t es = esize(d.act_dtype);
     const size_t D = d.d_model, I = (size_t)d.n_heads * d.head_dim, F = d.d_ffn;
     p.nv_seq = nv_seq;
-    p.S = d.n_text + nv_seq + d.n_ctrl * d.H * d.W + d.n_audio;
+    p.S = d.n_text + nv_seq + nc + d.n_audio;
     p.Sp = (p.S + 127) / 128 * 128;
     // time positions: video t + off, control k, audio j + off
     p.ntab_t = std::max(std::max(d.T + d.ctrl_offset, d.n_audio + d.ctrl_offset), std::max(d.n_ctrl, 1));
@@ -131,10 +131,9 @@ Plan make_plan(const dit_dims& d, int nv_seq, bool delta) {
     p.u = take((size_t)p.S * F * (fp8 ? 4 : es));   // fp8: fp32 u, quantised from full precision
     p.u8 = fp8 ? take((size_t)p.S * F) : 0;
     p.delta = delta ? take((size_t)nv_seq * D * 4) : 0;
-    // fp32 partial tiles of the O and down projections' K-split tails
-    p.part_bytes = d.act_dtype == DIT_F32 ? 0
-                                          : std::max(gemm_split_bytes(fp8, EPI_RESID, p.S, (int)D, (int)I),
-                                                     gemm_split_bytes(fp8, EPI_DOWN, p.S, (int)D, (int)F));
+    // fp32 partial tiles of the O and down projections' K-split tails (a bound
+    // that grows with S, so a workspace sized for more tokens always suffices)
+    p.part_bytes = d.act_dtype == DIT_F32 ? 0 : gemm_split_bytes_bound(p.S, (int)D);
     p.part = p.part_bytes ? take(p.part_bytes) : 0;
     p.sc = take(16 * sizeof(float));
     p.total = off;
@@ -145,7 +144,8 @@ Plan make_plan(const dit_dims& d, int nv_seq, bool delta) {
 // `in`: the joint sequence; `vpos`: flat positions of its video tokens
 // (nullptr: raster); `out`: output segments (or delta); `refin`: rows the
 // delta is taken against.
-int run_block(const dit_dims& d, const dit_block_weights& w, const SeqIn& in, const int32_t* vpos, const SeqOut& out,
+int run_block(const dit_dims& d, const dit_block_weights& w, const SeqIn& in, const int32_t* vpos, const int32_t* cpos,
+              const SeqOut& out,
               const SeqIn& refin, uint8_t* ws, const Plan& P, hipStream_t st) {
     const bool f32 = d.act_dtype == DIT_F32;
     const bool fp8 = d.w_dtype == DIT_FP8_E4M3;
@@ -161,6 +161,7 @@ int run_block(const dit_dims& d, const dit_block_weights& w, const SeqIn& in, co
     rope.tab_h = tab + (size_t)nt_pos * (d.rope_t / 2);
     rope.tab_w = rope.tab_h + (size_t)d.H * (d.rope_h / 2);
     rope.vpos = vpos;
+    rope.cpos = cpos;
     rope.rt = d.rope_t; rope.rh = d.rope_h; rope.rw = d.rope_w;
     rope.H = d.H; rope.W = d.W;
     rope.nt = in.nt; rope.nv = in.nv; rope.nc = in.nc;
@@ -347,22 +348,39 @@ int32_t dit_nearest_kept_map(int32_t T, int32_t H, int32_t W, int32_t stride, in
     return DIT_OK;
 }
 
+int32_t dit_history_count(int32_t n_hist, int32_t H, int32_t W, int32_t* count) {
+    if (n_hist < 0 || H < 1 || W < 1 || !count || (long long)(n_hist + 1) * H * W > (1LL << 30)) return DIT_EINVAL;
+    const HistPlan hp = history_plan(n_hist, H, W);
+    *count = hp.start[hp.n];
+    return DIT_OK;
+}
+
+int32_t dit_history_index(int32_t n_hist, int32_t H, int32_t W, int32_t* idx, void* stream) {
+    if (n_hist < 0 || H < 1 || W < 1 || (long long)(n_hist + 1) * H * W > (1LL << 30)) return DIT_EINVAL;
+    const HistPlan hp = history_plan(n_hist, H, W);
+    if (hp.start[hp.n] > 0 && !idx) return DIT_EINVAL;
+    HIPCHK(history_index_launch(hp, H, W, idx, (hipStream_t)stream));
+    return DIT_OK;
+}
+
 int32_t dit_block_workspace_size(const dit_dims* dims, int32_t compress_on, size_t* bytes) {
     int r = validate_dims(dims);
     if (r) return r;
     if (!bytes) return DIT_EINVAL;
     const int nv = dims->T * dims->H * dims->W;
     const int nk = dims->T * keep_count(dims->H, dims->stride) * keep_count(dims->W, dims->stride);
-    *bytes = make_plan(*dims, compress_on ? nk : nv, compress_on != 0).total;
+    // every control position (a listed subset needs no more)
+    *bytes = make_plan(*dims, compress_on ? nk : nv, compress_on != 0, dims->n_ctrl * dims->H * dims->W).total;
     return DIT_OK;
 }
 
 namespace {
 
 int block_forward_impl(const dit_dims* dims, const void* x_text, const void* x_video, const void* x_ctrl,
-                       const void* x_audio, const dit_block_weights* weights, int32_t compress_on, const int32_t* keep,
-                       const int32_t* nk, void* y_text, void* y_video, void* y_ctrl, void* y_audio, void* ws,
-                       size_t ws_bytes, void* stream) {
+                       const int32_t* ctrl_idx, int32_t n_ctrl_tok, const void* x_audio,
+                       const dit_block_weights* weights, int32_t compress_on, const int32_t* keep, const int32_t* nk,
+                       void* y_text, void* y_video, void* y_ctrl, void* y_audio, void* ws, size_t ws_bytes,
+                       void* stream) {
     const dit_dims& d = *dims;
     int r;
     if ((r = check_weights(d, weights))) return r;
@@ -370,20 +388,21 @@ int block_forward_impl(const dit_dims* dims, const void* x_text, const void* x_v
     if (d.n_text > 0 && (!x_text || !y_text || !aligned16(x_text) || !aligned16(y_text))) return DIT_EINVAL;
     if (d.n_audio > 0 && (!x_audio || !y_audio || !aligned16(x_audio) || !aligned16(y_audio))) return DIT_EINVAL;
     if (d.n_ctrl > 0 && (!x_ctrl || !y_ctrl || !aligned16(x_ctrl) || !aligned16(y_ctrl))) return DIT_EINVAL;
+    if (ctrl_idx && (n_ctrl_tok < 1 || n_ctrl_tok > d.n_ctrl * d.H * d.W)) return DIT_EINVAL;
     if (compress_on && (!keep || !nk)) return DIT_EINVAL;
     if (!ws || ((uintptr_t)ws & 255)) return DIT_EINVAL;
     const int nv = d.T * d.H * d.W;
-    const int nc = d.n_ctrl * d.H * d.W;
+    const int nc = ctrl_idx ? n_ctrl_tok : d.n_ctrl * d.H * d.W;
     const int nkept = d.T * keep_count(d.H, d.stride) * keep_count(d.W, d.stride);
-    const Plan P = make_plan(d, compress_on ? nkept : nv, compress_on != 0);
+    const Plan P = make_plan(d, compress_on ? nkept : nv, compress_on != 0, nc);
     if (ws_bytes < P.total) return DIT_EWORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     uint8_t* w8 = (uint8_t*)ws;
 
-    SeqIn in{x_text, x_video, x_ctrl, x_audio, compress_on ? keep : nullptr, d.n_text, compress_on ? nkept : nv, nc,
-             d.n_audio};
+    SeqIn in{x_text,   x_video, x_ctrl, x_audio, compress_on ? keep : nullptr, ctrl_idx, d.n_text,
+             compress_on ? nkept : nv, nc, d.n_audio};
     SeqOut out{y_text, y_video, y_ctrl, y_audio, compress_on ? (float*)(w8 + P.delta) : nullptr, nullptr, nullptr};
-    r = run_block(d, *weights, in, compress_on ? keep : nullptr, out, in, w8, P, st);
+    r = run_block(d, *weights, in, compress_on ? keep : nullptr, ctrl_idx, out, in, w8, P, st);
     if (r) return r;
     if (compress_on) {
         TR("broadcast_residual");
@@ -403,19 +422,20 @@ int32_t dit_block_forward(const dit_dims* dims, const void* x_text, const void* 
     int r = validate_dims(dims);
     if (r) return r;
     if (dims->n_ctrl != 0) return DIT_EINVAL;
-    return block_forward_impl(dims, x_text, x_video, nullptr, x_audio, weights, compress_on, keep, nk, y_text, y_video,
-                              nullptr, y_audio, ws, ws_bytes, stream);
+    return block_forward_impl(dims, x_text, x_video, nullptr, nullptr, 0, x_audio, weights, compress_on, keep, nk, y_text,
+                              y_video, nullptr, y_audio, ws, ws_bytes, stream);
 }
 
 int32_t dit_block_forward_ctrl(const dit_dims* dims, const void* x_text, const void* x_video, const void* x_ctrl,
-                               const void* x_audio, const dit_block_weights* weights, int32_t compress_on,
-                               const int32_t* keep, const int32_t* nk, void* y_text, void* y_video, void* y_ctrl,
-                               void* y_audio, void* ws, size_t ws_bytes, void* stream) {
+                               const int32_t* ctrl_idx, int32_t n_ctrl_tok, const void* x_audio,
+                               const dit_block_weights* weights, int32_t compress_on, const int32_t* keep,
+                               const int32_t* nk, void* y_text, void* y_video, void* y_ctrl, void* y_audio, void* ws,
+                               size_t ws_bytes, void* stream) {
     int r = validate_dims(dims);
     if (r) return r;
     if (dims->n_ctrl < 1) return DIT_EINVAL;
-    return block_forward_impl(dims, x_text, x_video, x_ctrl, x_audio, weights, compress_on, keep, nk, y_text, y_video,
-                              y_ctrl, y_audio, ws, ws_bytes, stream);
+    return block_forward_impl(dims, x_text, x_video, x_ctrl, ctrl_idx, n_ctrl_tok, x_audio, weights, compress_on, keep,
+                              nk, y_text, y_video, y_ctrl, y_audio, ws, ws_bytes, stream);
 }
 
 int32_t dit_stack_workspace_size(const dit_dims* dims, const uint8_t* compressed_host, int32_t n_layers,
@@ -426,10 +446,10 @@ int32_t dit_stack_workspace_size(const dit_dims* dims, const uint8_t* compressed
     const dit_dims& d = *dims;
     const size_t es = esize(d.act_dtype);
     const int nv = d.T * d.H * d.W;
-    const int nc = d.n_ctrl * d.H * d.W;
+    const int nc = d.n_ctrl * d.H * d.W;   // every control position (a listed subset needs no more)
     const int nkept = d.T * keep_count(d.H, d.stride) * keep_count(d.W, d.stride);
     const size_t Soff = (size_t)d.n_text + nv + nc + d.n_audio, Son = (size_t)d.n_text + nkept + nc + d.n_audio;
-    const Plan Pf = make_plan(d, nv, false), Pc = make_plan(d, nkept, true);
+    const Plan Pf = make_plan(d, nv, false, nc), Pc = make_plan(d, nkept, true, nc);
     *bytes = align256(Soff * d.d_model * es) + align256(Son * d.d_model * es) + std::max(Pf.total, Pc.total);
     return DIT_OK;
 }
@@ -438,8 +458,9 @@ namespace {
 
 int stack_impl(const dit_dims* dims, const dit_block_weights* layers_host, int32_t n_layers,
                const uint8_t* compressed_host, int32_t n_evals, const float* t_video_host,
-               const float* t_audio_host, const void* x_text, void* x_video, const void* x_ctrl, void* x_audio,
-               const int32_t* keep, const int32_t* nk, void* ws, size_t ws_bytes, void* stream) {
+               const float* t_audio_host, const void* x_text, void* x_video, const void* x_ctrl,
+               const int32_t* ctrl_idx, int32_t n_ctrl_tok, void* x_audio, const int32_t* keep, const int32_t* nk,
+               void* ws, size_t ws_bytes, void* stream) {
     const dit_dims& d = *dims;
     int r;
     if (n_layers < 0 || n_evals < 0 || (n_layers > 0 && (!layers_host || !compressed_host))) return DIT_EINVAL;
@@ -454,6 +475,7 @@ int stack_impl(const dit_dims* dims, const dit_block_weights* layers_host, int32
     if (d.n_text > 0 && (!x_text || !aligned16(x_text))) return DIT_EINVAL;
     if (d.n_audio > 0 && (!x_audio || !aligned16(x_audio))) return DIT_EINVAL;
     if (d.n_ctrl > 0 && (!x_ctrl || !aligned16(x_ctrl))) return DIT_EINVAL;
+    if (ctrl_idx && (n_ctrl_tok < 1 || n_ctrl_tok > d.n_ctrl * d.H * d.W)) return DIT_EINVAL;
     if (!ws || ((uintptr_t)ws & 255)) return DIT_EINVAL;
     size_t need = 0;
     dit_stack_workspace_size(dims, compressed_host, n_layers, &need);
@@ -466,14 +488,14 @@ int stack_impl(const dit_dims* dims, const dit_block_weights* layers_host, int32
     const size_t D = d.d_model;
     const int nt = d.n_text, na = d.n_audio;
     const int nv = d.T * d.H * d.W;
-    const int nc = d.n_ctrl * d.H * d.W;
+    const int nc = ctrl_idx ? n_ctrl_tok : d.n_ctrl * d.H * d.W;
     const int nkept = d.T * keep_count(d.H, d.stride) * keep_count(d.W, d.stride);
     const size_t Soff = (size_t)nt + nv + nc + na, Son = (size_t)nt + nkept + nc + na;
     uint8_t* w8 = (uint8_t*)ws;
     uint8_t* Z = w8;
     uint8_t* Zc = Z + align256(Soff * D * es);
     uint8_t* bws = Zc + align256(Son * D * es);
-    const Plan Pf = make_plan(d, nv, false), Pc = make_plan(d, nkept, true);
+    const Plan Pf = make_plan(d, nv, false, nc), Pc = make_plan(d, nkept, true, nc);
     float* delta = (float*)(bws + Pc.delta);
 
     // full-resolution state [text | video | control | audio] and the packed
@@ -486,16 +508,17 @@ int stack_impl(const dit_dims* dims, const dit_block_weights* layers_host, int32
     void* Zcv = Zc + (size_t)nt * D * es;
     void* Zck = Zc + ((size_t)nt + nkept) * D * es;
     void* Zca = Zc + ((size_t)nt + nkept + nc) * D * es;
-    const SeqIn state{Zt, Zv, Zk, Za, nullptr, nt, nv, nc, na};
+    const SeqIn state{Zt, Zv, Zk, Za, nullptr, nullptr, nt, nv, nc, na};
 
     for (int ev = 0; ev < n_evals; ++ev) {
         // current full-resolution state: the inputs for the first layer, Z after
-        SeqIn cur{x_text, x_video, x_ctrl, x_audio, nullptr, nt, nv, nc, na};
+        // (listed control tokens are read through ctrl_idx by the first layer, packed after it)
+        SeqIn cur{x_text, x_video, x_ctrl, x_audio, nullptr, ctrl_idx, nt, nv, nc, na};
         int l = 0;
         while (l < n_layers) {
             if (!compressed_host[l]) {
                 SeqOut out{Zt, Zv, Zk, Za, nullptr, nullptr, nullptr};
-                if ((r = run_block(d, layers_host[l], cur, nullptr, out, cur, bws, Pf, st))) return r;
+                if ((r = run_block(d, layers_host[l], cur, nullptr, ctrl_idx, out, cur, bws, Pf, st))) return r;
                 cur = state;
                 ++l;
                 continue;
@@ -503,13 +526,13 @@ int stack_impl(const dit_dims* dims, const dit_block_weights* layers_host, int32
             int e = l;
             while (e < n_layers && compressed_host[e]) ++e;
             // span [l, e): gather on read at its start, broadcast the summed update at its end
-            const SeqIn start{cur.xt, cur.xv, cur.xc, cur.xa, keep, nt, nkept, nc, na};
-            const SeqIn packed{Zct, Zcv, Zck, Zca, nullptr, nt, nkept, nc, na};
+            const SeqIn start{cur.xt, cur.xv, cur.xc, cur.xa, keep, cur.cidx, nt, nkept, nc, na};
+            const SeqIn packed{Zct, Zcv, Zck, Zca, nullptr, nullptr, nt, nkept, nc, na};
             for (int i = l; i < e; ++i) {
                 const SeqIn& in = (i == l) ? start : packed;
                 SeqOut out = (i + 1 < e) ? SeqOut{Zct, Zcv, Zck, Zca, nullptr, nullptr, nullptr}
                                          : SeqOut{Zt, nullptr, Zk, Za, delta, nullptr, nullptr};
-                if ((r = run_block(d, layers_host[i], in, keep, out, start, bws, Pc, st))) return r;
+                if ((r = run_block(d, layers_host[i], in, keep, ctrl_idx, out, start, bws, Pc, st))) return r;
             }
             TR("broadcast_residual");
             HIPCHK(broadcast_residual_launch(bf, cur.xv, delta, nk, Zv, nv, (int)D, st));
@@ -540,19 +563,19 @@ int32_t dit_stack_sample(const dit_dims* dims, const dit_block_weights* layers_h
     if (r) return r;
     if (dims->n_ctrl != 0) return DIT_EINVAL;
     return stack_impl(dims, layers_host, n_layers, compressed_host, n_evals, t_video_host, t_audio_host, x_text,
-                      x_video, nullptr, x_audio, keep, nk, ws, ws_bytes, stream);
+                      x_video, nullptr, nullptr, 0, x_audio, keep, nk, ws, ws_bytes, stream);
 }
 
 int32_t dit_stack_sample_ctrl(const dit_dims* dims, const dit_block_weights* layers_host, int32_t n_layers,
                               const uint8_t* compressed_host, int32_t n_evals, const float* t_video_host,
                               const float* t_audio_host, const void* x_text, void* x_video, const void* x_ctrl,
-                              void* x_audio, const int32_t* keep, const int32_t* nk, void* ws, size_t ws_bytes,
-                              void* stream) {
+                              const int32_t* ctrl_idx, int32_t n_ctrl_tok, void* x_audio, const int32_t* keep,
+                              const int32_t* nk, void* ws, size_t ws_bytes, void* stream) {
     int r = validate_dims(dims);
     if (r) return r;
     if (dims->n_ctrl < 1) return DIT_EINVAL;
     return stack_impl(dims, layers_host, n_layers, compressed_host, n_evals, t_video_host, t_audio_host, x_text,
-                      x_video, x_ctrl, x_audio, keep, nk, ws, ws_bytes, stream);
+                      x_video, x_ctrl, ctrl_idx, n_ctrl_tok, x_audio, keep, nk, ws, ws_bytes, stream);
 }
 
 int32_t dit_quantize_fp8(const void* src, int32_t src_dtype, int64_t n, uint8_t* dst, float* scale, void* stream) {

@@ -69,14 +69,15 @@ DIT_DEV void atomic_max_nonneg(float* addr, float x) { atomicMax((unsigned int*)
 // ----------------------------------------------------------------- sequence layout
 // The joint sequence is [text | video tokens | control | audio]. Video tokens
 // are either every position of x_video (vidx == nullptr) or the rows listed in
-// vidx; control tokens (nc of them, possibly none) are every position of the
-// control frames.
+// vidx; control tokens (nc of them, possibly none) likewise every position of
+// the control frames or the rows listed in cidx.
 struct SeqIn {
     const void* xt;
     const void* xv;
     const void* xc;
     const void* xa;
     const int32_t* vidx;   // video token j -> row of xv (nullptr: j)
+    const int32_t* cidx;   // control token j -> row of xc (nullptr: j)
     int nt, nv, nc, na;
 };
 
@@ -99,6 +100,7 @@ struct Rope {
     const float2* tab_h;   // [H][rh/2]
     const float2* tab_w;   // [W][rw/2]
     const int32_t* vpos;   // video token j -> flat position (nullptr: j)
+    const int32_t* cpos;   // control token j -> flat position in the control grid (nullptr: j)
     const float2* rows;    // per sequence row: (cos, sin) of all head_dim / 2 pairs (MFMA epilogue)
     int rt, rh, rw;
     int H, W;
@@ -115,7 +117,7 @@ DIT_DEV const T* seq_row(const SeqIn& s, int m, int D) {
         return (const T*)s.xv + (size_t)r * D;
     }
     m -= s.nv;
-    if (m < s.nc) return (const T*)s.xc + (size_t)m * D;
+    if (m < s.nc) return (const T*)s.xc + (size_t)(s.cidx ? s.cidx[m] : m) * D;
     return (const T*)s.xa + (size_t)(m - s.nc) * D;
 }
 
@@ -127,7 +129,7 @@ DIT_DEV int3 rope_coords(const Rope& r, int m) {
     const int hw = r.H * r.W;
     if (m < r.nv || m - r.nv < r.nc) {
         const bool video = m < r.nv;
-        const int p = video ? (r.vpos ? r.vpos[m] : m) : m - r.nv;
+        const int p = video ? (r.vpos ? r.vpos[m] : m) : (r.cpos ? r.cpos[m - r.nv] : m - r.nv);
         const int t = p / hw;
         const int rem = p - t * hw;
         const int h = rem / r.W;

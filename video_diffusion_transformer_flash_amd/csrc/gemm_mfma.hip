@@ -659,8 +659,13 @@ hipError_t dispatch(const void* A, const void* W0, const void* W1, int M, int N,
 }  // namespace detail
 using namespace detail;
 
-size_t gemm_split_bytes(bool fp8, int mode, int M, int N, int K) {
-    return split_plan(fp8, mode, M, N, K, device_cus()).bytes;
+// A split never has more than min(cus, 8 x tiles) slice units (at most 8
+// slices of at most cus / tail units each), and no split happens below 32 tiles.
+size_t gemm_split_bytes_bound(int M, int N) {
+    if (M <= 0 || N % SPLIT_BF) return 0;
+    const long tiles = (long)((M + SPLIT_BT - 1) / SPLIT_BT) * (N / SPLIT_BF);
+    if (tiles < 32) return 0;
+    return (size_t)std::min<long>(device_cus(), 8 * tiles) * SPLIT_BT * SPLIT_BF * sizeof(float);
 }
 
 // N: output features (for SWIGLU: 2 * F, gate and up interleaved per tile)

@@ -30,9 +30,19 @@ hipError_t euler_launch(bool bf16, void* x, const void* v, size_t n, float dt, h
 
 hipError_t gemm_mfma(bool fp8, int mode, const void* A, const void* W0, const void* W1, int M, int N, int K,
                      const EpiParams& ep, hipStream_t st);
-// bytes of fp32 partial tiles gemm_mfma uses for a K-split tail (0: none);
-// the current device's compute-unit count decides it
-size_t gemm_split_bytes(bool fp8, int mode, int M, int N, int K);
+// upper bound of the fp32 partial-tile bytes gemm_mfma uses for a K-split
+// tail of the RESID / DOWN modes (0: it never splits); it does not decrease
+// with M, and the current device's compute-unit count enters it
+size_t gemm_split_bytes_bound(int M, int N);
+
+// Bounded long-video history: the kept frames and their strides (at most 11)
+struct HistPlan {
+    int n;                 // frames kept
+    int frame[11], stride[11], hk[11], wk[11];
+    int start[12];         // first token of each kept frame; start[n] = token count
+};
+HistPlan history_plan(int n_hist, int H, int W);
+hipError_t history_index_launch(const HistPlan& hp, int H, int W, int32_t* idx, hipStream_t st);
 hipError_t gemm_f32(int mode, const void* A, const void* W0, const void* W1, int M, int N, int K, const EpiParams& ep,
                     hipStream_t st);
 

@@ -44,6 +44,20 @@ __global__ void nearest_map_kernel(int T, int H, int W, int s, int Hk, int Wk, i
     nk[p] = t * Hk * Wk + rh * Wk + rw;
 }
 
+// Bounded long-video history (tokendh.com article, long-video section;
+// PaperDaily review, section 3): token j of the history list -> flat position
+// in the [n_hist, H, W] grid of the history latents; the kept frames, their
+// strides and token ranges come from history_plan.
+__global__ void history_index_kernel(HistPlan hp, int H, int W, int32_t* idx) {
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= hp.start[hp.n]) return;
+    int e = 0;
+    while (e + 1 < hp.n && j >= hp.start[e + 1]) ++e;
+    const int r = j - hp.start[e];
+    const int a = r / hp.wk[e], b = r - (r / hp.wk[e]) * hp.wk[e];
+    idx[j] = hp.frame[e] * H * W + a * hp.stride[e] * W + b * hp.stride[e];
+}
+
 // ----------------------------------------------------------------- rotary tables
 // (cos, sin) of pos * base^(-2i/width) in fp64, stored fp32; three bands back to back.
 __global__ void rope_table_kernel(float2* tab, int n_t, int rt, int n_h, int rh, int n_w, int rw, double base) {
@@ -310,6 +324,34 @@ inline unsigned nblk(size_t n, unsigned b = 256) { return (unsigned)((n + b - 1)
 
 }  // namespace detail
 using namespace detail;
+
+// The first frame at stride 1, the two most recent at stride 2, up to eight
+// frames right before those at stride 4; older middle frames are dropped.
+// A frame at stride s keeps rows and columns that are multiples of s.
+HistPlan history_plan(int n_hist, int H, int W) {
+    HistPlan hp{};
+    auto add = [&](int f, int s) {
+        hp.frame[hp.n] = f;
+        hp.stride[hp.n] = s;
+        hp.hk[hp.n] = (H + s - 1) / s;
+        hp.wk[hp.n] = (W + s - 1) / s;
+        hp.start[hp.n + 1] = hp.start[hp.n] + hp.hk[hp.n] * hp.wk[hp.n];
+        ++hp.n;
+    };
+    if (n_hist <= 0) return hp;
+    add(0, 1);
+    const int recent0 = std::max(1, n_hist - 2);          // first of the (up to) two recent frames
+    for (int f = std::max(1, recent0 - 8); f < recent0; ++f) add(f, 4);
+    for (int f = recent0; f < n_hist; ++f) add(f, 2);
+    return hp;
+}
+
+hipError_t history_index_launch(const HistPlan& hp, int H, int W, int32_t* idx, hipStream_t st) {
+    const int n = hp.start[hp.n];
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(history_index_kernel, dim3(nblk(n)), dim3(256), 0, st, hp, H, W, idx);
+    return hipGetLastError();
+}
 
 hipError_t keep_index_launch(int T, int H, int W, int s, int Hk, int Wk, int32_t* keep, hipStream_t st) {
     const int n = T * Hk * Wk;
