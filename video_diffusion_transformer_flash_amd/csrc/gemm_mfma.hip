@@ -181,31 +181,29 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
         asm volatile("" : "+s"(a));
         return (LDSPTR)(uintptr_t)a;
     };
-    auto issueT = [&](int kt, auto bufc) {
+    auto issueT_at = [&](int kt, LDSPTR lt) {
         const int koff = kt * RB;
-        LDSPTR lt = untracked(stT(bufc) + wave * 1024);
 #pragma unroll
         for (int i = 0; i < BT / RPI; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsT, lt + i * RPI * RB, 16, voT[i], koff, 0, 0);
     };
-    auto issueF = [&](int kt, auto bufc) {
+    auto issueF_one = [&](int kt, LDSPTR lf, auto ic) {
+        constexpr int i = decltype(ic)::value;
         const int koff = kt * RB;
-        LDSPTR lf = untracked(stF(bufc) + wave * 1024);
-#pragma unroll
-        for (int i = 0; i < BF / RPI; ++i) {
-            const int rowr = RPI * i + RPW * wave;         // first of this wave's rows (uniform)
-            if constexpr (MODE == EPI_SWIGLU) {
-                // 32-row blocks of the tile alternate gate / up rows of the same
-                // ffn features: block b holds gate (b even) or up rows b/2*32 ..
-                const int blk = rowr / 32;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds((blk & 1) ? rsF1 : rsF0, lf + i * RPI * RB, 16, voF,
-                                                         ((blk >> 1) * 32 + rowr % 32) * rowbytes + koff, 0, 0);
-            } else {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsF0, lf + i * RPI * RB, 16, voF, rowr * rowbytes + koff, 0,
-                                                         0);
-            }
+        const int rowr = RPI * i + RPW * wave;         // first of this wave's rows (uniform)
+        if constexpr (MODE == EPI_SWIGLU) {
+            // 32-row blocks of the tile alternate gate / up rows of the same
+            // ffn features: block b holds gate (b even) or up rows b/2*32 ..
+            const int blk = rowr / 32;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds((blk & 1) ? rsF1 : rsF0, lf + i * RPI * RB, 16, voF,
+                                                     ((blk >> 1) * 32 + rowr % 32) * rowbytes + koff, 0, 0);
+        } else {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsF0, lf + i * RPI * RB, 16, voF, rowr * rowbytes + koff, 0, 0);
         }
     };
+    auto issueF_at = [&](int kt, LDSPTR lf) { static_for<BF / RPI>([&](auto i) { issueF_one(kt, lf, i); }); };
+    auto issueT = [&](int kt, auto bufc) { issueT_at(kt, untracked(stT(bufc) + wave * 1024)); };
+    auto issueF = [&](int kt, auto bufc) { issueF_at(kt, untracked(stF(bufc) + wave * 1024)); };
 
     // Register prefetch (PF = 2): the same fetches into registers, register
     // set j % 2 holding step j; they are written to the free LDS stage at the
@@ -305,12 +303,46 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
             }
     };
 
+    // One fragment read (index: weight blocks, then token blocks, per 16-byte
+    // read r) and one MFMA, for the explicitly ordered substeps of SCHED 3.
+    auto read_one = [&](auto setc, auto sc, auto tbc, auto fbc, auto ic) {
+        constexpr int SET = decltype(setc)::value, S = decltype(sc)::value, I = decltype(ic)::value;
+        constexpr int r = I / (NBF + NBT), j = I % (NBF + NBT);
+        if constexpr (j < NBF) fF[SET][j][r] = *(const uint4*)(stF(fbc) + rowF0 + aC[S][r] + j * 32 * RB);
+        else fT[SET][j - NBF][r] = *(const uint4*)(stT(tbc) + rowT0 + aC[S][r] + (j - NBF) * 32 * RB);
+    };
+    auto mfma_one = [&](auto setc, auto ic) {
+        constexpr int SET = decltype(setc)::value, a = decltype(ic)::value / NBF, b = decltype(ic)::value % NBF;
+        if constexpr (!FP8) {
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_v, fF[SET][b][0]),
+                                                                 __builtin_bit_cast(bf16x8_v, fT[SET][a][0]), acc[a][b],
+                                                                 0, 0, 0);
+        } else {
+            const uint4 x0 = fF[SET][b][0], x1 = fF[SET][b][1], y0 = fT[SET][a][0], y1 = fT[SET][a][1];
+            const i32x8 fa = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+            const i32x8 fb = {(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w, (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
+            acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, acc[a][b], 0, 0, 0, 0, 0, 0);
+        }
+    };
+
     // Instruction order inside a substep (SCHED 1: the next substep's
     // fragment reads first, then the MFMAs; SCHED 2: reads interleaved one
-    // per MFMA; 0: left to the compiler).
+    // per MFMA; SCHED 3: as 2, and the memory -> LDS fills of the step are
+    // spread over its first substeps, one per MFMA, instead of being issued
+    // in a burst at its start; 0: left to the compiler). With one wave per
+    // SIMD nothing else issues MFMAs while a wave issues its fills.
     constexpr int NRD = NR * (NBF + NBT), NMF = NBT * NBF;
-    auto order_substep = [&]() {
-        if constexpr (SCHED == 1) {
+    auto order_substep = [&](auto nfc) {
+        constexpr int NFI = decltype(nfc)::value;   // fills issued in this substep
+        if constexpr (SCHED == 3) {
+            static_for<NMF>([&](auto i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                if constexpr (i < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+                if constexpr (i < NFI) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // VMEM (fill)
+            });
+            if constexpr (NRD > NMF) __builtin_amdgcn_sched_group_barrier(0x100, NRD - NMF, 0);
+            if constexpr (NFI > NMF) __builtin_amdgcn_sched_group_barrier(0x010, NFI - NMF, 0);
+        } else if constexpr (SCHED == 1) {
             __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);   // DS reads
             __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);   // MFMA
         } else if constexpr (SCHED == 2) {
@@ -330,6 +362,27 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
     // step; with NS = 2, NSF = 3 the weight loads of step kt + 2 may.
     static_assert(PF == 0 || (PF == 2 && NS == 2 && NSF == 2), "register prefetch runs on two stages");
     static_assert(NSF == NS || (NS == 2 && NSF == 3 && PF == 0), "uneven stages: two token, three weight");
+    // SCHED 3 spreads the fills of the uneven direct-load pipeline over the
+    // substeps before the barrier; SCHED 4 issues them in the substep after
+    // it, one step earlier (step kt fills token step kt + 2 and weight step
+    // kt + 3 into the stages it has just finished reading), which gives every
+    // fill one more substep to land before its wait.
+    constexpr bool SPREAD = SCHED >= 3, LATE = SCHED == 4;
+    static_assert(!SPREAD || (PF == 0 && NS == 2 && NSF == 3 && SUB >= 2), "spread fills: uneven stages");
+    // explicit substeps: after MFMA i come reads [i RPG, (i + 1) RPG) and fills [i FPG, (i + 1) FPG)
+    constexpr int RPG = (NRD + NMF - 1) / NMF, FPG = (NPT + NPF + NMF - 1) / NMF;
+    auto reads_after = [&](auto setc, auto sc, auto tbc, auto fbc, auto ic) {
+        static_for<RPG>([&](auto k) {
+            constexpr int j = decltype(ic)::value * RPG + decltype(k)::value;
+            if constexpr (j < NRD) read_one(setc, sc, tbc, fbc, std::integral_constant<int, j>{});
+        });
+    };
+    // fill f of a step's set: token fills 0..NPT-1, then weight fills
+    auto fill_one = [&](auto fc, LDSPTR lt, LDSPTR lf, int ktT, int ktF) {
+        constexpr int f = decltype(fc)::value;
+        if constexpr (f < NPT) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsT, lt + f * RPI * RB, 16, voT[f], ktT * RB, 0, 0);
+        else if constexpr (f < NPT + NPF) issueF_one(ktF, lf, std::integral_constant<int, f - NPT>{});
+    };
     constexpr int LOOP = (NS == NSF) ? NS : 6;    // steps per loop iteration (stage indices repeat)
 
     // One K step on token stage TB and weight stage FB: the fragments of
@@ -343,17 +396,47 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
         if constexpr (PF == 0 && NS == NSF) {
             if (kt + NS - 1 < nk) issueT(kt + NS - 1, std::integral_constant<int, (TB + NS - 1) % NS>{});
             if (kt + NSF - 1 < nk) issueF(kt + NSF - 1, std::integral_constant<int, (FB + NSF - 1) % NSF>{});
-        } else if constexpr (PF == 0) {
+        } else if constexpr (PF == 0 && !SPREAD) {
             // uneven stages, branch-free: past the last step the fills repeat
             // step nk - 1 into stages that are not read again
             issueT(min(kt + 1, nk - 1), std::integral_constant<int, (TB + 1) % 2>{});
             issueF(min(kt + 2, nk - 1), std::integral_constant<int, (FB + 2) % 3>{});
         }
+        // (SPREAD: the fill bases are taken here, outside the substeps, so
+        // that their register moves do not split the substeps' scheduling)
+        LDSPTR ltS = nullptr, lfS = nullptr;
+        if constexpr (SPREAD && !LATE) {
+            ltS = untracked(stT(std::integral_constant<int, (TB + 1) % 2>{}) + wave * 1024);
+            lfS = untracked(stF(std::integral_constant<int, (FB + 2) % 3>{}) + wave * 1024);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         static_for<SUB - 1>([&](auto s) {
-            load_frags(std::integral_constant<int, (P + s + 1) & 1>{}, std::integral_constant<int, s + 1>{}, tbc,
-                       fbc);
-            mfmas(std::integral_constant<int, (P + s) & 1>{});
-            order_substep();
+            if constexpr (SPREAD) {
+                // in this order: MFMA i, fragment read i of the next substep,
+                // fill i (token fills in substep 0, weight fills after them,
+                // in substep 1 or, with two substeps, also in substep 0)
+                constexpr int S = decltype(s)::value;
+                // fills [F0, F1) of the step go in this substep
+                constexpr int F0 = LATE || S > 1 || (S == 1 && SUB == 2) ? 0 : (S == 0 ? 0 : NPT);
+                constexpr int F1 = LATE || S > 1 ? 0 : (SUB == 2 ? NPT + NPF : (S == 0 ? NPT : NPT + NPF));
+                constexpr int FG = (F1 - F0 + NMF - 1) / NMF;
+                const int ktT = min(kt + 1, nk - 1), ktF = min(kt + 2, nk - 1);
+                static_for<NMF>([&](auto i) {
+                    mfma_one(std::integral_constant<int, (P + S) & 1>{}, i);
+                    reads_after(std::integral_constant<int, (P + S + 1) & 1>{}, std::integral_constant<int, S + 1>{},
+                                tbc, fbc, i);
+                    static_for<FG>([&](auto k) {
+                        constexpr int f = F0 + decltype(i)::value * FG + decltype(k)::value;
+                        if constexpr (f < F1) fill_one(std::integral_constant<int, f>{}, ltS, lfS, ktT, ktF);
+                    });
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            } else {
+                load_frags(std::integral_constant<int, (P + s + 1) & 1>{}, std::integral_constant<int, s + 1>{},
+                           tbc, fbc);
+                mfmas(std::integral_constant<int, (P + s) & 1>{});
+                order_substep(std::integral_constant<int, 0>{});
+            }
             __builtin_amdgcn_sched_barrier(0);   // keep later fragment loads out of this substep
         });
         if constexpr (PF == 0) {
@@ -375,11 +458,32 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
             }
         }
         lds_barrier();                   // nobody reads stages TB / FB any more
-        if (NS != NSF || kt + 1 < nk)    // (uneven stages: after the last step these reads are unused)
-            load_frags(std::integral_constant<int, (P + SUB) & 1>{}, std::integral_constant<int, 0>{},
-                       std::integral_constant<int, (TB + 1) % NS>{}, std::integral_constant<int, (FB + 1) % NSF>{});
-        mfmas(std::integral_constant<int, (P + SUB - 1) & 1>{});
-        order_substep();
+        if constexpr (LATE) {
+            // last substep: MFMA i, read i of the next step's first substep,
+            // fill i: token step kt + 2 into stage TB, then weight step kt + 3
+            // into stage FB (past the last step: repeats of step nk - 1 into
+            // stages that are not read again)
+            const LDSPTR ltL = untracked(stT(tbc) + wave * 1024), lfL = untracked(stF(fbc) + wave * 1024);
+            __builtin_amdgcn_sched_barrier(0);
+            const int ktT = min(kt + 2, nk - 1), ktF = min(kt + 3, nk - 1);
+            static_for<NMF>([&](auto i) {
+                mfma_one(std::integral_constant<int, (P + SUB - 1) & 1>{}, i);
+                reads_after(std::integral_constant<int, (P + SUB) & 1>{}, std::integral_constant<int, 0>{},
+                            std::integral_constant<int, (TB + 1) % NS>{}, std::integral_constant<int, (FB + 1) % NSF>{},
+                            i);
+                static_for<FPG>([&](auto k) {
+                    fill_one(std::integral_constant<int, decltype(i)::value * FPG + decltype(k)::value>{}, ltL, lfL,
+                             ktT, ktF);
+                });
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        } else {
+            if (NS != NSF || kt + 1 < nk)    // (uneven stages: after the last step these reads are unused)
+                load_frags(std::integral_constant<int, (P + SUB) & 1>{}, std::integral_constant<int, 0>{},
+                           std::integral_constant<int, (TB + 1) % NS>{}, std::integral_constant<int, (FB + 1) % NSF>{});
+            mfmas(std::integral_constant<int, (P + SUB - 1) & 1>{});
+            order_substep(std::integral_constant<int, 0>{});
+        }
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -394,6 +498,15 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
             });
             if (NS - 1 <= nk) vmwait(std::integral_constant<int, (NPT + NPF) * (NS - 2)>{});
             else vmwait(I0{});
+        } else if constexpr (LATE) {
+            // steps 0 and 1 of both operands and weight step 2; at the first
+            // step's wait only weight step 2 may still be in flight
+            issueT(0, I0{});
+            issueF(0, I0{});
+            issueF(min(1, nk - 1), std::integral_constant<int, 1>{});
+            issueT(min(1, nk - 1), std::integral_constant<int, 1>{});
+            issueF(min(2, nk - 1), std::integral_constant<int, 2>{});
+            vmwait(std::integral_constant<int, NPF + NPT + NPF>{});
         } else {
             issueT(0, I0{});
             issueF(0, I0{});
@@ -429,15 +542,17 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
     }
 
     // ---------------------------------------------------------------- epilogue
-    // Each wave stages 32 tokens x its 64 outputs (fp32, scaled) per round in
-    // a private LDS slice, rows padded to 272 bytes so that both the writes
+    // Each wave stages 32 tokens x 64 of its outputs (fp32, scaled) per round
+    // in a private LDS slice (a wave with 128 outputs takes two rounds per 32
+    // tokens, one per half), rows padded to 272 bytes so that both the writes
     // from the accumulator layout and the row reads are free of bank
     // conflicts, then works in row layout: a lane takes eight consecutive
     // outputs of one token (for v^T: one output column and eight consecutive
     // tokens), so every global load and store is 16-32 contiguous bytes per
     // lane and 128-256 per token row. The pipeline's LDS is free here: every
     // wave has passed the last step's barrier, after which nobody reads it.
-    static_assert(WF == 64, "a wave's rows hold 64 outputs");
+    static_assert(WF % 64 == 0, "a wave's rows hold whole halves of 64 outputs");
+    constexpr int NH = WF / 64;
     constexpr int RS = 64 * 4 + 16;
     // wave slices packed into the stage arrays in order sT0.., sF0..
     constexpr int SL = 32 * RS, capT = LDS_T / SL, capF = LDS_F / SL;
@@ -469,21 +584,23 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
 #pragma unroll
         for (int b = 0; b < NBF; ++b) scb[b] = sc;
     }
-    const int fw = f0 + wf * WF;          // first output (for SwiGLU: interleaved gate/up row) of the wave
+    const int fwave = f0 + wf * WF;       // first output (for SwiGLU: interleaved gate/up row) of the wave
     float mx = 0.f;
     auto row8 = [&](int r, int c0, float v[8]) {
         const float4 x = *(const float4*)(wl + r * RS + c0 * 4), y = *(const float4*)(wl + r * RS + c0 * 4 + 16);
         v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w; v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
     };
-    static_for<NBT>([&](auto a) {
+    static_for<NBT * NH>([&](auto ah) {
+        constexpr int a = decltype(ah)::value / NH, hb = 2 * (decltype(ah)::value % NH);   // token block, first feature block of the half
         // accumulator layout -> LDS rows: lane (token lrow) holds outputs b 32 + 8 g + 4 h .. + 3
-        static_for<NBF>([&](auto b) {
+        static_for<2>([&](auto b) {
             static_for<4>([&](auto g) {
                 *(float4*)(wl + lrow * RS + (b * 32 + 8 * g + 4 * lhalf) * 4) =
-                    make_float4(acc[a][b][4 * g] * scb[b], acc[a][b][4 * g + 1] * scb[b],
-                                acc[a][b][4 * g + 2] * scb[b], acc[a][b][4 * g + 3] * scb[b]);
+                    make_float4(acc[a][hb + b][4 * g] * scb[hb + b], acc[a][hb + b][4 * g + 1] * scb[hb + b],
+                                acc[a][hb + b][4 * g + 2] * scb[hb + b], acc[a][hb + b][4 * g + 3] * scb[hb + b]);
             });
         });
+        const int fw = fwave + 32 * hb;         // first output of the half
         const int mb = t0 + wt * WT + a * 32;   // first token of the round
         if constexpr (MODE == EPI_QKV) {
             const int which = fw / ep.I;
@@ -644,15 +761,19 @@ hipError_t launch_t(const void* A, const void* W0, const void* W1, int M, int N,
 template <bool FP8, int MODE>
 hipError_t dispatch(const void* A, const void* W0, const void* W1, int M, int N, int K, const EpiParams& ep,
                     hipStream_t st) {
+    // 256 x 256 tiles: fills spread over the substeps; for the long-K down
+    // projection issued one step early (measured on the 540p block: QKV,
+    // gate/up and O fastest with the first, down with the second)
+    constexpr int SCH = MODE == EPI_DOWN ? 4 : 3;
     if constexpr (MODE == EPI_RESID || MODE == EPI_DOWN) {
         // 256 x 256 tiles with a K-split tail when the partial buffer holds it
         const SplitPlan sp = split_plan(FP8, MODE, M, N, K, device_cus());
         if (sp.splits > 1 && ep.part && sp.bytes <= ep.part_bytes)
-            return launch_t<256, 256, 2, 4, 2, 3, 128, 0, 2, 0, FP8, MODE>(A, W0, W1, M, N, K, ep, st, sp);
+            return launch_t<256, 256, 2, 4, 2, 3, 128, 0, 2, SCH, FP8, MODE>(A, W0, W1, M, N, K, ep, st, sp);
     }
     // big tiles when there are enough of them to fill 256 CUs several times
     const long t256 = (long)((M + 255) / 256) * (N / 256);
-    if (N % 256 == 0 && t256 >= 512) return launch_t<256, 256, 2, 4, 2, 3, 128, 0, 2, 0, FP8, MODE>(A, W0, W1, M, N, K, ep, st);
+    if (N % 256 == 0 && t256 >= 512) return launch_t<256, 256, 2, 4, 2, 3, 128, 0, 2, SCH, FP8, MODE>(A, W0, W1, M, N, K, ep, st);
     return launch_t<128, 128, 2, 2, 2, 3, 128, 0, 2, 0, FP8, MODE>(A, W0, W1, M, N, K, ep, st);
 }
 
