@@ -96,19 +96,24 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void attn_bf16_pipe_ker
         asm volatile("" : "+s"(a));
         return (LDSPTR)(uintptr_t)a;
     };
+    constexpr int NF = 16 / NW;   // fills per operand, wave and tile
+    auto fillK_one = [&](int kt, LDSPTR lk, int i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, lk + i * NW * 1024, 16, voK, kt * KT * 256 + i * 4 * NW * 256, 0,
+                                                 0);
+    };
+    auto fillV_one = [&](int kt, LDSPTR lv, int i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, lv + i * NW * 1024, 16, voV, kt * KT * 2 + i * 8 * NW * Sp * 2, 0,
+                                                 0);
+    };
     auto fillK = [&](int kt, auto bc) {
         LDSPTR lk = untracked(stK(bc) + wave * 1024);
 #pragma unroll
-        for (int i = 0; i < 16 / NW; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, lk + i * NW * 1024, 16, voK, kt * KT * 256 + i * 4 * NW * 256,
-                                                     0, 0);
+        for (int i = 0; i < NF; ++i) fillK_one(kt, lk, i);
     };
     auto fillV = [&](int kt, auto bc) {
         LDSPTR lv = untracked(stV(bc) + wave * 1024);
 #pragma unroll
-        for (int i = 0; i < 16 / NW; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, lv + i * NW * 1024, 16, voV,
-                                                     kt * KT * 2 + i * 8 * NW * Sp * 2, 0, 0);
+        for (int i = 0; i < NF; ++i) fillV_one(kt, lv, i);
     };
     auto vmwait0 = []() { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); };
 
@@ -139,16 +144,16 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void attn_bf16_pipe_ker
     // Iteration t on K stage KB = t % 2 (V^T(t - 1) is in stage KB ^ 1).
     // QK: tile t exists (t < nkt); PV: tile t - 1 exists (t >= 1); MASK: tile
     // t is the last one and keys >= S are masked.
+    // Entering iteration t: K(t) and V^T(t - 1) are in LDS, the first half of
+    // K(t)'s fragments in kpre; this wave's fills of K(t + 1) and V^T(t) are in
+    // flight. The barrier sits in phase B right after its last V^T read: then
+    // every wave is done with K(t) and V^T(t - 1), and the rest of phase B
+    // fills K(t + 2) and V^T(t + 1) into their stages and reads K(t + 1)'s
+    // first fragments, so phase A starts on fragments already in registers.
+    bf16x8_v kpre[4][2];
     auto step = [&](int t, auto kbc, auto qkc, auto pvc, auto maskc) {
         const int KB = kbc;
         constexpr bool QK = decltype(qkc)::value, PV = decltype(pvc)::value, MASK = decltype(maskc)::value;
-        if constexpr (QK) {
-            // V^T(t) goes to stage KB (V^T(t - 2) was read last iteration);
-            // K(t + 1) to stage KB ^ 1 (past the last tile it repeats the
-            // last tile into a stage that is not read again)
-            fillV(t, KB);
-            fillK(min(t + 1, nkt - 1), KB ^ 1);
-        }
         // The two phases are written slot by slot, one MFMA per slot with the
         // VALU work and LDS reads that should issue beside it; the fences keep
         // the compiler from regrouping them (it otherwise issues all MFMAs of a
@@ -156,27 +161,26 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void attn_bf16_pipe_ker
         auto fence = []() { __builtin_amdgcn_sched_barrier(0); };
         // ---- phase A: S(t) = K(t) Q^T on the matrix core, O *= alpha on the VALU
         f32x16 sc[2];
-        bf16x8_v kf[8][2];
+        bf16x8_v kf[4][2];   // second half of K(t)'s fragments
         const uint8_t* bK = stK(KB);
         if constexpr (QK) {
 #pragma unroll
             for (int b = 0; b < 2; ++b)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sc[b][r] = 0.f;
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int b = 0; b < 2; ++b) kf[s][b] = *(const bf16x8_v*)(bK + kOff[s] + b * 8192);
         }
         fence();
         static_for<16>([&](auto ic) {
             constexpr int i = ic, s = i / 2, b = i % 2;
-            if constexpr (QK) sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s][b], qf[s], sc[b], 0, 0, 0);
+            if constexpr (QK) {
+                if constexpr (s < 4) sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kpre[s][b], qf[s], sc[b], 0, 0, 0);
+                else sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s - 4][b], qf[s], sc[b], 0, 0, 0);
+            }
             if constexpr (PV) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) o[i / 4][(i % 4) * 4 + r] *= alpha;
             }
-            if constexpr (QK && s < 4) kf[s + 4][b] = *(const bf16x8_v*)(bK + kOff[s + 4] + b * 8192);
+            if constexpr (QK && s < 4) kf[s][b] = *(const bf16x8_v*)(bK + kOff[s + 4] + b * 8192);
             fence();
         });
         // ---- phase B: O^T += V^T(t - 1) P^T(t - 1) on the matrix core, softmax of S(t) on the VALU
@@ -189,6 +193,14 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void attn_bf16_pipe_ker
 #pragma unroll
                 for (int d = 0; d < 4; ++d) vread(ks, d);
         }
+        // fill bases of K(t + 2) (stage KB) and V^T(t + 1) (stage KB ^ 1), taken outside the slots
+        LDSPTR lkN = nullptr, lvN = nullptr;
+        if constexpr (QK) {
+            lkN = untracked(stK(KB) + wave * 1024);
+            lvN = untracked(stV(KB ^ 1) + wave * 1024);
+        }
+        const int ktK = min(t + 2, nkt - 1), ktV = min(t + 1, nkt - 1);   // past the end: repeats, not read again
+        const uint8_t* bKn = stK(KB ^ 1);
         fence();
         float t0 = 0.f, t1 = 0.f, mc = 0.f, psum = 0.f;
         uint32_t pn[2][8];   // P of tile t
@@ -246,6 +258,18 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void attn_bf16_pipe_ker
                 // the 16 exp pairs over slots 5..15: two in slots 5..9, one after
                 if constexpr (j >= 5 && j <= 9) { pair(2 * (j - 5)); pair(2 * (j - 5) + 1); }
                 if constexpr (j >= 10) pair(j);
+                if constexpr (j == 7) {
+                    // the last V^T reads were in this slot: own fills of K(t + 1)
+                    // and V^T(t) landed, then everyone's; K(t), V^T(t - 1) are free
+                    vmwait0();
+                    lds_barrier();
+                }
+                if constexpr (j >= 8) {
+                    constexpr int f = j - 8;   // fills K(t + 2) then V^T(t + 1), one per slot
+                    if constexpr (f < NF) fillK_one(ktK, lkN, f);
+                    else if constexpr (f < 2 * NF) fillV_one(ktV, lvN, f - NF);
+                    kpre[f / 2][f % 2] = *(const bf16x8_v*)(bKn + kOff[f / 2] + (f % 2) * 8192);
+                }
             }
             fence();
         });
@@ -256,12 +280,6 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void attn_bf16_pipe_ker
 #pragma unroll
                 for (int j = 0; j < 8; ++j) pk[b][j] = pn[b][j];
         }
-        if constexpr (QK) {
-            // this wave's fills have landed, then everyone's; stages KB (K)
-            // and KB ^ 1 (V^T) are free
-            vmwait0();
-            lds_barrier();
-        }
     };
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
@@ -271,6 +289,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void attn_bf16_pipe_ker
     fillK(0, 0);
     vmwait0();
     lds_barrier();
+#pragma unroll
+    for (int f = 0; f < 8; ++f) kpre[f / 2][f % 2] = *(const bf16x8_v*)(sK0 + kOff[f / 2] + (f % 2) * 8192);
+    fillK(min(1, nkt - 1), 1);
+    fillV(0, 0);
     int t = 1;
     if (nkt == 1) {
         step(0, B0{}, T_{}, F_{}, T_{});
