@@ -38,17 +38,17 @@ PEAK_HBM = 8000.0      # GB/s
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 # HBM traffic of the dominant kernel, from two rocprofv3 counter runs of
-# `bench.py --no-cpu --no-off --steps 2 --warmup 1 --copy-calib` (FETCH_SIZE,
+# `bench.py --no-cpu --no-off --no-sweep --no-stack --steps 2 --warmup 1 --copy-calib` (FETCH_SIZE,
 # then WRITE_SIZE; KiB per dispatch), each divided by what the same counter
 # reads per byte of a plain 1 GiB copy. Valid only for the kernel source it was
 # taken on (sha256 of the listed files); otherwise reported as null.
 TRAFFIC = {
-    "gemm_gate_up": {"files": ['video_diffusion_transformer_flash_amd/csrc/gemm_mfma.hip', 'video_diffusion_transformer_flash_amd/csrc/epilogue.h', 'video_diffusion_transformer_flash_amd/csrc/common.h'], "sha": "82580fd1367c3622",
-                     "fetch_bytes": 2919885376, "write_bytes": 107118592,
+    "gemm_gate_up": {"files": ['video_diffusion_transformer_flash_amd/csrc/gemm_mfma.hip', 'video_diffusion_transformer_flash_amd/csrc/epilogue.h', 'video_diffusion_transformer_flash_amd/csrc/common.h'], "sha": "2a9fa8fe151744a8",
+                     "fetch_bytes": 2923342472, "write_bytes": 107118635,
                      "copy_scale": {"FETCH_SIZE": 1.99994, "WRITE_SIZE": 1.0},
                      "source": "profiles/gemm_gate_up_540p_compressed_hbm_traffic.md"},
-    "broadcast_residual": {"files": ['video_diffusion_transformer_flash_amd/csrc/rowops.hip', 'video_diffusion_transformer_flash_amd/csrc/common.h'], "sha": "ae731ca96373fb0c",
-                           "fetch_bytes": 206361936, "write_bytes": 131604480,
+    "broadcast_residual": {"files": ['video_diffusion_transformer_flash_amd/csrc/rowops.hip', 'video_diffusion_transformer_flash_amd/csrc/common.h'], "sha": "d045e595b3b4f2f1",
+                           "fetch_bytes": 206354543, "write_bytes": 131604480,
                            "copy_scale": {"FETCH_SIZE": 1.99994, "WRITE_SIZE": 1.0},
                            "source": "profiles/broadcast_residual_540p_compressed_hbm_traffic.md"},
 }

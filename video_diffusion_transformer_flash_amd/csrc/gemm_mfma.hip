@@ -762,9 +762,10 @@ template <bool FP8, int MODE>
 hipError_t dispatch(const void* A, const void* W0, const void* W1, int M, int N, int K, const EpiParams& ep,
                     hipStream_t st) {
     // 256 x 256 tiles: fills spread over the substeps; for the long-K down
-    // projection issued one step early (measured on the 540p block: QKV,
-    // gate/up and O fastest with the first, down with the second)
-    constexpr int SCH = MODE == EPI_DOWN ? 4 : 3;
+    // projection and every fp8 projection issued one step early (measured on
+    // the 540p block and the fp8 stack: bf16 QKV, gate/up and O fastest with
+    // the first, the others with the second)
+    constexpr int SCH = (FP8 || MODE == EPI_DOWN) ? 4 : 3;
     if constexpr (MODE == EPI_RESID || MODE == EPI_DOWN) {
         // 256 x 256 tiles with a K-split tail when the partial buffer holds it
         const SplitPlan sp = split_plan(FP8, MODE, M, N, K, device_cus());
