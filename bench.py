@@ -43,7 +43,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # reads per byte of a plain 1 GiB copy. Valid only for the kernel source it was
 # taken on (sha256 of the listed files); otherwise reported as null.
 TRAFFIC = {
-    "gemm_gate_up": {"files": ['video_diffusion_transformer_flash_amd/csrc/gemm_mfma.hip', 'video_diffusion_transformer_flash_amd/csrc/epilogue.h', 'video_diffusion_transformer_flash_amd/csrc/common.h'], "sha": "2a9fa8fe151744a8",
+    "gemm_gate_up": {"files": ['video_diffusion_transformer_flash_amd/csrc/gemm_mfma.hip', 'video_diffusion_transformer_flash_amd/csrc/epilogue.h', 'video_diffusion_transformer_flash_amd/csrc/common.h'], "sha": "5be5d83378e9c797",
                      "fetch_bytes": 2923342472, "write_bytes": 107118635,
                      "copy_scale": {"FETCH_SIZE": 1.99994, "WRITE_SIZE": 1.0},
                      "source": "profiles/gemm_gate_up_540p_compressed_hbm_traffic.md"},

@@ -47,8 +47,9 @@ DIT_DEV void swap32(float x, float& lo, float& hi) {
 // to the rescale of O, then the P V MFMAs of tile t - 1 next to the softmax of
 // tile t, so that each wave's own instruction stream keeps its SIMD's matrix
 // core and VALU busy together instead of alternating between them. K and V^T
-// tiles sit one tile apart in LDS: iteration t fills K(t + 1) and V^T(t) while
-// it reads K(t) and V^T(t - 1), two stages per operand as before.
+// tiles sit one tile apart in LDS: iteration t reads K(t) and V^T(t - 1) while
+// K(t + 1) and V^T(t) are in flight, two stages per operand; its second half
+// fills K(t + 2) and V^T(t + 1) (details at the iteration below).
 template <int NW>
 __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void attn_bf16_pipe_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ Vt, bf16_t* __restrict__ O,

@@ -16,8 +16,10 @@
 // step, with a 16-byte-chunk XOR swizzle so that 16 lanes reading one chunk
 // column of 16 consecutive rows hit 16 distinct bank groups of the 64-bank
 // LDS. Fragment reads of the next MFMA substep are issued under the current
-// substep's MFMAs. Workgroup ids are remapped so that neighbouring tiles share
-// an XCD (L2).
+// substep's MFMAs, and the 256 x 256 kernels spread a K step's fills over its
+// substeps, one after each MFMA (or issue them a step early, right after the
+// barrier), instead of a burst that stalls the wave's MFMA issue. Workgroup
+// ids are remapped so that neighbouring tiles share an XCD (L2).
 //
 // K-split tail: when the tiles fill the compute units a whole number of
 // times plus a small remainder, the remainder tiles are cut along K into
