@@ -30,6 +30,7 @@ class BlockDims:
     stride: int = 2
     n_ctrl: int = 0        # control frames at the video's spatial grid (0: none)
     ctrl_offset: int = 0   # target time minus control time (> 0 with control frames)
+    n_fixed: int = 0       # leading video frames the sampler holds fixed (a long video's boundary frame)
 
     @property
     def inner(self) -> int:

@@ -26,4 +26,4 @@ from .compress import (keep_axis, nearest_axis, keep_dims, keep_index, nearest_k
 from .block import (rmsnorm, rope_rotate, attention, swiglu, block_core, block_forward,  # noqa: F401
                     token_coords, BlockWeights)
 from .fp8 import e4m3_encode, e4m3_decode, quantize_weight_fp8, E4M3_MAX  # noqa: F401
-from .sampler import flow_schedule, stack_sample, flash_layer_flags  # noqa: F401
+from .sampler import flow_schedule, stack_sample, flash_layer_flags, long_video_sample  # noqa: F401
