@@ -81,6 +81,9 @@ typedef struct {
     int32_t w_dtype;              /* dit_dtype of the projection weights */
     int32_t n_ctrl;               /* control frames on the video's H x W grid (0: none; *_ctrl calls only) */
     int32_t ctrl_offset;          /* target time minus control time, >= 1 with control frames */
+    int32_t n_fixed;              /* leading video frames the samplers hold fixed: their Euler update is
+                                     skipped, e.g. a long video's shared boundary frame (0..T; the block
+                                     itself ignores it) */
 } dit_dims;
 
 /* One block's parameters (device pointers). Gains g1, g2 [D] have act_dtype;

@@ -58,6 +58,8 @@ def _dims(**kw):
     (dict(n_ctrl=1, ctrl_offset=0), _lib.DIT_EINVAL),          # control frames need a positive offset
     (dict(n_ctrl=-1), _lib.DIT_EINVAL),
     (dict(ctrl_offset=-2), _lib.DIT_EINVAL),
+    (dict(n_fixed=-1), _lib.DIT_EINVAL),
+    (dict(n_fixed=7), _lib.DIT_EINVAL),                          # more fixed frames than T = 6
 ])
 def test_dims_rejected(bad, code):
     n = ctypes.c_size_t()

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle as O
-from dit_synth import BlockDims
+from dit_synth import BlockDims, round_bf16
 from helpers import FP8_MAX_BOUND, gpu_weights, inputs, oracle_weights, rel_err, rms_err, to_numpy, torch_act
 
 pytestmark = pytest.mark.gpu
@@ -153,5 +153,41 @@ def test_history_stack_vs_oracle():
                          tv.astype(np.float32), None, d, x_ctrl=x["x_ctrl"],
                          ctrl_idx=O.history_index(d.n_ctrl, d.H, d.W))
     err = rel_err([to_numpy(xv), to_numpy(xa)], list(ref))
+    print(f"  max|err|/rms = {err:.3e}")
+    assert err <= 6e-2
+
+
+# ---------------------------------------------------------------- chunk-by-chunk long video
+def test_long_video_vs_oracle():
+    """5 chunks of 3 frames (the first; then a boundary frame held fixed and
+    2 new frames, with up to 8 history frames read through the bounded
+    selection), 4 layers (2 compressed), 3 evaluations."""
+    d = CTRL_BF16.with_(name="long_video", d_model=256, n_heads=2, d_ffn=512, T=3, H=8, W=12, n_ctrl=0,
+                        ctrl_offset=0, seed=17)
+    flags = [0, 1, 1, 0]
+    tv, ta = O.flow_schedule(3, 12.0), O.flow_schedule(3, 3.0)
+    x, _ = inputs(d)
+    layers = [inputs(d, layer=l)[1] for l in range(len(flags))]
+    g = np.random.default_rng(99)
+    first = x["x_video"]
+    new = [round_bf16(g.standard_normal((d.T - 1, d.H, d.W, d.d_model)).astype(np.float32)) for _ in range(4)]
+    audio = [x["x_audio"]] + [round_bf16(g.standard_normal((d.n_audio, d.d_model)).astype(np.float32))
+                              for _ in range(4)]
+    print("long video: 5 chunks", flush=True)
+    dims = V.make_dims(d)
+    gl = [gpu_weights(lw, d.dtype)[0] for lw in layers]
+    keep, nk = V.keep_index(d.T, d.H, d.W), V.nearest_kept_map(d.T, d.H, d.W)
+    xt = torch_act(x["x_text"], d.dtype)
+    ga = [torch_act(a, d.dtype) for a in audio]
+    frames = V.long_video_sample(dims, gl, flags, tv, ta, xt, torch_act(first, d.dtype),
+                                 [torch_act(n, d.dtype) for n in new], ga, keep, nk)
+    # the first chunk alone gives the same first frames, boundary included (later chunks hold it fixed)
+    f0, a0 = torch_act(first, d.dtype), torch_act(audio[0], d.dtype)
+    V.stack_sample(dims, gl, flags, tv, ta, xt, f0, a0, keep, nk)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_numpy(frames[:d.T]), to_numpy(f0))
+    ref_f, ref_a = O.long_video_sample(x["x_text"], first, new, audio, [oracle_weights(lw, "bf16") for lw in layers],
+                                       flags, tv.astype(np.float32), ta.astype(np.float32), d)
+    err = rel_err([to_numpy(frames)] + [to_numpy(a) for a in ga], [ref_f] + list(ref_a))
     print(f"  max|err|/rms = {err:.3e}")
     assert err <= 6e-2

@@ -16,7 +16,8 @@ from ._lib import DIT_BF16, DIT_F32, DIT_FP8_E4M3, BlockWeights, Dims, DitError,
 
 __all__ = ["Dims", "make_dims", "keep_dims", "keep_index", "nearest_kept_map", "block_workspace_size",
            "block_forward", "stack_workspace_size", "stack_sample", "quantize_fp8", "gather_kept",
-           "broadcast_residual", "attention", "trace_enable", "trace_records", "DitError"]
+           "broadcast_residual", "attention", "history_index", "long_video_sample", "trace_enable", "trace_records",
+           "DitError"]
 
 _ACT = {"f32": DIT_F32, "bf16": DIT_BF16, "fp8": DIT_BF16}
 _WT = {"f32": DIT_F32, "bf16": DIT_BF16, "fp8": DIT_FP8_E4M3}
@@ -41,7 +42,8 @@ def make_dims(cfg, stride: int = None) -> Dims:
                 n_heads=cfg.n_heads, head_dim=cfg.head_dim, d_ffn=cfg.d_ffn, rope_t=cfg.rope[0], rope_h=cfg.rope[1],
                 rope_w=cfg.rope[2], rope_base=cfg.rope_base, eps=cfg.eps,
                 stride=cfg.stride if stride is None else stride, act_dtype=_ACT[cfg.dtype], w_dtype=_WT[cfg.dtype],
-                n_ctrl=getattr(cfg, "n_ctrl", 0), ctrl_offset=getattr(cfg, "ctrl_offset", 0))
+                n_ctrl=getattr(cfg, "n_ctrl", 0), ctrl_offset=getattr(cfg, "ctrl_offset", 0),
+                n_fixed=getattr(cfg, "n_fixed", 0))
 
 
 def keep_dims(H: int, W: int, stride: int = 2):
@@ -157,6 +159,35 @@ def stack_sample(dims: Dims, layers: list, flags, t_video, t_audio, x_text, x_vi
                                          _ptr(nk), _ptr(ws), ws.numel(), _stream())
         check(st, "dit_stack_sample_ctrl")
     return x_video, x_audio
+
+
+def long_video_sample(dims: Dims, layers: list, flags, t_video, t_audio, x_text, first_video, new_video, audio,
+                      keep=None, nk=None):
+    """Chunk-by-chunk long video on the chunk grid of `dims` (T frames).
+
+    The first chunk denoises first_video [T, H, W, D]. Each later chunk is
+    [the last frame made so far, held fixed (n_fixed = 1) | T - 1 new frames
+    from its block of new_video], with every earlier frame as control frames
+    at the time offset n_hist, of which the block reads the bounded history
+    selection (dit_history_index). audio: one [n_audio, D] tensor per chunk,
+    denoised in place. Returns the frames [T + (chunks - 1)(T - 1), H, W, D]."""
+    T = dims.T
+    frames = torch.empty((T + len(new_video) * (T - 1),) + tuple(first_video.shape[1:]), dtype=first_video.dtype,
+                         device=first_video.device)
+    frames[:T].copy_(first_video)
+    d = Dims.from_buffer_copy(dims)
+    d.n_ctrl, d.ctrl_offset, d.n_fixed = 0, 0, 0
+    stack_sample(d, layers, flags, t_video, t_audio, x_text, frames[:T], audio[0], keep, nk)
+    made = T
+    for noise, a in zip(new_video, audio[1:]):
+        n_hist = made - 1                       # frames before the boundary
+        frames[made:made + T - 1].copy_(noise)
+        d = Dims.from_buffer_copy(dims)
+        d.n_ctrl, d.ctrl_offset, d.n_fixed = n_hist, n_hist, 1
+        stack_sample(d, layers, flags, t_video, t_audio, x_text, frames[n_hist:n_hist + T], a, keep, nk,
+                     x_ctrl=frames[:n_hist], ctrl_idx=history_index(n_hist, dims.H, dims.W))
+        made += T - 1
+    return frames
 
 
 def quantize_fp8(src, codes=None, scale=None):

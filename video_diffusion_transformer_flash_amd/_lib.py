@@ -19,7 +19,7 @@ class Dims(ctypes.Structure):
                 ("d_model", c_i32), ("n_heads", c_i32), ("head_dim", c_i32), ("d_ffn", c_i32),
                 ("rope_t", c_i32), ("rope_h", c_i32), ("rope_w", c_i32), ("rope_base", c_f32), ("eps", c_f32),
                 ("stride", c_i32), ("act_dtype", c_i32), ("w_dtype", c_i32), ("n_ctrl", c_i32),
-                ("ctrl_offset", c_i32)]
+                ("ctrl_offset", c_i32), ("n_fixed", c_i32)]
 
 
 class BlockWeights(ctypes.Structure):

@@ -77,6 +77,7 @@ int validate_dims(const dit_dims* d) {
     if (!(d->rope_base > 0.f) || !(d->eps >= 0.f)) return DIT_EINVAL;
     if (d->n_ctrl < 0 || d->ctrl_offset < 0 || (d->n_ctrl > 0 && d->ctrl_offset < 1)) return DIT_EINVAL;
     if (d->n_ctrl > (1 << 20) || d->ctrl_offset > (1 << 20)) return DIT_EINVAL;
+    if (d->n_fixed < 0 || d->n_fixed > d->T) return DIT_EINVAL;
     const long long nv = (long long)d->T * d->H * d->W;
     const long long S = nv + (long long)d->n_ctrl * d->H * d->W + d->n_text + d->n_audio;
     if (S > (1LL << 30) || nv * d->d_model > (1LL << 40)) return DIT_EINVAL;
@@ -546,7 +547,11 @@ int stack_impl(const dit_dims* dims, const dit_block_weights* layers_host, int32
         const void* vv = n_layers ? (const void*)Zv : (const void*)x_video;
         const void* va = n_layers ? (const void*)Za : (const void*)x_audio;
         TR("euler");
-        HIPCHK(euler_launch(bf, x_video, vv, (size_t)nv * D, dtv, st));
+        // the first n_fixed frames keep their state (their velocity is not applied)
+        const size_t fixed = (size_t)d.n_fixed * d.H * d.W * D;
+        if (fixed < (size_t)nv * D)
+            HIPCHK(euler_launch(bf, (uint8_t*)x_video + fixed * es, (const uint8_t*)vv + fixed * es,
+                                (size_t)nv * D - fixed, dtv, st));
         if (na > 0) HIPCHK(euler_launch(bf, x_audio, va, (size_t)na * D, dta, st));
     }
     TR("end");
