@@ -47,9 +47,9 @@ TRAFFIC = {
                      "fetch_bytes": 2923342472, "write_bytes": 107118635,
                      "copy_scale": {"FETCH_SIZE": 1.99994, "WRITE_SIZE": 1.0},
                      "source": "profiles/gemm_gate_up_540p_compressed_hbm_traffic.md"},
-    "broadcast_residual": {"files": ['video_diffusion_transformer_flash_amd/csrc/rowops.hip', 'video_diffusion_transformer_flash_amd/csrc/common.h'], "sha": "d045e595b3b4f2f1",
-                           "fetch_bytes": 206354543, "write_bytes": 131604480,
-                           "copy_scale": {"FETCH_SIZE": 1.99994, "WRITE_SIZE": 1.0},
+    "broadcast_residual": {"files": ['video_diffusion_transformer_flash_amd/csrc/rowops.hip', 'video_diffusion_transformer_flash_amd/csrc/common.h'], "sha": "77ce29bdaa28141f",
+                           "fetch_bytes": 206408630, "write_bytes": 131604480,
+                           "copy_scale": {"FETCH_SIZE": 1.99992, "WRITE_SIZE": 1.0},
                            "source": "profiles/broadcast_residual_540p_compressed_hbm_traffic.md"},
 }
 

@@ -280,21 +280,28 @@ __global__ __launch_bounds__(512) void broadcast_residual_kernel(const T* x, con
                                                                  int D) {
     // x and out may be the same buffer: every element is read, then written, by one thread
     constexpr int U = 4;
-    const int p = xcd_remap(blockIdx.x, (n_video + 1) / 2) * 2 + (threadIdx.x >> 8);
+    // p is wave-uniform, so the kept slot nk[p] comes through a scalar load,
+    // and the x loads (which do not depend on it) go out before it arrives
+    const int p = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, (n_video + 1) / 2) * 2 + (threadIdx.x >> 8));
     if (p >= n_video) return;
-    const int j = __builtin_amdgcn_readfirstlane(nk[p]);
     const int per_row = D / 8;
     const T* xr = x + (size_t)p * D;
-    const float* dr = delta + (size_t)j * D;
     T* orow = out + (size_t)p * D;
-    for (int c0 = threadIdx.x & 255; c0 < per_row; c0 += U * 256) {
-        Chunk8<T> xv[U];
+    Chunk8<T> xv[U];
+    auto load_x = [&](int c0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (c0 + u * 256 < per_row) xv[u].load(xr + 8 * (c0 + u * 256));
+    };
+    int c0 = threadIdx.x & 255;
+    load_x(c0);
+    const float* dr = delta + (size_t)nk[p] * D;
+    for (;;) {
         float4 d0[U], d1[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int c = c0 + u * 256;
             if (c < per_row) {
-                xv[u].load(xr + 8 * c);
                 d0[u] = *(const float4*)(dr + 8 * c);
                 d1[u] = *(const float4*)(dr + 8 * c + 4);
             }
@@ -304,6 +311,9 @@ __global__ __launch_bounds__(512) void broadcast_residual_kernel(const T* x, con
             const int c = c0 + u * 256;
             if (c < per_row) xv[u].add_store(orow + 8 * c, d0[u], d1[u]);
         }
+        c0 += U * 256;
+        if (c0 >= per_row) break;
+        load_x(c0);
     }
 }
 
