@@ -180,8 +180,10 @@ LONG_FP8 = BlockDims("long_fp8", d_model=256, n_heads=8, head_dim=128, d_ffn=204
                      n_audio=8, rope=(32, 48, 48), dtype="fp8", seed=22)
 
 
-@pytest.mark.parametrize("d,compress", [(LONG_BF16, False), (LONG_BF16.with_(name="long_bf16_c16", T=16, seed=23), True)],
-                         ids=["long_bf16", "long_bf16_c16"])
+LONG_CASES = [(LONG_BF16, False), (LONG_BF16.with_(name="long_bf16_c16", T=16, seed=23), True)]
+
+
+@pytest.mark.parametrize("d,compress", LONG_CASES, ids=["long_bf16", "long_bf16_c16"])
 def test_many_tokens_sampled(d, compress):
     check_sampled(d, compress)
 
