@@ -333,6 +333,55 @@ def stack_timing(reps=2):
             "outputs_finite": ok}
 
 
+def decoder_timing(reps=3):
+    """A stand-in for the distilled light decoder: 26 blocks at its widths
+    (hidden 2048, 16 heads of 128, FFN 4 x 2048) over the 540p latent grid
+    (6 x 34 x 60 tokens, no text or audio, no compression), bf16, each layer
+    with its own weights. The pages give the decoder's depth and widths only
+    (its upsampling and convolutions are not described), so this times a
+    transformer of that size on the latent tokens, not the decoder itself."""
+    import torch
+    import video_diffusion_transformer_flash_amd as V
+    from dit_synth import CONFIGS, DECODER_LAYERS
+    d = CONFIGS["decoder"]
+    x, w0 = _gpu_block_inputs(d, 5000)
+    one = d.with_(T=1, H=1, W=1)
+    layers = [w0] + [_gpu_block_inputs(one, 5001 + l)[1] for l in range(1, DECODER_LAYERS)]
+    dims = V.make_dims(d)
+    ws = V.workspace(V.block_workspace_size(dims, False))
+    xt, xa = x["x_text"], x["x_audio"]
+    bufs = [x["x_video"].clone(), torch.empty_like(x["x_video"])]
+    yt, ya = torch.empty_like(xt), torch.empty_like(xa)
+
+    def run():
+        for l, w in enumerate(layers):
+            src, dst = bufs[l % 2], bufs[(l + 1) % 2]
+            V.block_forward(dims, xt, src, xa, w, False, None, None, out=(yt, dst, ya), ws=ws)
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(reps):
+        bufs[0].copy_(x["x_video"])
+        e0.record()
+        run()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = sorted(ts)[len(ts) // 2]
+    fl = block_flops(d, d.n_video)
+    tf = DECODER_LAYERS * sum(fl.values()) / 1e12
+    ok = bool(torch.isfinite(bufs[DECODER_LAYERS % 2].float()).all())
+    del layers, w0, ws, bufs
+    torch.cuda.empty_cache()
+    return {"workload": f"{DECODER_LAYERS} blocks of width 2048 (16 x 128 heads, FFN 8192), 540p latent grid "
+                        "6x34x60 (12240 tokens), bf16, uncompressed", "ms": round(ms, 2), "reps": reps,
+            "ms_per_layer": round(ms / DECODER_LAYERS, 3), "tflop": round(tf, 2),
+            "TFLOP/s": round(tf / (ms * 1e-3), 1), "frac_of_bf16_peak": round(tf / (ms * 1e-3) / PEAK_BF16, 4),
+            "attention_share_of_flops": round(fl["attention"] / sum(fl.values()), 3), "outputs_finite": ok}
+
+
 def copy_calibration(nbytes=1 << 30, reps=3):
     """Plain elementwise copies of a known size (b = a * 1 over fp32, 16-byte
     vector accesses like the library's kernels): the reference dispatches
@@ -389,6 +438,7 @@ def main():
     ap.add_argument("--copy-calib", action="store_true", help="add 1 GiB reference copies (counter calibration)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the 768p frame sweep")
     ap.add_argument("--no-stack", action="store_true", help="skip the 42-layer fp8 stack")
+    ap.add_argument("--no-decoder", action="store_true", help="skip the decoder-width 26-layer stand-in")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures the block on one GPU; the multi-GPU sharding is not part of this build "
@@ -446,6 +496,8 @@ def main():
         line["sweep_768p"] = sweep()
     if not a.no_stack:
         line["stack"] = stack_timing()
+    if not a.no_decoder:
+        line["decoder_standin"] = decoder_timing()
     if not a.no_cpu:
         line["cpu_baseline"] = cpu_baseline(d, host, True)
     print(json.dumps(line), flush=True)

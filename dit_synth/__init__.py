@@ -5,7 +5,7 @@ draws random numbers and formats them for storage (bf16 rounding, raw bit
 patterns). It holds none of the block's arithmetic: no normalisation, rotary
 embedding, attention, projection, compression or quantisation.
 
-Value recipe (the workload description of the five block configurations):
+Value recipe (the workload description of the block configurations):
   * activations (text, video, audio rows)  ~ N(0, 1)
   * projection weights W[out, in]          ~ N(0, 1/fan_in)   (second argument
     read as the variance, so std = 1/sqrt(fan_in))
@@ -22,7 +22,8 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-from .configs import BlockDims, CONFIGS, FLASH_EVALS, FLASH_LAYERS, SWEEP_FRAMES, get_config  # noqa: F401
+from .configs import (BlockDims, CONFIGS, DECODER_LAYERS, FLASH_EVALS, FLASH_LAYERS, SWEEP_FRAMES,  # noqa: F401
+                      get_config)
 
 # tensor ids inside one seed
 TID_X_TEXT, TID_X_VIDEO, TID_X_AUDIO, TID_X_CTRL = 0, 1, 2, 3

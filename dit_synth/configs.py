@@ -62,6 +62,12 @@ CONFIGS = {
     "768p": BlockDims("768p", T=6, H=48, W=84, n_text=512, n_audio=132, dtype="bf16", seed=3, **FLASH),
     # 42-layer, 3-evaluation fp8 stack on the 540p grid
     "stack": BlockDims("stack", T=6, H=34, W=60, n_text=256, n_audio=132, dtype="fp8", seed=4, **FLASH),
+    # the light decoder's width (hidden 2048, FFN 4x: tokendh.com article,
+    # decoder section) as a block over the 540p latent grid alone (no text or
+    # audio tokens, no compression): a timing stand-in, since the pages give
+    # the decoder's depth and widths but not its layers
+    "decoder": BlockDims("decoder", d_model=2048, n_heads=16, head_dim=128, d_ffn=8192, T=6, H=34, W=60, n_text=0,
+                         n_audio=0, rope=(32, 48, 48), dtype="bf16", seed=11),
 }
 
 # Flash layer schedule: 2 full, 26 compressed, 14 full (tokendh.com article,
@@ -69,6 +75,8 @@ CONFIGS = {
 FLASH_LAYERS = (2, 26, 14)
 FLASH_EVALS = 3
 SWEEP_FRAMES = (2, 8, 32)
+# the distilled student decoder's depth (tokendh.com article, decoder section)
+DECODER_LAYERS = 26
 
 
 def get_config(name: str) -> BlockDims:

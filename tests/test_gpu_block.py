@@ -131,9 +131,13 @@ def test_deterministic_and_in_place():
 
 def sampled(d, compress, n_video=96, seed=0):
     g = np.random.default_rng(seed)
-    sv = np.unique(np.concatenate([g.integers(0, d.n_video, n_video), [0, d.n_video - 1, d.W - 1]]))
-    st = np.unique(np.concatenate([g.integers(0, d.n_text, 8), [d.n_text - 1]]))
-    sa = np.unique(np.concatenate([g.integers(0, d.n_audio, 8), [d.n_audio - 1]]))
+
+    def pick(n, k, fixed):
+        return np.unique(np.concatenate([g.integers(0, n, k), fixed])) if n else np.zeros(0, np.int64)
+
+    sv = pick(d.n_video, n_video, [0, d.n_video - 1, d.W - 1])
+    st = pick(d.n_text, 8, [d.n_text - 1])
+    sa = pick(d.n_audio, 8, [d.n_audio - 1])
     return {"text": st, "video": sv, "audio": sa}
 
 
@@ -190,3 +194,17 @@ def test_many_tokens_sampled(d, compress):
 
 def test_many_tokens_fp8():
     check_full(LONG_FP8, False)
+
+
+# The light decoder's widths (2048, 16 heads of 128, FFN 8192) as a video-only
+# block: every element on a small grid, sampled rows on the 540p latent grid
+# that the decoder timing runs at.
+DECODER_SMALL = CONFIGS["decoder"].with_(name="decoder_small", T=2, H=9, W=15, seed=12)
+
+
+def test_decoder_width_small():
+    check_full(DECODER_SMALL, False)
+
+
+def test_decoder_width_sampled():
+    check_sampled(CONFIGS["decoder"], False)
