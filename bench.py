@@ -13,7 +13,7 @@ timed as a second line item.
 The bandwidth-bound kernels (gather of the kept rows, nearest-kept broadcast
 plus residual) are also timed alone on the same shapes with the 256 MB
 Infinity Cache and the L2s flushed before every repetition, which is the number
-their HBM roofline fraction is judged on. The flush reads a 1 GiB buffer: a
+their HBM roofline fraction is quoted on. The flush reads a 1 GiB buffer: a
 write flush would leave up to ~290 MB of dirty lines whose write-back to HBM
 would then be charged to the kernel under test.
 
@@ -441,8 +441,8 @@ def main():
     ap.add_argument("--no-decoder", action="store_true", help="skip the decoder-width 26-layer stand-in")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures the block on one GPU; the multi-GPU sharding is not part of this build "
-              "(run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures the block on one GPU; sharding across GPUs is designed but not "
+              "implemented (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
