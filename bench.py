@@ -275,13 +275,11 @@ def sweep(steps=2, warmup=1):
     return res
 
 
-def stack_timing(reps=2):
-    """The Flash-shaped stack: 42 blocks with fp8 projections (layers 1-2 full,
-    3-28 compressed, 29-42 full) on the 540p grid, 3 flow-matching Euler
-    evaluations on the fixed schedule t_k = u/(u + s(1-u)), u = k/3 (s = 12
-    video, 3 audio). Reported against the mixed roofline: GEMM FLOPs at the fp8
-    peak plus attention FLOPs at the bf16 peak."""
-    import torch
+def _stack_setup():
+    """The Flash stack's configuration and device-generated fp8 layers: layer
+    flags (2 full, 26 compressed, 14 full), the 540p inputs, the index maps and
+    the fixed 3-step schedules t_k = u/(u + s(1-u)), u = k/3 (s = 12 video, 3
+    audio)."""
     import video_diffusion_transformer_flash_amd as V
     from dit_synth import CONFIGS, FLASH_EVALS, FLASH_LAYERS
     d = CONFIGS["stack"]
@@ -297,7 +295,64 @@ def stack_timing(reps=2):
     def sched(n, s):
         return [(k / n) / ((k / n) + s * (1 - k / n)) for k in range(n + 1)]
 
-    tv, ta = sched(FLASH_EVALS, 12.0), sched(FLASH_EVALS, 3.0)
+    return d, dims, flags, x, w0, layers, keep, nk, sched(FLASH_EVALS, 12.0), sched(FLASH_EVALS, 3.0)
+
+
+def long_video_timing(chunks=4):
+    """Chunk-by-chunk long video with the Flash stack (fp8, 42 layers, 3
+    evaluations per chunk) on the 540p chunk grid: the first chunk denoises 6
+    latent frames, each later chunk holds the last frame made so far fixed and
+    adds 5 new ones with the bounded history of the earlier frames joined as
+    control tokens. Reports each chunk's time and its history token count."""
+    import torch
+    import video_diffusion_transformer_flash_amd as V
+    d, dims, flags, x, w0, layers, keep, nk, tv, ta = _stack_setup()
+    g = torch.Generator(device="cuda").manual_seed(4100)
+    new = [torch.randn((d.T - 1, d.H, d.W, d.d_model), generator=g, device="cuda").bfloat16()
+           for _ in range(chunks - 1)]
+    audio = [x["x_audio"].clone() for _ in range(chunks)]
+    times = []
+    orig = V.stack_sample
+
+    def timed(*args, **kw):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        r = orig(*args, **kw)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+        return r
+
+    V.stack_sample = timed
+    try:
+        V.long_video_sample(dims, layers, flags, tv, ta, x["x_text"], x["x_video"].clone(), new, audio, keep, nk)
+        times.clear()   # the first pass warms up; the second is reported
+        frames = V.long_video_sample(dims, layers, flags, tv, ta, x["x_text"], x["x_video"].clone(), new, audio,
+                                     keep, nk)
+    finally:
+        V.stack_sample = orig
+    # chunk k > 0 starts after T + (k - 1)(T - 1) frames; all but the boundary are history
+    hist = [0] + [int(V.history_index(d.T + k * (d.T - 1) - 1, d.H, d.W).numel()) for k in range(chunks - 1)]
+    ok = bool(torch.isfinite(frames.float()).all())
+    del layers, w0, frames, new, audio
+    torch.cuda.empty_cache()
+    return {"workload": f"{chunks} chunks of the 42-layer fp8 stack (3 evaluations each) on the 540p chunk grid "
+                        "6x34x60: 6 frames, then 5 new frames per chunk with a fixed boundary frame and the "
+                        "bounded history as control tokens", "frames": d.T + (chunks - 1) * (d.T - 1),
+            "chunk_ms": [round(t, 1) for t in times], "history_tokens": hist,
+            "total_ms": round(sum(times), 1), "outputs_finite": ok}
+
+
+def stack_timing(reps=2):
+    """The Flash-shaped stack: 42 blocks with fp8 projections (layers 1-2 full,
+    3-28 compressed, 29-42 full) on the 540p grid, 3 flow-matching Euler
+    evaluations on the fixed schedule t_k = u/(u + s(1-u)), u = k/3 (s = 12
+    video, 3 audio). Reported against the mixed roofline: GEMM FLOPs at the fp8
+    peak plus attention FLOPs at the bf16 peak."""
+    import torch
+    import video_diffusion_transformer_flash_amd as V
+    from dit_synth import FLASH_EVALS
+    d, dims, flags, x, w0, layers, keep, nk, tv, ta = _stack_setup()
     ws = V.workspace(V.stack_workspace_size(dims, flags))
     xv0, xa0 = x["x_video"].clone(), x["x_audio"].clone()
 
@@ -439,6 +494,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the 768p frame sweep")
     ap.add_argument("--no-stack", action="store_true", help="skip the 42-layer fp8 stack")
     ap.add_argument("--no-decoder", action="store_true", help="skip the decoder-width 26-layer stand-in")
+    ap.add_argument("--no-long", action="store_true", help="skip the chunk-by-chunk long video")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures the block on one GPU; sharding across GPUs is designed but not "
@@ -498,6 +554,8 @@ def main():
         line["stack"] = stack_timing()
     if not a.no_decoder:
         line["decoder_standin"] = decoder_timing()
+    if not a.no_long:
+        line["long_video"] = long_video_timing()
     if not a.no_cpu:
         line["cpu_baseline"] = cpu_baseline(d, host, True)
     print(json.dumps(line), flush=True)
