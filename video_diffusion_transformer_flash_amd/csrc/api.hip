@@ -201,6 +201,7 @@ int run_block(const dit_dims& d, const dit_block_weights& w, const SeqIn& in, co
 
     // 1-2. RMSNorm1 + QKV (+ rotary)
     if (fp8) {
+        HIPCHK(fill_launch(sc, 4, 0.f, st));   // the four running maxima of this block, one launch
         TR("rmsnorm1");
         HIPCHK(rmsnorm_fp8_launch(true, in, nullptr, w.g1, (uint8_t*)n, rinv, sc + 0, S, D, d.eps, st));
         ep.amax_a = sc + 0; ep.s_w = w.s_wqkv;
@@ -218,7 +219,6 @@ int run_block(const dit_dims& d, const dit_block_weights& w, const SeqIn& in, co
     if (f32) {
         HIPCHK(attention_f32(q, k, vt, o, S, Sp, nh, dh, csoft, st));
     } else {
-        if (fp8) HIPCHK(fill_launch(sc + 1, 1, 0.f, st));
         HIPCHK(attention_bf16(q, k, vt, o, S, Sp, nh, dh, csoft, fp8 ? sc + 1 : nullptr, st));
     }
     // 4. O projection + residual -> h (fp32)
@@ -239,7 +239,6 @@ int run_block(const dit_dims& d, const dit_block_weights& w, const SeqIn& in, co
     if (fp8) {
         TR("rmsnorm2");
         HIPCHK(rmsnorm_fp8_launch(false, in, h, w.g2, (uint8_t*)n, rinv, sc + 2, S, D, d.eps, st));
-        HIPCHK(fill_launch(sc + 3, 1, 0.f, st));
         ep.amax_a = sc + 2; ep.s_w = w.s_wgate; ep.s_w2 = w.s_wup; ep.u_amax = sc + 3;
         TR("gemm_gate_up");
         HIPCHK(gemm_mfma(true, EPI_SWIGLU, n, w.wgate, w.wup, S, 2 * F, D, ep, st));

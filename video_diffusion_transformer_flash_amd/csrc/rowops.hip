@@ -408,11 +408,11 @@ hipError_t rmsnorm_launch(int act, bool seq_input, const SeqIn& seq, const float
     return hipGetLastError();
 }
 
-// bf16 activations, fp8 output: stats pass (rinv, amax) then quantise pass
+// bf16 activations, fp8 output: stats pass (rinv, amax) then quantise pass;
+// *amax must hold 0 (or a lower bound of the result) on entry
 hipError_t rmsnorm_fp8_launch(bool seq_input, const SeqIn& seq, const float* dense, const void* g, uint8_t* out,
                               float* rinv, float* amax, int M, int D, float eps, hipStream_t st) {
     const dim3 grid(nblk(M, 4)), gstat(nblk(M, 16)), block(256);   // stats: 4 rows per wave
-    hipLaunchKernelGGL(fill_kernel, dim3(1), dim3(64), 0, st, amax, 1, 0.f);
     if (seq_input) {
         hipLaunchKernelGGL((rmsnorm_kernel<bf16_t, bf16_t, uint8_t, true, 1>), gstat, block, 0, st, seq, dense,
                            (const bf16_t*)g, out, rinv, amax, M, D, eps);
