@@ -38,17 +38,17 @@ PEAK_HBM = 8000.0      # GB/s
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 # HBM traffic of the dominant kernel, from two rocprofv3 counter runs of
-# `bench.py --no-cpu --no-off --no-sweep --no-stack --steps 2 --warmup 1 --copy-calib` (FETCH_SIZE,
+# `bench.py --no-cpu --no-off --no-sweep --no-stack --no-decoder --no-long --steps 2 --warmup 1 --copy-calib` (FETCH_SIZE,
 # then WRITE_SIZE; KiB per dispatch), each divided by what the same counter
 # reads per byte of a plain 1 GiB copy. Valid only for the kernel source it was
 # taken on (sha256 of the listed files); otherwise reported as null.
 TRAFFIC = {
     "gemm_gate_up": {"files": ['video_diffusion_transformer_flash_amd/csrc/gemm_mfma.hip', 'video_diffusion_transformer_flash_amd/csrc/epilogue.h', 'video_diffusion_transformer_flash_amd/csrc/common.h'], "sha": "5be5d83378e9c797",
-                     "fetch_bytes": 2923342472, "write_bytes": 107118635,
-                     "copy_scale": {"FETCH_SIZE": 1.99994, "WRITE_SIZE": 1.0},
+                     "fetch_bytes": 2905696690, "write_bytes": 107118613,
+                     "copy_scale": {"FETCH_SIZE": 1.99992, "WRITE_SIZE": 1.0},
                      "source": "profiles/gemm_gate_up_540p_compressed_hbm_traffic.md"},
-    "broadcast_residual": {"files": ['video_diffusion_transformer_flash_amd/csrc/rowops.hip', 'video_diffusion_transformer_flash_amd/csrc/common.h'], "sha": "77ce29bdaa28141f",
-                           "fetch_bytes": 206408630, "write_bytes": 131604480,
+    "broadcast_residual": {"files": ['video_diffusion_transformer_flash_amd/csrc/rowops.hip', 'video_diffusion_transformer_flash_amd/csrc/common.h'], "sha": "7f6d728a117b5b17",
+                           "fetch_bytes": 206407378, "write_bytes": 131604719,
                            "copy_scale": {"FETCH_SIZE": 1.99992, "WRITE_SIZE": 1.0},
                            "source": "profiles/broadcast_residual_540p_compressed_hbm_traffic.md"},
 }
