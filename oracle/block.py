@@ -78,11 +78,20 @@ def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
     return x / np.sqrt(ms + eps) * g
 
 
-def linear(a: np.ndarray, w: np.ndarray, lowbit: bool) -> np.ndarray:
+# Precision each low-bit projection input is held in when its e4m3 codes are
+# decided (codes are integers decided by floating point, so the oracle decides
+# them in the precision the kernels quantise from): the normalised rows and
+# the SwiGLU product in fp32, the attention output in bf16 (the precision in
+# which the attention step hands it on).
+LOWBIT_PRECISION = {"n1": "f32", "o": "bf16", "n2": "f32", "u": "f32"}
+
+
+def linear(a: np.ndarray, w: np.ndarray, lowbit: bool, precision: str = "f64") -> np.ndarray:
     """a @ w^T; with lowbit the input is first quantised to e4m3 with a
-    per-tensor dynamic scale (the weights are already dequantised fp8)."""
+    per-tensor dynamic scale, its codes decided in `precision` (the weights
+    are already dequantised fp8)."""
     if lowbit:
-        a, s = quantize_act_fp8(a)
+        a, s = quantize_act_fp8(a, precision)
         return (a @ w.T) * s
     return a @ w.T
 
@@ -91,9 +100,10 @@ def silu(z: np.ndarray) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
-def swiglu(n2: np.ndarray, wgate: np.ndarray, wup: np.ndarray, lowbit: bool = False) -> np.ndarray:
+def swiglu(n2: np.ndarray, wgate: np.ndarray, wup: np.ndarray, lowbit: bool = False,
+           precision: str = "f64") -> np.ndarray:
     if lowbit:  # one quantised input feeds both projections
-        a, s = quantize_act_fp8(n2)
+        a, s = quantize_act_fp8(n2, precision)
         return silu((a @ wgate.T) * s) * ((a @ wup.T) * s)
     return silu(n2 @ wgate.T) * (n2 @ wup.T)
 
@@ -149,9 +159,13 @@ def rope_rotate(x: np.ndarray, coords: np.ndarray, kinds: np.ndarray, bands, bas
     return out
 
 
-def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, chunk: int = 1024) -> np.ndarray:
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, chunk: int = 1024, p_store=None) -> np.ndarray:
     """q [Sq, heads, dh], k and v [Sk, heads, dh] -> [Sq, heads, dh]:
-    softmax(q k^T / sqrt(dh)) v per head, max-subtracted, unmasked."""
+    softmax(q k^T / sqrt(dh)) v per head, max-subtracted, unmasked.
+
+    p_store (tests only, default none): applied to the unnormalised weights
+    exp(logit - max) before they multiply v and enter the normaliser; a
+    rounding model of an implementation that stores them."""
     sq, nh, dh = q.shape
     out = np.empty((sq, nh, v.shape[-1]), dtype=np.float64)
     scale = 1.0 / np.sqrt(dh)
@@ -162,25 +176,35 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, chunk: int = 1024) ->
             logits = (q[r0:r0 + chunk, h, :] @ kh.T) * scale
             logits -= logits.max(axis=1, keepdims=True)
             p = np.exp(logits)
+            if p_store is not None:
+                p = p_store(p)
             p /= p.sum(axis=1, keepdims=True)
             out[r0:r0 + chunk, h, :] = p @ vh
     return out
 
 
 def block_core(X: np.ndarray, coords: np.ndarray, kinds: np.ndarray, w: BlockWeights, d,
-               rows: np.ndarray = None) -> np.ndarray:
+               rows: np.ndarray = None, store=None) -> np.ndarray:
     """The block on an already assembled joint sequence X [S, D] -> y.
     With `rows`, only those output rows are evaluated (keys and values still
     come from every token); not available for the low-bit form, whose
-    per-tensor activation scales need every row."""
+    per-tensor activation scales need every row.
+
+    store (tests only, default none): store(name, array) -> array is applied
+    to the intermediates an implementation keeps in memory ("n1", "q", "k"
+    after the rotary embedding, "v", "p" the attention weights, "o", "h",
+    "n2", "u"), a rounding model used to measure how far two correct
+    implementations that round differently can drift apart."""
     X = np.asarray(X, dtype=np.float64)
     S, D = X.shape
     nh, dh, I = d.n_heads, d.head_dim, d.n_heads * d.head_dim
     if rows is not None and w.lowbit:
         raise ValueError("row sampling needs the full tensor for low-bit scales")
-    n1 = rmsnorm(X, w.g1, d.eps)
+    st = store if store is not None else (lambda name, a: a)
+    lp = LOWBIT_PRECISION
+    n1 = st("n1", rmsnorm(X, w.g1, d.eps))
     if w.lowbit:
-        qkv = linear(n1, w.wqkv, True)
+        qkv = linear(n1, w.wqkv, True, lp["n1"])
         q, k, v = qkv[:, :I], qkv[:, I:2 * I], qkv[:, 2 * I:]
     else:
         n1q = n1 if rows is None else n1[rows]
@@ -188,18 +212,20 @@ def block_core(X: np.ndarray, coords: np.ndarray, kinds: np.ndarray, w: BlockWei
         k = n1 @ w.wqkv[I:2 * I].T
         v = n1 @ w.wqkv[2 * I:].T
     qrows = np.arange(S) if rows is None or w.lowbit else np.asarray(rows)
-    q = rope_rotate(q.reshape(len(qrows), nh, dh), coords[qrows], kinds[qrows], d.rope, d.rope_base)
-    k = rope_rotate(k.reshape(S, nh, dh), coords, kinds, d.rope, d.rope_base)
-    o = attention(q, k, v.reshape(S, nh, dh)).reshape(len(qrows), I)
+    q = st("q", rope_rotate(q.reshape(len(qrows), nh, dh), coords[qrows], kinds[qrows], d.rope, d.rope_base))
+    k = st("k", rope_rotate(k.reshape(S, nh, dh), coords, kinds, d.rope, d.rope_base))
+    v = st("v", v.reshape(S, nh, dh))
+    p_store = None if store is None else (lambda p: store("p", p))
+    o = st("o", attention(q, k, v, p_store=p_store).reshape(len(qrows), I))
     Xr = X[qrows]
-    h = Xr + linear(o, w.wo, w.lowbit)
-    n2 = rmsnorm(h, w.g2, d.eps)
-    u = swiglu(n2, w.wgate, w.wup, w.lowbit)
-    return h + linear(u, w.wdown, w.lowbit)
+    h = st("h", Xr + linear(o, w.wo, w.lowbit, lp["o"]))
+    n2 = st("n2", rmsnorm(h, w.g2, d.eps))
+    u = st("u", swiglu(n2, w.wgate, w.wup, w.lowbit, lp["n2"]))
+    return h + linear(u, w.wdown, w.lowbit, lp["u"])
 
 
 def block_forward(x_text, x_video, x_audio, w: BlockWeights, d, compress: bool, stride: int = None,
-                  sample: dict = None, x_ctrl=None, t_shift: int = 0, ctrl_idx=None):
+                  sample: dict = None, x_ctrl=None, t_shift: int = 0, ctrl_idx=None, store=None):
     """The full block on the three inputs (x_video [T, H, W, D]).
 
     Returns (y_text [Nt, D], y_video [T, H, W, D], y_audio [Na, D]), and
@@ -213,7 +239,8 @@ def block_forward(x_text, x_video, x_audio, w: BlockWeights, d, compress: bool, 
 
     sample = {"text": idx, "video": flat positions, "audio": idx} evaluates only
     those outputs (returned flat, in the same three-tuple form; no control
-    frames)."""
+    frames). store: the rounding model of block_core (tests only), also
+    applied to the outputs as "out"."""
     s = d.stride if stride is None else stride
     D = d.d_model
     nc = getattr(d, "n_ctrl", 0)
@@ -238,7 +265,7 @@ def block_forward(x_text, x_video, x_audio, w: BlockWeights, d, compress: bool, 
     X = np.concatenate([xt, xv_seq, xc, xa], axis=0)
 
     if sample is None:
-        y = block_core(X, coords, kinds, w, d)
+        y = block_core(X, coords, kinds, w, d, store=store)
         yt, yv_seq = y[:d.n_text], y[d.n_text:d.n_text + nvs]
         yc, ya = y[d.n_text + nvs:d.n_text + nvs + ncs], y[d.n_text + nvs + ncs:]
         if compress:
@@ -246,12 +273,14 @@ def block_forward(x_text, x_video, x_audio, w: BlockWeights, d, compress: bool, 
             yv = xv + delta[nk]
         else:
             yv = yv_seq
+        if store is not None:
+            yt, yv, yc, ya = (store("out", a) for a in (yt, yv, yc, ya))
         out = (yt, yv.reshape(d.T, d.H, d.W, D), ya)
         if not nc:
             return out
         return out + ((yc if ctrl_idx is not None else yc.reshape(nc, d.H, d.W, D)),)
-    if nc:
-        raise ValueError("row sampling is not available with control frames")
+    if nc or store is not None:
+        raise ValueError("row sampling is not available with control frames or a rounding model")
 
     st = np.asarray(sample.get("text", []), dtype=np.int64)
     sv = np.asarray(sample.get("video", []), dtype=np.int64)

@@ -92,11 +92,41 @@ def quantize_weight_fp8(w: np.ndarray):
     return e4m3_encode(q), np.float32(scale)
 
 
-def quantize_act_fp8(a: np.ndarray):
-    """Per-tensor dynamic activation quantisation in fp64: returns
-    (decoded e4m3 values, scale s) with a ~= values * s. This is what the
-    low-bit GEMM consumes: (values @ W_codes^T) * s * s_W."""
+def round_to(a: np.ndarray, precision: str) -> np.ndarray:
+    """Round fp64 values to the nearest value of `precision` ("f64", "f32" or
+    "bf16"; ties to even), returned as fp64. bf16 keeps the top 16 bits of
+    the fp32 pattern: round-half-even on the 16 dropped bits of the fp32
+    value (finite inputs only)."""
     a = np.asarray(a, dtype=np.float64)
+    if precision == "f64":
+        return a
+    a32 = a.astype(np.float32)
+    if precision == "f32":
+        return a32.astype(np.float64)
+    if precision != "bf16":
+        raise ValueError(precision)
+    u = a32.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def quantize_act_fp8(a: np.ndarray, precision: str = "f64"):
+    """Per-tensor dynamic activation quantisation: returns (decoded e4m3
+    values, scale s) with a ~= values * s. This is what the low-bit GEMM
+    consumes: (values @ W_codes^T) * s * s_W.
+
+    A code is an integer decided by floating point, so it is decided in the
+    precision the quantised tensor is held in (`precision`): the values are
+    first rounded to it, amax is taken over the rounded values, and with
+    "f32" or "bf16" the scaled value a * (448 / amax) is formed in IEEE fp32
+    (the factor itself correctly rounded to fp32) before the e4m3 rounding.
+    "f64" does all of it in fp64."""
+    a = round_to(a, precision)
     amax = float(np.max(np.abs(a))) if a.size else 0.0
     s = amax / E4M3_MAX if amax > 0 else 1.0
-    return e4m3_decode(e4m3_encode(a / s)), s
+    if precision == "f64":
+        scaled = a / s
+    else:
+        inv = np.float32(E4M3_MAX) / np.float32(amax) if amax > 0 else np.float32(1)
+        scaled = (a.astype(np.float32) * inv).astype(np.float64)
+    return e4m3_decode(e4m3_encode(scaled)), s

@@ -57,7 +57,8 @@ def _scatter_ctrl(rows, ctrl_idx, d):
     return g.reshape(d.n_ctrl, d.H, d.W, d.d_model)
 
 
-def stack_sample(x_text, x_video, x_audio, layers, flags, t_video, t_audio, d, x_ctrl=None, ctrl_idx=None):
+def stack_sample(x_text, x_video, x_audio, layers, flags, t_video, t_audio, d, x_ctrl=None, ctrl_idx=None,
+                 store=None):
     """Run len(t_video) - 1 evaluations of the layer stack with Euler updates.
 
     Every compressed layer is applied literally (gather the kept tokens,
@@ -65,6 +66,8 @@ def stack_sample(x_text, x_video, x_audio, layers, flags, t_video, t_audio, d, x
     Control frames (x_ctrl, optionally only the tokens at ctrl_idx) are
     re-fed unchanged every evaluation, like text. The first d.n_fixed video
     frames keep their value (no Euler update).
+    store: the block's rounding model (tests only; block_core), also applied
+    to the updated state as "state".
     Returns the final (x_video, x_audio) in fp64."""
     t_video = np.asarray(t_video, dtype=np.float64)
     t_audio = t_video if t_audio is None else np.asarray(t_audio, dtype=np.float64)
@@ -76,22 +79,25 @@ def stack_sample(x_text, x_video, x_audio, layers, flags, t_video, t_audio, d, x
         first = True
         for w, c in zip(layers, flags):
             if zc is None:
-                zt, zv, za = block_forward(zt, zv, za, w, d, compress=bool(c))
+                zt, zv, za = block_forward(zt, zv, za, w, d, compress=bool(c), store=store)
             elif ctrl_idx is None:
-                zt, zv, za, zc = block_forward(zt, zv, za, w, d, compress=bool(c), x_ctrl=zc)
+                zt, zv, za, zc = block_forward(zt, zv, za, w, d, compress=bool(c), x_ctrl=zc, store=store)
             else:
                 # the selected tokens, packed after the first layer
                 zin = zc if first else _scatter_ctrl(zc, ctrl_idx, d)
-                zt, zv, za, zc = block_forward(zt, zv, za, w, d, compress=bool(c), x_ctrl=zin, ctrl_idx=ctrl_idx)
+                zt, zv, za, zc = block_forward(zt, zv, za, w, d, compress=bool(c), x_ctrl=zin, ctrl_idx=ctrl_idx,
+                                               store=store)
             first = False
         step = (t_video[k + 1] - t_video[k]) * zv
         step[:getattr(d, "n_fixed", 0)] = 0.0
         xv = xv + step
         xa = xa + (t_audio[k + 1] - t_audio[k]) * za
+        if store is not None:
+            xv, xa = store("state", xv), store("state", xa)
     return xv, xa
 
 
-def long_video_sample(x_text, first_video, new_video, audio, layers, flags, t_video, t_audio, d):
+def long_video_sample(x_text, first_video, new_video, audio, layers, flags, t_video, t_audio, d, store=None):
     """Chunk-by-chunk long video.
 
     first_video [T, H, W, D]: noise of the first chunk (no history, every
@@ -101,16 +107,17 @@ def long_video_sample(x_text, first_video, new_video, audio, layers, flags, t_vi
     set here). A later chunk is [boundary | new frames]: the boundary is the
     last frame made so far, held fixed; its history is every frame before it,
     read through the bounded selection history_index(n_hist, H, W).
+    store: the block's rounding model (tests only; stack_sample).
     Returns (frames [T + (chunks - 1)(T - 1), H, W, D], [audio per chunk])."""
     v, a = stack_sample(x_text, first_video, audio[0], layers, flags, t_video, t_audio,
-                        d.with_(n_ctrl=0, ctrl_offset=0, n_fixed=0))
+                        d.with_(n_ctrl=0, ctrl_offset=0, n_fixed=0), store=store)
     frames, audio_out = list(v), [a]
     for noise, an in zip(new_video, audio[1:]):
         n_hist = len(frames) - 1                 # frames before the boundary
         target = np.concatenate([frames[-1][None], np.asarray(noise, dtype=np.float64)])
         dc = d.with_(n_ctrl=n_hist, ctrl_offset=n_hist, n_fixed=1)
         v, a = stack_sample(x_text, target, an, layers, flags, t_video, t_audio, dc,
-                            x_ctrl=np.stack(frames[:n_hist]), ctrl_idx=history_index(n_hist, d.H, d.W))
+                            x_ctrl=np.stack(frames[:n_hist]), ctrl_idx=history_index(n_hist, d.H, d.W), store=store)
         frames += list(v[1:])
         audio_out.append(a)
     return np.stack(frames), audio_out

@@ -1,0 +1,88 @@
+"""Noise floors of the parity metric (test infrastructure, CPU only).
+
+A block with low-bit projections quantises four activation tensors to e4m3
+codes with per-tensor scales. A code is a discontinuous function of the value
+it encodes, so two correct implementations whose intermediates differ by
+rounding alone give codes that differ by one step wherever a value sits near a
+rounding boundary; a changed code in the attention output or a norm output
+moves whole token rows, and such changes cascade through the next norm. The
+max |error| / RMS metric therefore has a floor that no implementation rounding
+differently from the oracle can go below.
+
+The floor of a case is measured with the oracle itself: the oracle against
+the oracle with a rounding model of the GPU kernels' documented storage
+points (GPU_STORE) applied through its `store` hook. The parity bar of a
+low-bit case is FLOOR_MARGIN times that floor (max and RMS). The floors of
+the cases the GPU tests use are written to tests/golden/parity_floors.json by
+tests/golden/make_floors.py, which calls only the oracle and the seeded input
+generator; test_floors.py recomputes the small ones.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+
+import oracle as O
+from oracle.fp8 import round_to
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "parity_floors.json")
+FLOOR_MARGIN = 1.5
+
+# Precision in which the GPU kernels store each intermediate (None: not
+# stored; the value goes on in registers or straight into its quantiser).
+#   bf16 block: normalised rows, q / k / v, the attention weights P, the
+#     attention output, the SwiGLU product and the outputs in bf16; h in fp32.
+#   fp8 projections: the normalised rows go to the e4m3 quantiser from fp32,
+#     the SwiGLU product is kept in fp32 until its quantisation; the rest as
+#     for bf16.
+#   stacks: the state between layers and evaluations in the activation dtype.
+GPU_STORE = {
+    "bf16": {"n1": "bf16", "q": "bf16", "k": "bf16", "v": "bf16", "p": "bf16", "o": "bf16", "h": "f32",
+             "n2": "bf16", "u": "bf16", "out": "bf16", "state": "bf16"},
+    "fp8": {"n1": None, "q": "bf16", "k": "bf16", "v": "bf16", "p": "bf16", "o": "bf16", "h": "f32", "n2": None,
+            "u": "f32", "out": "bf16", "state": "bf16"},
+    "f32": {k: "f32" for k in ("n1", "q", "k", "v", "p", "o", "h", "n2", "u", "out", "state")},
+}
+
+
+def gpu_store(dtype: str):
+    table = GPU_STORE[dtype]
+
+    def store(name, a):
+        prec = table.get(name)
+        return a if prec is None else round_to(a, prec)
+    return store
+
+
+def errors(got, ref):
+    g = np.concatenate([np.asarray(x, dtype=np.float64).ravel() for x in got])
+    r = np.concatenate([np.asarray(x, dtype=np.float64).ravel() for x in ref])
+    rms = np.sqrt(np.mean(r * r))
+    return float(np.max(np.abs(g - r)) / rms), float(np.sqrt(np.mean((g - r) ** 2)) / rms)
+
+
+def block_floor(d, x, ow, compress: bool):
+    """(max, rms) of oracle vs the oracle under GPU_STORE, over every output."""
+    ref = O.block_forward(x["x_text"], x["x_video"], x["x_audio"], ow, d, compress)
+    mod = O.block_forward(x["x_text"], x["x_video"], x["x_audio"], ow, d, compress, store=gpu_store(d.dtype))
+    return errors(mod, ref)
+
+
+def stack_floor(d, x, layers, flags, tv, ta):
+    ref = O.stack_sample(x["x_text"], x["x_video"], x["x_audio"], layers, flags, tv, ta, d)
+    mod = O.stack_sample(x["x_text"], x["x_video"], x["x_audio"], layers, flags, tv, ta, d,
+                         store=gpu_store(d.dtype))
+    return errors(mod, ref)
+
+
+def load():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def bar(case: str):
+    """(max bar, rms bar) of a low-bit or stack case: FLOOR_MARGIN x its floor."""
+    fl = load()[case]
+    return FLOOR_MARGIN * fl["max"], FLOOR_MARGIN * fl["rms"]
