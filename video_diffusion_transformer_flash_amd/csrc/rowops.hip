@@ -165,6 +165,125 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(SeqIn seq, const float* __
     }
 }
 
+// Single-pass form: one wave per row with the whole row in registers (up to
+// NCM 16-byte chunks per lane: D <= 64 * NCM * 16 / sizeof(TI)); the row is
+// read from memory once. MODE as above; MODE 2 still reads the row again,
+// since the codes need the tensor's max, known only after every row.
+template <int N, typename T> DIT_DEV void ldn(const T* p, float v[N]);
+template <> DIT_DEV void ldn<4, float>(const float* p, float v[4]) { ld4<float>(p, v); }
+template <> DIT_DEV void ldn<4, bf16_t>(const bf16_t* p, float v[4]) { ld4<bf16_t>(p, v); }
+template <> DIT_DEV void ldn<8, bf16_t>(const bf16_t* p, float v[8]) {
+    const uint4 x = *(const uint4*)p;
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+template <> DIT_DEV void ldn<8, float>(const float* p, float v[8]) {
+    ld4<float>(p, v);
+    ld4<float>(p + 4, v + 4);
+}
+// 16 bytes of TI -> N = 16 / sizeof(TI) floats
+template <typename TI> DIT_DEV void unpack16(const uint4& r, float* v);
+template <> DIT_DEV void unpack16<bf16_t>(const uint4& r, float* v) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+template <> DIT_DEV void unpack16<float>(const uint4& r, float* v) {
+    v[0] = __uint_as_float(r.x); v[1] = __uint_as_float(r.y); v[2] = __uint_as_float(r.z); v[3] = __uint_as_float(r.w);
+}
+template <int N, typename TO> DIT_DEV void stn(TO* p, const float* v);
+template <> DIT_DEV void stn<4, float>(float* p, const float* v) { *(float4*)p = make_float4(v[0], v[1], v[2], v[3]); }
+template <> DIT_DEV void stn<4, bf16_t>(bf16_t* p, const float* v) {
+    *(uint2*)p = make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
+}
+template <> DIT_DEV void stn<8, bf16_t>(bf16_t* p, const float* v) {
+    *(uint4*)p = make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7]));
+}
+DIT_DEV uint32_t e4m3x4(const float* v, float qs) {
+    return f32_to_e4m3(v[0] * qs) | (f32_to_e4m3(v[1] * qs) << 8) | (f32_to_e4m3(v[2] * qs) << 16) |
+           (f32_to_e4m3(v[3] * qs) << 24);
+}
+template <> DIT_DEV void stn<4, uint8_t>(uint8_t* p, const float* v) { *(uint32_t*)p = e4m3x4(v, 1.f); }
+template <> DIT_DEV void stn<8, uint8_t>(uint8_t* p, const float* v) {
+    *(uint2*)p = make_uint2(e4m3x4(v, 1.f), e4m3x4(v + 4, 1.f));
+}
+
+template <typename TI, typename TG, typename TO, bool SEQ, int MODE, int NCM>
+__global__ __launch_bounds__(256) void rmsnorm_reg_kernel(SeqIn seq, const float* __restrict__ dense,
+                                                          const TG* __restrict__ g, TO* __restrict__ out,
+                                                          float* __restrict__ rinv, float* __restrict__ amax, int M,
+                                                          int D, float eps) {
+    constexpr int EPC = 16 / sizeof(TI);   // elements per 16-byte chunk
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + wave);
+    float mx = 0.f;
+    if (m < M) {
+        const TI* x = SEQ ? seq_row<TI>(seq, m, D) : (const TI*)(dense + (size_t)m * D);
+        const int nch = D / EPC;
+        uint4 r[NCM];
+#pragma unroll
+        for (int i = 0; i < NCM; ++i)
+            if (lane + 64 * i < nch) r[i] = ((const uint4*)x)[lane + 64 * i];
+        float rr;
+        if constexpr (MODE == 2) {
+            rr = rinv[m];
+        } else {
+            float ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < NCM; ++i)
+                if (lane + 64 * i < nch) {
+                    float v[EPC];
+                    unpack16<TI>(r[i], v);
+#pragma unroll
+                    for (int k = 0; k < EPC; ++k) ss = fmaf(v[k], v[k], ss);
+                }
+            ss = wave_sum(ss);
+            rr = 1.f / sqrtf(ss / (float)D + eps);
+        }
+        float qs = 1.f;
+        if constexpr (MODE == 2) {
+            const float a = *amax;
+            qs = a > 0.f ? 448.f / a : 1.f;
+        }
+#pragma unroll
+        for (int i = 0; i < NCM; ++i) {
+            const int c = lane + 64 * i;
+            if (c < nch) {
+                float v[EPC], gv[EPC];
+                unpack16<TI>(r[i], v);
+                ldn<EPC, TG>(g + c * EPC, gv);
+#pragma unroll
+                for (int k = 0; k < EPC; ++k) v[k] = v[k] * rr * gv[k];
+                if constexpr (MODE == 0) {
+                    stn<EPC, TO>(out + (size_t)m * D + c * EPC, v);
+                } else if constexpr (MODE == 1) {
+#pragma unroll
+                    for (int k = 0; k < EPC; ++k) mx = fmaxf(mx, fabsf(v[k]));
+                } else {
+#pragma unroll
+                    for (int k = 0; k < EPC; ++k) v[k] *= qs;
+                    stn<EPC, uint8_t>((uint8_t*)out + (size_t)m * D + c * EPC, v);
+                }
+            }
+        }
+        if (MODE == 1 && lane == 0) rinv[m] = rr;
+    }
+    if constexpr (MODE == 1) {
+        __shared__ float wmax[4];
+        mx = wave_max(mx);
+        if (lane == 0) wmax[wave] = mx;
+        __syncthreads();
+        if (threadIdx.x == 0) atomic_max_nonneg(amax, fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
+    }
+}
+
 // ----------------------------------------------------------------- quantisation
 // e4m3 codes of src * 448 / amax for a bf16 / fp32 tensor (amax on the device)
 template <typename T>
@@ -387,23 +506,31 @@ hipError_t rope_rows_launch(const Rope& r, float2* rows, int S, int npair, hipSt
     return hipGetLastError();
 }
 
+// register-resident rows when they fit: D <= 6144 (12 chunks of 16 bytes per
+// lane for bf16 rows, 24 for fp32 rows)
+constexpr int DMAX_REG = 6144;
+
+template <typename TI, typename TG, typename TO, bool SEQ, int MODE>
+void rms_go(dim3 grid, dim3 gstat, hipStream_t st, const SeqIn& seq, const float* dense, const void* g, void* out,
+            float* rinv, float* amax, int M, int D, float eps) {
+    constexpr int NCM = DMAX_REG * (int)sizeof(TI) / 1024;
+    if (D <= DMAX_REG)
+        hipLaunchKernelGGL((rmsnorm_reg_kernel<TI, TG, TO, SEQ, MODE, NCM>), grid, dim3(256), 0, st, seq, dense,
+                           (const TG*)g, (TO*)out, rinv, amax, M, D, eps);
+    else
+        hipLaunchKernelGGL((rmsnorm_kernel<TI, TG, TO, SEQ, MODE>), MODE == 1 ? gstat : grid, dim3(256), 0, st, seq,
+                           dense, (const TG*)g, (TO*)out, rinv, amax, M, D, eps);
+}
+
 hipError_t rmsnorm_launch(int act, bool seq_input, const SeqIn& seq, const float* dense, const void* g, void* out,
                           int M, int D, float eps, hipStream_t st) {
-    const dim3 grid(nblk(M, 4)), block(256);
+    const dim3 grid(nblk(M, 4)), gstat(nblk(M, 16));
     if (act == DIT_F32) {
-        if (seq_input)
-            hipLaunchKernelGGL((rmsnorm_kernel<float, float, float, true, 0>), grid, block, 0, st, seq, dense,
-                               (const float*)g, (float*)out, (float*)nullptr, (float*)nullptr, M, D, eps);
-        else
-            hipLaunchKernelGGL((rmsnorm_kernel<float, float, float, false, 0>), grid, block, 0, st, seq, dense,
-                               (const float*)g, (float*)out, (float*)nullptr, (float*)nullptr, M, D, eps);
+        if (seq_input) rms_go<float, float, float, true, 0>(grid, gstat, st, seq, dense, g, out, nullptr, nullptr, M, D, eps);
+        else rms_go<float, float, float, false, 0>(grid, gstat, st, seq, dense, g, out, nullptr, nullptr, M, D, eps);
     } else {
-        if (seq_input)
-            hipLaunchKernelGGL((rmsnorm_kernel<bf16_t, bf16_t, bf16_t, true, 0>), grid, block, 0, st, seq, dense,
-                               (const bf16_t*)g, (bf16_t*)out, (float*)nullptr, (float*)nullptr, M, D, eps);
-        else
-            hipLaunchKernelGGL((rmsnorm_kernel<float, bf16_t, bf16_t, false, 0>), grid, block, 0, st, seq, dense,
-                               (const bf16_t*)g, (bf16_t*)out, (float*)nullptr, (float*)nullptr, M, D, eps);
+        if (seq_input) rms_go<bf16_t, bf16_t, bf16_t, true, 0>(grid, gstat, st, seq, dense, g, out, nullptr, nullptr, M, D, eps);
+        else rms_go<float, bf16_t, bf16_t, false, 0>(grid, gstat, st, seq, dense, g, out, nullptr, nullptr, M, D, eps);
     }
     return hipGetLastError();
 }
@@ -412,17 +539,13 @@ hipError_t rmsnorm_launch(int act, bool seq_input, const SeqIn& seq, const float
 // *amax must hold 0 (or a lower bound of the result) on entry
 hipError_t rmsnorm_fp8_launch(bool seq_input, const SeqIn& seq, const float* dense, const void* g, uint8_t* out,
                               float* rinv, float* amax, int M, int D, float eps, hipStream_t st) {
-    const dim3 grid(nblk(M, 4)), gstat(nblk(M, 16)), block(256);   // stats: 4 rows per wave
+    const dim3 grid(nblk(M, 4)), gstat(nblk(M, 16));   // the two-pass fallback's stats pass: 4 rows per wave
     if (seq_input) {
-        hipLaunchKernelGGL((rmsnorm_kernel<bf16_t, bf16_t, uint8_t, true, 1>), gstat, block, 0, st, seq, dense,
-                           (const bf16_t*)g, out, rinv, amax, M, D, eps);
-        hipLaunchKernelGGL((rmsnorm_kernel<bf16_t, bf16_t, uint8_t, true, 2>), grid, block, 0, st, seq, dense,
-                           (const bf16_t*)g, out, rinv, amax, M, D, eps);
+        rms_go<bf16_t, bf16_t, uint8_t, true, 1>(grid, gstat, st, seq, dense, g, out, rinv, amax, M, D, eps);
+        rms_go<bf16_t, bf16_t, uint8_t, true, 2>(grid, gstat, st, seq, dense, g, out, rinv, amax, M, D, eps);
     } else {
-        hipLaunchKernelGGL((rmsnorm_kernel<float, bf16_t, uint8_t, false, 1>), gstat, block, 0, st, seq, dense,
-                           (const bf16_t*)g, out, rinv, amax, M, D, eps);
-        hipLaunchKernelGGL((rmsnorm_kernel<float, bf16_t, uint8_t, false, 2>), grid, block, 0, st, seq, dense,
-                           (const bf16_t*)g, out, rinv, amax, M, D, eps);
+        rms_go<float, bf16_t, uint8_t, false, 1>(grid, gstat, st, seq, dense, g, out, rinv, amax, M, D, eps);
+        rms_go<float, bf16_t, uint8_t, false, 2>(grid, gstat, st, seq, dense, g, out, rinv, amax, M, D, eps);
     }
     return hipGetLastError();
 }
