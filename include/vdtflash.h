@@ -241,6 +241,37 @@ int32_t dit_attention(int32_t S, int32_t n_heads, int32_t head_dim, int32_t dtyp
                       const void* q, const void* k, const void* v, void* o, void* ws, size_t ws_bytes,
                       void* stream);
 
+/* The block's normalisation step on its own [PD-2] (the first and second
+ * RMSNorm, with the e4m3 quantisation of the low-bit projections' inputs):
+ * n[m] = x[m] / sqrt(mean(x[m]^2) + eps) * g for M rows of D elements.
+ * x [M][D] has in_dtype (F32 or BF16), g [D] the activation dtype of the
+ * combination. Combinations (in_dtype -> out_dtype):
+ *   F32 -> F32 (g F32); BF16 -> BF16 and F32 -> BF16 (g BF16);
+ *   BF16 -> FP8_E4M3 and F32 -> FP8_E4M3 (g BF16): out receives the e4m3
+ *   codes (uint8 [M][D]) of n * (448 / amax) with amax = max |n| over the
+ *   whole tensor (the per-tensor scale is amax / 448), round to nearest even,
+ *   and the call also writes rinv [M] (fp32 row factors 1 / sqrt(mean + eps))
+ *   and *amax (fp32, device; both required for FP8 only, ignored otherwise).
+ * n is computed in fp32. D must be a multiple of 64. */
+int32_t dit_rmsnorm(int32_t M, int32_t D, int32_t in_dtype, int32_t out_dtype, const void* x, const void* g, float eps,
+                    void* out, float* rinv, float* amax, void* stream);
+
+/* The attention output projection with its residual on its own [PD-2]
+ * (low-bit projections, fused residual update):
+ *   h[m][n] = x_res[m][n] + s * sum_k A[m][k] W[n][k]
+ * A [M][K] and W [N][K] both have a_dtype: BF16 (s = 1) or FP8_E4M3 codes
+ * (s = (*a_amax / 448) * (*w_scale), both fp32 on the device: A's codes are
+ * those of A * 448 / amax, W ~= codes * w_scale). x_res [M][N] is bf16, h
+ * [M][N] fp32. N and K multiples of 128. fp32 accumulation on the matrix
+ * cores; when the output tiles fill the compute units a whole number of
+ * times plus a remainder, the remainder tiles are split along K into slices
+ * whose fp32 sums go to the workspace (ws, 256-byte aligned, at least the
+ * queried size) and are added in a fixed order. */
+int32_t dit_project_residual_workspace_size(int32_t M, int32_t N, int32_t K, int32_t a_dtype, size_t* bytes);
+int32_t dit_project_residual(int32_t M, int32_t N, int32_t K, int32_t a_dtype, const void* x_res, const void* a,
+                             const float* a_amax, const void* w, const float* w_scale, float* h, void* ws,
+                             size_t ws_bytes, void* stream);
+
 /* Profiling trace (process-global, not thread-safe). With capacity > 0 the
  * library records a hipEvent on the call's stream before each kernel group of
  * every later call (names: rope_tables, rmsnorm1, gemm_qkv, attention,

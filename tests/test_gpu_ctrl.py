@@ -2,27 +2,22 @@
 positive time offset before the target frames) against the fp64 oracle, and
 the permutation equivalence with the plain block on the GPU itself.
 
-Bars as for the plain block: 1e-4 (fp32), 2e-2 (bf16) on max|err|/RMS; fp8:
-6e-2 on the RMS error and the e4m3 code-flip bound on the max error."""
+Bars as for the plain block: 1e-4 (fp32), 2e-2 (bf16) on max|err|/RMS; fp8
+blocks and the stacks: 1.5 x the case's noise floor (tests/floors.py)."""
 import numpy as np
 import pytest
 
 import oracle as O
-from dit_synth import BlockDims, round_bf16
-from helpers import FP8_MAX_BOUND, gpu_weights, inputs, oracle_weights, rel_err, rms_err, to_numpy, torch_act
+from cases import CTRL_BF16, CTRL_F32, CTRL_FP8, CTRL_STACK, HIST, HIST_STACK, LONG_VIDEO
+from dit_synth import round_bf16
+from helpers import check_parity, gpu_weights, inputs, oracle_weights, rel_err, to_numpy, torch_act
 
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 V = pytest.importorskip("video_diffusion_transformer_flash_amd")
 
-TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 6e-2}
-
-CTRL_BF16 = BlockDims("ctrl_bf16", d_model=512, n_heads=4, head_dim=128, d_ffn=1024, T=2, H=9, W=15, n_text=16,
-                      n_audio=8, rope=(32, 48, 48), dtype="bf16", seed=11, n_ctrl=2, ctrl_offset=3)
-CTRL_F32 = BlockDims("ctrl_f32", d_model=256, n_heads=4, head_dim=64, d_ffn=704, T=2, H=9, W=15, n_text=16,
-                     n_audio=8, rope=(16, 24, 24), dtype="f32", seed=12, n_ctrl=1, ctrl_offset=2)
-CONFIGS = {"bf16": CTRL_BF16, "fp8": CTRL_BF16.with_(name="ctrl_fp8", dtype="fp8", seed=13), "f32": CTRL_F32}
+CONFIGS = {"bf16": CTRL_BF16, "fp8": CTRL_FP8, "f32": CTRL_F32}
 
 
 def run_gpu(d, x, w, compress):
@@ -36,14 +31,8 @@ def run_gpu(d, x, w, compress):
     return [to_numpy(yt), to_numpy(yv), to_numpy(ya), to_numpy(yc)]
 
 
-def check(got, ref, dtype):
-    err, rerr = rel_err(got, ref), rms_err(got, ref)
-    print(f"  max|err|/rms = {err:.3e}, rms err = {rerr:.3e} (bar {TOL[dtype]})")
-    assert np.all(np.isfinite(np.concatenate([g.ravel() for g in got])))
-    if dtype == "fp8":
-        assert rerr <= TOL["fp8"] and err <= FP8_MAX_BOUND
-    else:
-        assert err <= TOL[dtype]
+def check(got, ref, dtype, case=None):
+    check_parity(got, ref, dtype, case if dtype == "fp8" else None)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
@@ -55,7 +44,7 @@ def test_ctrl_block_vs_oracle(dtype, compress):
     got = run_gpu(d, x, w, compress)
     ref = O.block_forward(x["x_text"], x["x_video"], x["x_audio"], oracle_weights(w, dtype), d, compress,
                           x_ctrl=x["x_ctrl"])
-    check(got, list(ref), dtype)
+    check(got, list(ref), dtype, f"ctrl_fp8_{'on' if compress else 'off'}")
 
 
 def test_ctrl_block_is_plain_block_over_control_then_video_on_gpu():
@@ -77,7 +66,7 @@ def test_ctrl_block_is_plain_block_over_control_then_video_on_gpu():
 
 
 def test_ctrl_stack_vs_oracle():
-    d = CTRL_BF16.with_(name="ctrl_stack", d_model=256, n_heads=2, d_ffn=512, seed=14)
+    d = CTRL_STACK
     flags = [0, 1, 1, 0]
     tv, ta = O.flow_schedule(3, 12.0), O.flow_schedule(3, 3.0)
     print(f"ctrl stack flags={flags}", flush=True)
@@ -93,9 +82,7 @@ def test_ctrl_stack_vs_oracle():
     assert np.array_equal(to_numpy(xc), xc0)   # control frames are inputs only
     ref = O.stack_sample(x["x_text"], x["x_video"], x["x_audio"], [oracle_weights(lw, "bf16") for lw in layers], flags,
                          tv.astype(np.float32), ta.astype(np.float32), d, x_ctrl=x["x_ctrl"])
-    err = rel_err([to_numpy(xv), to_numpy(xa)], list(ref))
-    print(f"  max|err|/rms = {err:.3e}")
-    assert err <= 6e-2
+    check_parity([to_numpy(xv), to_numpy(xa)], list(ref), "bf16", "ctrl_stack_bf16")
 
 
 # ---------------------------------------------------------------- bounded long-video history
@@ -104,9 +91,6 @@ def test_history_index_bit_exact(n_hist, H, W):
     got = V.history_index(n_hist, H, W)
     torch.cuda.synchronize()
     assert np.array_equal(got.cpu().numpy(), O.history_index(n_hist, H, W))
-
-
-HIST = CTRL_BF16.with_(name="hist_bf16", n_ctrl=12, ctrl_offset=12, seed=15)
 
 
 def run_gpu_hist(d, x, w, compress):
@@ -132,11 +116,11 @@ def test_history_block_vs_oracle(dtype, compress):
     got = run_gpu_hist(d, x, w, compress)
     ref = O.block_forward(x["x_text"], x["x_video"], x["x_audio"], oracle_weights(w, dtype), d, compress,
                           x_ctrl=x["x_ctrl"], ctrl_idx=O.history_index(d.n_ctrl, d.H, d.W))
-    check(got, list(ref), dtype)
+    check(got, list(ref), dtype, f"hist_fp8_{'on' if compress else 'off'}")
 
 
 def test_history_stack_vs_oracle():
-    d = HIST.with_(name="hist_stack", d_model=256, n_heads=2, d_ffn=512, n_ctrl=5, ctrl_offset=5, seed=16)
+    d = HIST_STACK
     flags = [0, 1, 0]
     tv = O.flow_schedule(3, 12.0)
     print(f"history stack flags={flags}", flush=True)
@@ -152,9 +136,7 @@ def test_history_stack_vs_oracle():
     ref = O.stack_sample(x["x_text"], x["x_video"], x["x_audio"], [oracle_weights(lw, "bf16") for lw in layers], flags,
                          tv.astype(np.float32), None, d, x_ctrl=x["x_ctrl"],
                          ctrl_idx=O.history_index(d.n_ctrl, d.H, d.W))
-    err = rel_err([to_numpy(xv), to_numpy(xa)], list(ref))
-    print(f"  max|err|/rms = {err:.3e}")
-    assert err <= 6e-2
+    check_parity([to_numpy(xv), to_numpy(xa)], list(ref), "bf16", "hist_stack_bf16")
 
 
 # ---------------------------------------------------------------- chunk-by-chunk long video
@@ -162,8 +144,7 @@ def test_long_video_vs_oracle():
     """5 chunks of 3 frames (the first; then a boundary frame held fixed and
     2 new frames, with up to 8 history frames read through the bounded
     selection), 4 layers (2 compressed), 3 evaluations."""
-    d = CTRL_BF16.with_(name="long_video", d_model=256, n_heads=2, d_ffn=512, T=3, H=8, W=12, n_ctrl=0,
-                        ctrl_offset=0, seed=17)
+    d = LONG_VIDEO
     flags = [0, 1, 1, 0]
     tv, ta = O.flow_schedule(3, 12.0), O.flow_schedule(3, 3.0)
     x, _ = inputs(d)
@@ -188,6 +169,4 @@ def test_long_video_vs_oracle():
     assert np.array_equal(to_numpy(frames[:d.T]), to_numpy(f0))
     ref_f, ref_a = O.long_video_sample(x["x_text"], first, new, audio, [oracle_weights(lw, "bf16") for lw in layers],
                                        flags, tv.astype(np.float32), ta.astype(np.float32), d)
-    err = rel_err([to_numpy(frames)] + [to_numpy(a) for a in ga], [ref_f] + list(ref_a))
-    print(f"  max|err|/rms = {err:.3e}")
-    assert err <= 6e-2
+    check_parity([to_numpy(frames)] + [to_numpy(a) for a in ga], [ref_f] + list(ref_a), "bf16", "long_video_bf16")

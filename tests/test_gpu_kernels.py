@@ -1,0 +1,163 @@
+"""Kernel-level GPU parity through the C ABI: the normalisation step (bf16
+and e4m3 outputs) and the projection with its residual (bf16 and e4m3
+operands; the 128 x 128, 256 x 256 and K-split tile paths), each against the
+oracle's own step, and attention at the 540p sequence lengths.
+
+Bars come from the arithmetic of each step:
+  * norm: the sum of squares is an fp32 sum of positive terms (84 per lane
+    and a 6-level wave reduction at width 5376), relative error under 90 u
+    (u = 2^-24), which the square root halves; the row factor, the output
+    and the scaled value for the e4m3 code then take a few more roundings:
+    under 128 u in all. bf16 out: that value rounded once to bf16 (8
+    significant bits, unit roundoff 2^-8), so |gpu - n| <= (2^-8 + 128 u) |n|;
+  * norm, e4m3 out: an e4m3 code is an integer decided by floating point.
+    Every code whose exact scaled value lies more than 2^-16 (relative) from
+    an e4m3 rounding boundary is unique and must equal the oracle's; at the
+    few values closer to a boundary either neighbouring code is correct;
+  * projection: products of bf16 or e4m3 values are exact in fp32, so fp32
+    accumulation over K terms errs by at most gamma_K = K u / (1 - K u)
+    (u = 2^-24) times sum_k |a_k w_k|, plus the scale product and the
+    residual add (3 u |h|). The matrix cores meet that bound for bf16. Their
+    e4m3 dot products (64 products per instruction) sum below fp32
+    round-to-nearest precision: on codes drawn over the whole e4m3 range
+    the error reached 10 x that bound (7.7e-5 of the output RMS), so the e4m3
+    bar is 32 x gamma_K; a wrong operand, scale or K slice errs by the
+    output's own size."""
+import numpy as np
+import pytest
+
+import oracle as O
+from dit_synth import round_bf16
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+V = pytest.importorskip("video_diffusion_transformer_flash_amd")
+
+U = 2.0 ** -24
+
+
+def dev(a, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+@pytest.mark.parametrize("in_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("M,D", [(1, 64), (37, 512), (3736, 5376)])
+def test_rmsnorm_bf16_out(in_dtype, M, D):
+    g = np.random.default_rng(M + D)
+    x = g.standard_normal((M, D)).astype(np.float32) * g.uniform(0.1, 10, (M, 1)).astype(np.float32)
+    if in_dtype == "bf16":
+        x = round_bf16(x)
+    gain = round_bf16((1 + np.sqrt(0.1) * g.standard_normal(D)).astype(np.float32))
+    out = V.rmsnorm(dev(x, in_dtype), dev(gain, "bf16"), 1e-6, "bf16").float().cpu().numpy().astype(np.float64)
+    ref = O.rmsnorm(x.astype(np.float64), gain.astype(np.float64), 1e-6)
+    assert np.all(np.abs(out - ref) <= (2.0 ** -8 + 128 * U) * np.abs(ref) + 1e-30)
+
+
+@pytest.mark.parametrize("M,D", [(37, 512), (3736, 5376)])
+def test_rmsnorm_f32(M, D):
+    g = np.random.default_rng(7 * M + D)
+    x = g.standard_normal((M, D)).astype(np.float32)
+    gain = (1 + np.sqrt(0.1) * g.standard_normal(D)).astype(np.float32)
+    out = V.rmsnorm(dev(x, "f32"), dev(gain, "f32"), 1e-6).cpu().numpy().astype(np.float64)
+    ref = O.rmsnorm(x.astype(np.float64), gain.astype(np.float64), 1e-6)
+    assert np.all(np.abs(out - ref) <= 128 * U * np.abs(ref) + 1e-30)
+
+
+def _e4m3_boundaries():
+    vals = np.sort(np.abs(O.e4m3_decode(np.arange(0, 127, dtype=np.uint8))))
+    return (vals[1:] + vals[:-1]) / 2
+
+
+@pytest.mark.parametrize("in_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("M,D", [(37, 512), (3736, 5376), (12628, 5376)])
+def test_rmsnorm_fp8_codes(in_dtype, M, D):
+    g = np.random.default_rng(3 * M + D)
+    x = g.standard_normal((M, D)).astype(np.float32)
+    if in_dtype == "bf16":
+        x = round_bf16(x)
+    gain = round_bf16((1 + np.sqrt(0.1) * g.standard_normal(D)).astype(np.float32))
+    codes, rinv, amax = V.rmsnorm(dev(x, in_dtype), dev(gain, "bf16"), 1e-6, "fp8")
+    codes = codes.cpu().numpy()
+    rinv, amax = rinv.cpu().numpy().astype(np.float64), float(amax.item())
+    x64 = x.astype(np.float64)
+    ref_rinv = 1.0 / np.sqrt(np.mean(x64 * x64, axis=1) + 1e-6)
+    assert np.max(np.abs(rinv - ref_rinv) / ref_rinv) <= 64 * U
+    n = O.rmsnorm(x64, gain.astype(np.float64), 1e-6)
+    ref_amax = float(np.abs(n).max())
+    assert abs(amax - ref_amax) <= 128 * U * ref_amax
+    # the oracle's codes, decided in fp32 (the precision the kernel quantises from)
+    vals, s = O.fp8.quantize_act_fp8(n, "f32")
+    gv = O.e4m3_decode(codes)
+    z = np.abs(n) * (448.0 / ref_amax)                     # exact scaled magnitude
+    bnd = _e4m3_boundaries()
+    j = np.clip(np.searchsorted(bnd, z), 1, len(bnd) - 1)
+    near = np.minimum(np.abs(z - bnd[j - 1]), np.abs(z - bnd[j])) <= 2.0 ** -16 * z
+    unique = ~near
+    assert np.array_equal(gv[unique], vals[unique])
+    # near a boundary: one of the two grid values around the exact one, same sign
+    grid = np.sort(np.abs(O.e4m3_decode(np.arange(0, 127, dtype=np.uint8))))
+    k = np.clip(np.searchsorted(grid, z[near]), 1, len(grid) - 1)
+    ga = np.abs(gv[near])
+    assert np.all((ga == grid[k - 1]) | (ga == grid[k]))
+    assert np.all((gv[near] == 0) | (np.signbit(gv[near]) == np.signbit(n[near])))
+    print(f"rmsnorm fp8 {in_dtype} {M}x{D}: {int(unique.sum())} unique codes equal, {int(near.sum())} at a boundary")
+
+
+def _proj_case(M, N, K, dtype, seed):
+    g = np.random.default_rng(seed)
+    xres = round_bf16(g.standard_normal((M, N)).astype(np.float32))
+    if dtype == "bf16":
+        a = round_bf16(g.standard_normal((M, K)).astype(np.float32))
+        w = round_bf16((g.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32))
+        h = V.project_residual(dev(xres, "bf16"), dev(a, "bf16"), dev(w, "bf16")).cpu().numpy()
+        a64, w64 = a.astype(np.float64), w.astype(np.float64)
+        scale = 1.0
+    else:
+        valid = np.concatenate([np.arange(0, 0x7F), np.arange(0x80, 0xFF)]).astype(np.uint8)   # no NaN codes
+        ac = valid[g.integers(0, len(valid), (M, K))]
+        wc = valid[g.integers(0, len(valid), (N, K))]
+        amax = np.float32(3.7)
+        ws = np.float32(1.3e-4)
+        t = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
+        h = V.project_residual(dev(xres, "bf16"), t(ac), t(wc), a_amax=t(np.array([amax])),
+                               w_scale=t(np.array([ws]))).cpu().numpy()
+        a64, w64 = O.e4m3_decode(ac), O.e4m3_decode(wc)
+        scale = float(amax) / 448.0 * float(ws)
+    acc = a64 @ w64.T
+    ref = xres.astype(np.float64) + scale * acc
+    slack = 1.0 if dtype == "bf16" else 32.0
+    bound = slack * (K * U / (1 - K * U)) * scale * (np.abs(a64) @ np.abs(w64).T) + 3 * U * np.abs(ref) + 1e-30
+    return h.astype(np.float64), ref, bound
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("M,N,K", [(200, 384, 512),        # 128 x 128 tiles, ragged token tail
+                                   (2048, 16384, 256),     # 256 x 256 tiles (512 of them)
+                                   (3736, 5376, 7168)])    # the 540p compressed O projection: K-split tail
+def test_project_residual(dtype, M, N, K):
+    h, ref, bound = _proj_case(M, N, K, dtype, M + N + K)
+    err = np.abs(h - ref)
+    print(f"project {dtype} {M}x{N}x{K}: max err / bound {np.max(err / bound):.3f}, "
+          f"max|err|/rms {err.max() / np.sqrt(np.mean(ref ** 2)):.2e}")
+    assert np.all(err <= bound)
+
+
+@pytest.mark.parametrize("S", [3736, 12628])
+@pytest.mark.parametrize("sharp", [1.0, 8.0])
+def test_attention_at_540p_lengths(S, sharp):
+    """bf16 attention over the 540p joint sequences (compressed and not), 2
+    heads, with and without sharp logits (q x 8). Bar as in the standalone
+    test: 3e-2 (bf16 P and output, each 2^-9 relative)."""
+    nh, dh = 2, 128
+    g = np.random.default_rng(S + int(sharp))
+    q, k, v = (round_bf16(g.standard_normal((S, nh * dh)).astype(np.float32)) for _ in range(3))
+    q = round_bf16(q * np.float32(sharp))
+    tt = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)  # noqa: E731
+    out = V.attention(tt(q), tt(k), tt(v), nh, 1.0 / np.sqrt(dh)).float().cpu().numpy()
+    ref = O.attention(q.reshape(S, nh, dh).astype(np.float64), k.reshape(S, nh, dh).astype(np.float64),
+                      v.reshape(S, nh, dh).astype(np.float64)).reshape(S, nh * dh)
+    err = np.max(np.abs(out - ref)) / np.sqrt(np.mean(ref ** 2))
+    print(f"attention S={S} sharp={sharp}: {err:.2e}")
+    assert err <= 3e-2

@@ -15,9 +15,9 @@ from . import _lib
 from ._lib import DIT_BF16, DIT_F32, DIT_FP8_E4M3, BlockWeights, Dims, DitError, check  # noqa: F401
 
 __all__ = ["Dims", "make_dims", "keep_dims", "keep_index", "nearest_kept_map", "block_workspace_size",
-           "block_forward", "stack_workspace_size", "stack_sample", "quantize_fp8", "gather_kept",
-           "broadcast_residual", "attention", "history_index", "long_video_sample", "trace_enable", "trace_records",
-           "DitError"]
+           "block_forward", "stack_workspace_size", "stack_sample", "quantize_fp8",
+           "gather_kept", "broadcast_residual", "attention", "rmsnorm", "project_residual", "history_index",
+           "long_video_sample", "trace_enable", "trace_records", "DitError"]
 
 _ACT = {"f32": DIT_F32, "bf16": DIT_BF16, "fp8": DIT_BF16}
 _WT = {"f32": DIT_F32, "bf16": DIT_BF16, "fp8": DIT_FP8_E4M3}
@@ -234,6 +234,44 @@ def attention(q, k, v, n_heads: int, scale: float, out=None, ws=None):
         out = torch.empty_like(q)
     check(lib().dit_attention(S, n_heads, hd, dt, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ws),
                               ws.numel(), _stream()), "dit_attention")
+    return out
+
+
+_DT = {torch.float32: DIT_F32, torch.bfloat16: DIT_BF16, torch.uint8: DIT_FP8_E4M3}
+
+
+def rmsnorm(x, g, eps: float, out_dtype: str = "same"):
+    """RMSNorm of the rows of x [M, D] with gains g [D]. out_dtype "same" /
+    "bf16" / "fp8"; fp8 returns (codes uint8 [M, D], rinv [M], amax [1])."""
+    M, D = x.shape
+    odt = {"same": _DT[x.dtype], "bf16": DIT_BF16, "fp8": DIT_FP8_E4M3}[out_dtype]
+    if odt == DIT_FP8_E4M3:
+        out = torch.empty((M, D), dtype=torch.uint8, device=x.device)
+        rinv = torch.empty(M, dtype=torch.float32, device=x.device)
+        amax = torch.empty(1, dtype=torch.float32, device=x.device)
+    else:
+        out = torch.empty((M, D), dtype=_TORCH[odt], device=x.device)
+        rinv = amax = None
+    check(lib().dit_rmsnorm(M, D, _DT[x.dtype], odt, _ptr(x), _ptr(g), float(eps), _ptr(out), _ptr(rinv), _ptr(amax),
+                            _stream()), "dit_rmsnorm")
+    return (out, rinv, amax) if odt == DIT_FP8_E4M3 else out
+
+
+def project_residual(x_res, a, w, a_amax=None, w_scale=None, out=None, ws=None):
+    """h = x_res + s * a w^T in fp32 (a, w bf16, or uint8 e4m3 codes with
+    device scales a_amax / 448 and w_scale)."""
+    M, K = a.shape
+    N = w.shape[0]
+    dt = _DT[a.dtype]
+    n = ctypes.c_size_t()
+    check(lib().dit_project_residual_workspace_size(M, N, K, dt, ctypes.byref(n)),
+          "dit_project_residual_workspace_size")
+    if ws is None:
+        ws = workspace(n.value)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    check(lib().dit_project_residual(M, N, K, dt, _ptr(x_res), _ptr(a), _ptr(a_amax), _ptr(w), _ptr(w_scale),
+                                     _ptr(out), _ptr(ws), ws.numel(), _stream()), "dit_project_residual")
     return out
 
 

@@ -51,6 +51,10 @@ SIGNATURES = {
     "dit_broadcast_residual": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "dit_attention_workspace_size": (c_i32, [c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_size)]),
     "dit_attention": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "dit_rmsnorm": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_f32, c_vp, c_vp, c_vp, c_vp]),
+    "dit_project_residual_workspace_size": (c_i32, [c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_size)]),
+    "dit_project_residual": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size,
+                                     c_vp]),
     "dit_trace_enable": (c_i32, [c_i32]),
     "dit_trace_count": (c_i32, []),
     "dit_trace_read": (c_i32, [c_i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(c_f32)]),

@@ -22,7 +22,8 @@ CFLAGS = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(HERE, "..", "include")]
 
-SOURCES = ["api.hip", "rowops.hip", "gemm_mfma.hip", "gemm_f32.hip", "attention.hip"]
+# every HIP source of csrc/, in a fixed order
+SOURCES = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> str:

@@ -67,6 +67,8 @@ int keep_count(int n, int s) { return (n + s - 1) / s + (((n - 1) % s) != 0 ? 1 
 
 int esize(int dt) { return dt == DIT_F32 ? 4 : (dt == DIT_BF16 ? 2 : 1); }
 
+
+
 int validate_dims(const dit_dims* d) {
     if (!d) return DIT_EINVAL;
     if (d->T < 1 || d->H < 1 || d->W < 1 || d->n_text < 0 || d->n_audio < 0 || d->stride < 1) return DIT_EINVAL;
@@ -196,6 +198,7 @@ int run_block(const dit_dims& d, const dit_block_weights& w, const SeqIn& in, co
     ep.hres = h;
     ep.out = out;
     ep.refin = refin;
+    ep.kg = KeepGeom{d.H, d.W, keep_count(d.H, d.stride), keep_count(d.W, d.stride), d.stride};
     ep.part = P.part_bytes ? (float*)(ws + P.part) : nullptr;
     ep.part_bytes = P.part_bytes;
 
@@ -374,8 +377,14 @@ int32_t dit_block_workspace_size(const dit_dims* dims, int32_t compress_on, size
     return DIT_OK;
 }
 
-namespace {
+}  // extern "C"
 
+namespace dit {
+
+void set_last_hip(int e) { g_last_hip = e; }
+
+// dit_block_forward / dit_block_forward_ctrl after their dims check, on a
+// caller-provided workspace (also used by the entry points of other files)
 int block_forward_impl(const dit_dims* dims, const void* x_text, const void* x_video, const void* x_ctrl,
                        const int32_t* ctrl_idx, int32_t n_ctrl_tok, const void* x_audio,
                        const dit_block_weights* weights, int32_t compress_on, const int32_t* keep, const int32_t* nk,
@@ -401,19 +410,25 @@ int block_forward_impl(const dit_dims* dims, const void* x_text, const void* x_v
 
     SeqIn in{x_text,   x_video, x_ctrl, x_audio, compress_on ? keep : nullptr, ctrl_idx, d.n_text,
              compress_on ? nkept : nv, nc, d.n_audio};
-    SeqOut out{y_text, y_video, y_ctrl, y_audio, compress_on ? (float*)(w8 + P.delta) : nullptr, nullptr, nullptr};
+    // compressed: the MFMA path adds each kept row's update onto its video
+    // positions in the down projection's epilogue; the fp32 path writes the
+    // updates and broadcasts them in a pass of its own
+    const bool fused = compress_on && d.act_dtype != DIT_F32;
+    SeqOut out{y_text, y_video, y_ctrl, y_audio, compress_on ? (float*)(w8 + P.delta) : nullptr,
+               fused ? x_video : nullptr, fused ? y_video : nullptr};
     r = run_block(d, *weights, in, compress_on ? keep : nullptr, ctrl_idx, out, in, w8, P, st);
     if (r) return r;
-    if (compress_on) {
+    if (compress_on && !fused) {
         TR("broadcast_residual");
-        HIPCHK(broadcast_residual_launch(d.act_dtype == DIT_BF16, x_video, (const float*)(w8 + P.delta), nk, y_video, nv,
-                                         d.d_model, st));
+        HIPCHK(broadcast_residual_launch(false, x_video, (const float*)(w8 + P.delta), nk, y_video, nv, d.d_model, st));
     }
     TR("end");
     return DIT_OK;
 }
 
-}  // namespace
+}  // namespace dit
+
+extern "C" {
 
 int32_t dit_block_forward(const dit_dims* dims, const void* x_text, const void* x_video, const void* x_audio,
                           const dit_block_weights* weights, int32_t compress_on, const int32_t* keep,
@@ -530,12 +545,17 @@ int stack_impl(const dit_dims* dims, const dit_block_weights* layers_host, int32
             const SeqIn packed{Zct, Zcv, Zck, Zca, nullptr, nullptr, nt, nkept, nc, na};
             for (int i = l; i < e; ++i) {
                 const SeqIn& in = (i == l) ? start : packed;
+                // the span's last layer adds the summed update onto every
+                // position of the full-resolution state (in its epilogue on
+                // the MFMA path, in a pass of its own for fp32)
                 SeqOut out = (i + 1 < e) ? SeqOut{Zct, Zcv, Zck, Zca, nullptr, nullptr, nullptr}
-                                         : SeqOut{Zt, nullptr, Zk, Za, delta, nullptr, nullptr};
+                                         : SeqOut{Zt, nullptr, Zk, Za, delta, bf ? cur.xv : nullptr, bf ? Zv : nullptr};
                 if ((r = run_block(d, layers_host[i], in, keep, ctrl_idx, out, start, bws, Pc, st))) return r;
             }
-            TR("broadcast_residual");
-            HIPCHK(broadcast_residual_launch(bf, cur.xv, delta, nk, Zv, nv, (int)D, st));
+            if (!bf) {
+                TR("broadcast_residual");
+                HIPCHK(broadcast_residual_launch(false, cur.xv, delta, nk, Zv, nv, (int)D, st));
+            }
             cur = state;
             l = e;
         }
@@ -612,6 +632,61 @@ int32_t dit_broadcast_residual(int32_t n_video, int32_t n_kept, int32_t D, int32
     if (dtype != DIT_F32 && dtype != DIT_BF16) return DIT_EUNSUPPORTED;
     if (n_video == 0) return DIT_OK;
     HIPCHK(broadcast_residual_launch(dtype == DIT_BF16, x_video, delta, nk, out, n_video, D, (hipStream_t)stream));
+    return DIT_OK;
+}
+
+int32_t dit_rmsnorm(int32_t M, int32_t D, int32_t in_dtype, int32_t out_dtype, const void* x, const void* g, float eps,
+                    void* out, float* rinv, float* amax, void* stream) {
+    if (M < 0 || D < 64 || D % 64 || !x || !g || !out || !aligned16(x) || !aligned16(g) || !aligned16(out)) return DIT_EINVAL;
+    if (!(eps >= 0.f)) return DIT_EINVAL;
+    const bool f32 = in_dtype == DIT_F32 && out_dtype == DIT_F32;
+    const bool bf = (in_dtype == DIT_BF16 || in_dtype == DIT_F32) && out_dtype == DIT_BF16;
+    const bool f8 = (in_dtype == DIT_BF16 || in_dtype == DIT_F32) && out_dtype == DIT_FP8_E4M3;
+    if (!(f32 || bf || f8)) return DIT_EUNSUPPORTED;
+    if (f8 && (!rinv || !amax || ((uintptr_t)rinv & 3) || ((uintptr_t)amax & 3))) return DIT_EINVAL;
+    if (M == 0) return DIT_OK;
+    hipStream_t st = (hipStream_t)stream;
+    // rows of a bf16 tensor go through the sequence reader (one segment), fp32 rows through the dense one
+    const bool seq = in_dtype == DIT_BF16 || f32;
+    const SeqIn in{x, nullptr, nullptr, nullptr, nullptr, nullptr, M, 0, 0, 0};
+    const float* dense = seq ? nullptr : (const float*)x;
+    if (f8) {
+        HIPCHK(fill_launch(amax, 1, 0.f, st));
+        HIPCHK(rmsnorm_fp8_launch(seq, in, dense, g, (uint8_t*)out, rinv, amax, M, D, eps, st));
+    } else {
+        HIPCHK(rmsnorm_launch(f32 ? DIT_F32 : DIT_BF16, seq, in, dense, g, out, M, D, eps, st));
+    }
+    return DIT_OK;
+}
+
+int32_t dit_project_residual_workspace_size(int32_t M, int32_t N, int32_t K, int32_t a_dtype, size_t* bytes) {
+    if (M < 0 || N < 128 || K < 128 || N % 128 || K % 128 || !bytes) return DIT_EINVAL;
+    if (a_dtype != DIT_BF16 && a_dtype != DIT_FP8_E4M3) return DIT_EUNSUPPORTED;
+    *bytes = std::max<size_t>(256, gemm_split_bytes_bound(M, N));
+    return DIT_OK;
+}
+
+int32_t dit_project_residual(int32_t M, int32_t N, int32_t K, int32_t a_dtype, const void* x_res, const void* a,
+                             const float* a_amax, const void* w, const float* w_scale, float* h, void* ws,
+                             size_t ws_bytes, void* stream) {
+    size_t need = 0;
+    int r = dit_project_residual_workspace_size(M, N, K, a_dtype, &need);
+    if (r) return r;
+    const bool fp8 = a_dtype == DIT_FP8_E4M3;
+    if (!x_res || !a || !w || !h || !aligned16(x_res) || !aligned16(a) || !aligned16(w) || !aligned16(h)) return DIT_EINVAL;
+    if (fp8 && (!a_amax || !w_scale)) return DIT_EINVAL;
+    if (!ws || ((uintptr_t)ws & 255)) return DIT_EINVAL;
+    if (ws_bytes < need) return DIT_EWORKSPACE;
+    if (M == 0) return DIT_OK;
+    EpiParams ep{};
+    ep.M = M; ep.Mpad = M; ep.D = N; ep.I = K; ep.F = K; ep.dh = 128;
+    ep.xin = SeqIn{x_res, nullptr, nullptr, nullptr, nullptr, nullptr, M, 0, 0, 0};
+    ep.h = h;
+    ep.amax_a = fp8 ? a_amax : nullptr;
+    ep.s_w = fp8 ? w_scale : nullptr;
+    ep.part = (float*)ws;
+    ep.part_bytes = gemm_split_bytes_bound(M, N);
+    HIPCHK(gemm_mfma(fp8, EPI_RESID, a, w, nullptr, M, N, K, ep, (hipStream_t)stream));
     return DIT_OK;
 }
 

@@ -82,17 +82,35 @@ struct SeqIn {
 };
 
 // Output rows of the block. With delta != nullptr the video rows are not
-// written to yv; instead delta[j] = y_j - ref_j (fp32) with ref_j the row
-// ref_v[ref_idx[j]] (ref_idx nullptr: j) of act dtype.
+// written to yv: their update y_j - ref_j (fp32; ref_j the row of the
+// reference sequence) either goes to delta[j], or, with bout set, straight to
+// every video position p whose nearest kept slot is j: bout[p] = bx[p] +
+// update (the nearest-kept broadcast with the full-resolution residual).
 struct SeqOut {
     void* yt;
     void* yv;
     void* yc;
     void* ya;
     float* delta;
-    const void* ref_v;
-    const int32_t* ref_idx;
+    const void* bx;        // full-resolution video input [T][H][W][D] of the broadcast
+    void* bout;            // its output (may be bx itself)
 };
+
+// The compression's grid: kept slot j is (t, a, b) in raster order over
+// [T][Hk][Wk]; along an axis of n the a-th kept index is min(a s, n - 1).
+struct KeepGeom {
+    int H, W, Hk, Wk, s;
+};
+
+// Positions r of an axis of length n (kept indices min(a s, n - 1), nk of
+// them) whose nearest kept index (ties to the lower) is the a-th one: the
+// interval [lo, hi]. Between kept k and k' the midpoint floor((k + k') / 2)
+// still goes to k.
+DIT_DEV void kept_preimage(int a, int n, int s, int nk, int& lo, int& hi) {
+    const int k = min(a * s, n - 1);
+    lo = a == 0 ? 0 : (min((a - 1) * s, n - 1) + k) / 2 + 1;
+    hi = a == nk - 1 ? n - 1 : (k + min((a + 1) * s, n - 1)) / 2;
+}
 
 // Rotary geometry: per-token coordinates and fp32 (cos, sin) tables per band.
 struct Rope {

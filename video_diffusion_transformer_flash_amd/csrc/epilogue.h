@@ -12,7 +12,10 @@
 //   SWIGLU: u = silu(gate) * up, with the running |u| max for fp8 (then u
 //           is kept in fp32 until its quantisation);
 //   DOWN  : y = h + acc to the text / video / audio outputs, or for kept video
-//           rows of a compressed block delta = y - X_ref in fp32.
+//           rows of a compressed block the update y - X_ref: in fp32 to a
+//           buffer, or (MFMA kernels) added straight onto every video
+//           position whose nearest kept slot is that row (the broadcast with
+//           the full-resolution residual, fused).
 #pragma once
 
 #include <type_traits>
@@ -47,6 +50,7 @@ struct EpiParams {
     const float* hres;
     SeqOut out;
     SeqIn refin;            // reference rows for delta (video segment only)
+    KeepGeom kg;            // the compression's grid (broadcast into out.bout)
     // RESID / DOWN: fp32 partial tiles of K-split tail tiles (nullptr or too
     // small: no split)
     float* part;
@@ -253,6 +257,49 @@ DIT_DEV float epi8_swiglu(const EpiParams& p, int m, int f0, const float g[8], c
     return mx;
 }
 
+// the update d of kept slot j (eight outputs from n0) onto every video
+// position whose nearest kept slot is j: bout[p] = bx[p] + d (a rectangle of
+// at most 2 x 2 positions at stride 2; loads first, then stores)
+template <typename T>
+DIT_DEV void bcast8(const EpiParams& p, int j, int n0, const float d[8]) {
+    const KeepGeom& g = p.kg;
+    const int per = g.Hk * g.Wk;
+    const int t = j / per, r = j - t * per, a = r / g.Wk, b = r - a * g.Wk;
+    int h0, h1, w0, w1;
+    kept_preimage(a, g.H, g.s, g.Hk, h0, h1);
+    kept_preimage(b, g.W, g.s, g.Wk, w0, w1);
+    const T* x = (const T*)p.out.bx;
+    T* out = (T*)p.out.bout;
+    const size_t base = (size_t)t * g.H * g.W;
+    if (h1 - h0 <= 1 && w1 - w0 <= 1) {
+        float v[4][8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int h = h0 + (q >> 1), w = w0 + (q & 1);
+            if (h <= h1 && w <= w1) load8<T>(x + (base + (size_t)h * g.W + w) * p.D + n0, v[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int h = h0 + (q >> 1), w = w0 + (q & 1);
+            if (h <= h1 && w <= w1) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[q][i] += d[i];
+                store8<T>(out + (base + (size_t)h * g.W + w) * p.D + n0, v[q]);
+            }
+        }
+        return;
+    }
+    for (int h = h0; h <= h1; ++h)
+        for (int w = w0; w <= w1; ++w) {
+            const size_t off = (base + (size_t)h * g.W + w) * p.D + n0;
+            float v[8];
+            load8<T>(x + off, v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] += d[i];
+            store8<T>(out + off, v);
+        }
+}
+
 template <typename T>
 DIT_DEV void epi8_down(const EpiParams& p, int m, int n0, const float v[8]) {
     if (m >= p.M) return;
@@ -271,7 +318,8 @@ DIT_DEV void epi8_down(const EpiParams& p, int m, int n0, const float v[8]) {
             load8<T>(seq_row<T>(p.refin, m, p.D) + n0, x);
 #pragma unroll
             for (int i = 0; i < 8; ++i) y[i] -= x[i];
-            store8<float>(o.delta + (size_t)j * p.D + n0, y);
+            if (o.bout) bcast8<T>(p, j, n0, y);
+            else store8<float>(o.delta + (size_t)j * p.D + n0, y);
         } else {
             store8<T>((T*)o.yv + (size_t)j * p.D + n0, y);
         }

@@ -50,6 +50,15 @@ hipError_t attention_bf16(const void* Q, const void* K, const void* Vt, void* O,
                           float c, float* o_amax, hipStream_t st);
 hipError_t attention_f32(const void* Q, const void* K, const void* Vt, void* O, int S, int Sp, int nh, int dh,
                          float c, hipStream_t st);
+// record a HIP error for dit_last_hip_error (api.hip)
+void set_last_hip(int e);
+// dit_block_forward(_ctrl) once dims are validated, on workspace `ws` (api.hip)
+int block_forward_impl(const dit_dims* dims, const void* x_text, const void* x_video, const void* x_ctrl,
+                       const int32_t* ctrl_idx, int32_t n_ctrl_tok, const void* x_audio,
+                       const dit_block_weights* weights, int32_t compress_on, const int32_t* keep, const int32_t* nk,
+                       void* y_text, void* y_video, void* y_ctrl, void* y_audio, void* ws, size_t ws_bytes,
+                       void* stream);
+
 hipError_t attention_pack(bool bf16, const void* q, const void* k, const void* v, void* Qp, void* Kp, void* Vtp,
                           int S, int Sp, int nh, int dh, float qscale, hipStream_t st);
 
