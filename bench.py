@@ -81,9 +81,14 @@ def block_flops(d, S):
 def hbm_bytes(d, S, Nv, Nk, es=2):
     """Algorithmic bytes of the bandwidth-bound kernels per launch."""
     D = d.d_model
-    return {"broadcast_residual": (2 * Nv * es + Nk * 4) * D,   # read x (bf16), read delta (fp32), write out
+    return {"broadcast_residual": (2 * Nv + Nk) * D * es,      # read x, read the update once, write out
             "rmsnorm1": 2 * S * D * es,                        # read X rows, write n
             "rmsnorm2": S * D * (4 + es)}                      # read h (fp32), write n
+
+
+def broadcast_bytes_moved(Nv, Nk, D, es=2):
+    """Bytes the standalone broadcast kernel moves: its update rows are fp32."""
+    return (2 * Nv * es + Nk * 4) * D
 
 
 def setup(cfg_name, compress):
@@ -114,7 +119,12 @@ def setup(cfg_name, compress):
     return d, step, S, d.T * Hk * Wk, (x, w)
 
 
-def time_steps(step, steps, warmup, trace=True):
+def time_steps(step, steps, warmup, trace=False):
+    """Warm up, then time exactly `steps` steps between two synchronisations:
+    returns (ms per step over the whole region, median of the per-step times,
+    per-kernel-group (ms, launches) from the library's HIP-event trace when
+    `trace` is on; the trace records an event between kernel groups, so the
+    headline figures come from an untraced run)."""
     import torch
     import video_diffusion_transformer_flash_amd as V
     for _ in range(warmup):
@@ -123,14 +133,16 @@ def time_steps(step, steps, warmup, trace=True):
     if trace:
         V.trace_enable(steps * 24 + 8)
     st = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
-    e0.record(st)
-    for _ in range(steps):
+    ev[0].record(st)
+    for i in range(steps):
         step()
-    e1.record(st)
+        ev[i + 1].record(st)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms = ev[0].elapsed_time(ev[-1]) / steps
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    med = per_step[len(per_step) // 2]
     recs = V.trace_records() if trace else []
     if trace:
         V.trace_enable(0)
@@ -139,7 +151,7 @@ def time_steps(step, steps, warmup, trace=True):
         a = per.setdefault(name, [0.0, 0])
         a[0] += t
         a[1] += 1
-    return ms, {k: (v[0] / v[1], v[1]) for k, v in per.items()}
+    return ms, med, {k: (v[0] / v[1], v[1]) for k, v in per.items()}
 
 
 def kernel_table(kern, flops, bytes_):
@@ -173,7 +185,10 @@ def bandwidth_kernels(d, reps=10):
     flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")   # 1 GiB
     fns = {"gather_kept": lambda: V.gather_kept(x, keep, out=xc),
            "broadcast_residual": lambda: V.broadcast_residual(x, delta, nk, out=out)}
-    byts = {"gather_kept": 2 * Nk * D * 2, "broadcast_residual": (2 * Nv * 2 + Nk * 4) * D}
+    # algorithmic bytes: read each kept row and write it; read x, the update
+    # (counted at 2 bytes per element, once per kept row) and write out
+    byts = {"gather_kept": 2 * Nk * D * 2, "broadcast_residual": (2 * Nv + Nk) * D * 2}
+    moved = {"gather_kept": 2 * Nk * D * 2, "broadcast_residual": broadcast_bytes_moved(Nv, Nk, D)}
     times = {k: [] for k in fns}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for r in range(reps + 2):
@@ -188,7 +203,7 @@ def bandwidth_kernels(d, reps=10):
     # reference: torch's own device copy moving the same bytes (half read, half
     # written) under the same flush
     cref = {}
-    for name, nb in byts.items():
+    for name, nb in moved.items():
         a = torch.ones(nb // 4, dtype=torch.bfloat16, device="cuda")
         b = torch.empty_like(a)
         ts = []
@@ -206,9 +221,11 @@ def bandwidth_kernels(d, reps=10):
     for name, ts in times.items():
         ms = sorted(ts)[len(ts) // 2]
         gbs = byts[name] / (ms * 1e-3) / 1e9
-        cgbs = byts[name] / (cref[name] * 1e-3) / 1e9
+        cgbs = moved[name] / (cref[name] * 1e-3) / 1e9
+        mgbs = moved[name] / (ms * 1e-3) / 1e9
         res[name] = {"ms": round(ms, 4), "bytes": byts[name], "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM, 4),
-                     "torch_copy_same_bytes_GB/s": round(cgbs, 1)}
+                     "bytes_moved": moved[name], "moved_GB/s": round(mgbs, 1),
+                     "moved_frac": round(mgbs / PEAK_HBM, 4), "torch_copy_same_bytes_GB/s": round(cgbs, 1)}
     del flush
     return res
 
@@ -263,7 +280,7 @@ def sweep(steps=2, warmup=1):
                 V.block_forward(dims, x["x_text"], x["x_video"], x["x_audio"], w, comp, keep if comp else None,
                                 nk if comp else None, out=out, ws=ws)
 
-            ms, _ = time_steps(step, steps, warmup, trace=False)
+            ms, _, _ = time_steps(step, steps, warmup)
             S = d.n_text + d.n_audio + (d.T * Hk * Wk if comp else d.n_video)
             tf = sum(block_flops(d, S).values()) / 1e12
             res.append({"T": T, "compress": comp, "tokens": S, "ms": round(ms, 3), "tflop": round(tf, 3),
@@ -343,7 +360,7 @@ def long_video_timing(chunks=4):
             "total_ms": round(sum(times), 1), "outputs_finite": ok}
 
 
-def stack_timing(reps=2):
+def stack_timing(reps=3):
     """The Flash-shaped stack: 42 blocks with fp8 projections (layers 1-2 full,
     3-28 compressed, 29-42 full) on the 540p grid, 3 flow-matching Euler
     evaluations on the fixed schedule t_k = u/(u + s(1-u)), u = k/3 (s = 12
@@ -371,7 +388,7 @@ def stack_timing(reps=2):
         e1.record()
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1))
-    ms = min(ts)
+    ms = sorted(ts)[len(ts) // 2]
     Hk, Wk = V.keep_dims(d.H, d.W, d.stride)
     S_on, S_off = d.n_text + d.n_audio + d.T * Hk * Wk, d.n_text + d.n_audio + d.n_video
     f_on, f_off = block_flops(d, S_on), block_flops(d, S_off)
@@ -451,15 +468,33 @@ def copy_calibration(nbytes=1 << 30, reps=3):
     torch.cuda.synchronize()
 
 
+def cpu_info():
+    """Host cores this process may use and the CPU's identification."""
+    info = {"cores": len(os.sched_getaffinity(0)), "cpu_model": "unknown"}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                k, _, v = line.partition(":")
+                k, v = k.strip(), v.strip()
+                if k == "model name" and info["cpu_model"] == "unknown":
+                    info["cpu_model"] = v
+                elif k in ("cpu family", "model", "stepping") and f"cpu_{k.replace(' ', '_')}" not in info:
+                    info[f"cpu_{k.replace(' ', '_')}"] = v
+                elif not line.strip() and info["cpu_model"] != "unknown":
+                    break
+    except OSError:
+        pass
+    return info
+
+
 def cpu_baseline(d, host, compress):
     """The fp64 oracle on the host cores: one full block of the same workload."""
-    import numpy as np
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+        blas = None
     x, w = host
     ow = O.BlockWeights.from_arrays(w)
     t0 = time.time()
@@ -468,19 +503,12 @@ def cpu_baseline(d, host, compress):
     Hk, Wk = O.keep_dims(d.H, d.W, d.stride)
     S = d.n_text + d.n_audio + (d.T * Hk * Wk if compress else d.n_video)
     tflop = sum(block_flops(d, S).values()) / 1e12
-    cpu = "unknown"
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                cpu = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
-    del np
-    return {"value": round(tflop / dt, 4), "unit": "TFLOP/s", "ms": round(dt * 1e3, 1), "cores": threads,
-            "kind": "oracle", "cpu_model": cpu,
-            "sample": f"one full block of the same workload (S={S}, compression {'on' if compress else 'off'}), "
-                      "fp64 numpy oracle, timed once"}
+    out = {"value": round(tflop / dt, 4), "unit": "TFLOP/s", "ms": round(dt * 1e3, 1)}
+    out.update(cpu_info())
+    out.update({"blas_threads": blas, "kind": "oracle",
+                "sample": f"one full block of the same workload (S={S}, compression {'on' if compress else 'off'}), "
+                          "fp64 numpy oracle, timed once"})
+    return out
 
 
 def main():
@@ -504,7 +532,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
     d, step, S, Nk, host = setup("540p_on", True)
-    ms, kern = time_steps(step, a.steps, a.warmup)
+    ms, med, _ = time_steps(step, a.steps, a.warmup)                 # headline: no trace events
+    ms_tr, _, kern = time_steps(step, a.steps, 1, trace=True)          # per-kernel groups (HIP events)
     flops = block_flops(d, S)
     tflop = sum(flops.values()) / 1e12
     value = tflop / (ms * 1e-3)
@@ -520,10 +549,13 @@ def main():
         "config": {"workload": "Flash DiT block, 540p/22f latent grid 6x34x60, compression on "
                                f"(3348 kept video + 256 text + 132 audio = {S} tokens), broadcast to 12240 positions",
                    "tflop_per_step": round(tflop, 4), "frac_of_bf16_peak": round(value / PEAK_BF16, 4)},
+        "median_step_ms": round(med, 4),
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4),
                      "flop_per_launch": flops[dom], "launch_ms": round(dom_ms, 4), "traffic": traffic_for(dom)},
         "kernels": table,
+        "kernels_note": f"HIP events between kernel groups over a second run of {a.steps} steps "
+                        f"({round(ms_tr, 4)} ms per step with the events)",
     }
     if a.copy_calib:
         copy_calibration()
@@ -532,13 +564,15 @@ def main():
     bc = bw["broadcast_residual"]
     line["hbm_roofline"] = {"bound": "hbm", "kernel": "broadcast_residual", "achieved": bc["GB/s"],
                             "peak": PEAK_HBM, "unit": "GB/s", "frac": bc["frac"], "bytes_per_launch": bc["bytes"],
+                            "bytes_moved": bc["bytes_moved"], "moved_frac": bc["moved_frac"],
                             "launch_ms": bc["ms"], "cache": "L2 and Infinity Cache flushed (1 GiB read) before each launch",
                             "traffic": traffic_for("broadcast_residual")}
     line["bandwidth_kernels"] = bw
     torch.cuda.empty_cache()
     if not a.no_off:
         d2, step2, S2, _, host2 = setup("540p_off", False)
-        ms2, kern2 = time_steps(step2, max(3, a.steps // 2), a.warmup)
+        ms2, _, _ = time_steps(step2, max(3, a.steps // 2), a.warmup)
+        _, _, kern2 = time_steps(step2, max(3, a.steps // 2), 1, trace=True)
         f2 = block_flops(d2, S2)
         tf2 = sum(f2.values()) / 1e12
         line["compress_off"] = {"workload": f"same block, compression off ({S2} tokens)", "ms": round(ms2, 4),

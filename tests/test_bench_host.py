@@ -42,11 +42,13 @@ def test_block_flops(name, compress, tflop):
 
 
 def test_broadcast_bytes():
-    """Broadcast + residual at 540p compressed: read x_video (bf16) and the
-    3348 kept fp32 update rows once, write 12240 bf16 rows."""
+    """Broadcast + residual at 540p compressed: algorithmic bytes read x_video
+    and the 3348 kept update rows once and write 12240 rows, all at 2 bytes
+    (299.2 MB); the standalone kernel's fp32 update rows make it move 335.2 MB."""
     d = CONFIGS["540p_on"]
     S, nk = _tokens(d, True)
     assert (S, nk) == (3736, 3348)
     b = bench.hbm_bytes(d, S, d.n_video, nk)
-    assert b["broadcast_residual"] == (2 * 12240 * 2 + 3348 * 4) * 5376 == 335204352
+    assert b["broadcast_residual"] == (2 * 12240 + 3348) * 5376 * 2 == 299206656
+    assert bench.broadcast_bytes_moved(12240, 3348, 5376) == (2 * 12240 * 2 + 3348 * 4) * 5376 == 335204352
     assert b["rmsnorm1"] == 2 * 3736 * 5376 * 2
