@@ -155,6 +155,18 @@ int32_t dit_block_forward(const dit_dims* dims,
                           void* y_text, void* y_video, void* y_audio,
                           void* ws, size_t ws_bytes, void* stream);
 
+/* dit_block_forward for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * workspace is a static array of the library, 128 MiB on every device the
+ * library runs on, held until the process ends. Blocks whose workspace
+ * (dit_block_workspace_size) exceeds 128 MiB are refused with
+ * DIT_EWORKSPACE before any launch. Uses the current device's array; every
+ * call on a GPU shares it, so calls that overlap on one GPU (other streams or
+ * threads) race. Outputs as dit_block_forward; allocates nothing. */
+int32_t dit_block_forward_noalloc(const dit_dims* dims, const void* x_text, const void* x_video, const void* x_audio,
+                                  const dit_block_weights* weights, int32_t compress_on, const int32_t* keep,
+                                  const int32_t* nk, void* y_text, void* y_video, void* y_audio, void* stream);
+
 /* The same block with control frames [TDH-backbone] (a reference's time
  * coordinate sits a fixed positive constant before the target's), [PD-1]
  * (aligned control frames and targets keep a stable positive time offset).

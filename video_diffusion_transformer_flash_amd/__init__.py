@@ -15,7 +15,7 @@ from . import _lib
 from ._lib import DIT_BF16, DIT_F32, DIT_FP8_E4M3, BlockWeights, Dims, DitError, check  # noqa: F401
 
 __all__ = ["Dims", "make_dims", "keep_dims", "keep_index", "nearest_kept_map", "block_workspace_size",
-           "block_forward", "stack_workspace_size", "stack_sample", "quantize_fp8",
+           "block_forward", "block_forward_noalloc", "stack_workspace_size", "stack_sample", "quantize_fp8",
            "gather_kept", "broadcast_residual", "attention", "rmsnorm", "project_residual", "history_index",
            "long_video_sample", "trace_enable", "trace_records", "DitError"]
 
@@ -123,6 +123,21 @@ def block_forward(dims: Dims, x_text, x_video, x_audio, weights: dict, compress:
                                           _ptr(out[0]), _ptr(out[1]), _ptr(out[3]), _ptr(out[2]), _ptr(ws),
                                           ws.numel(), _stream())
         check(st, "dit_block_forward_ctrl")
+    return out
+
+
+def block_forward_noalloc(dims: Dims, x_text, x_video, x_audio, weights: dict, compress: bool, keep=None, nk=None,
+                          out=None):
+    """One block on the library's static per-device scratch (no workspace is
+    allocated; calls that overlap on one GPU race); returns (y_text, y_video,
+    y_audio)."""
+    if out is None:
+        out = (torch.empty_like(x_text), torch.empty_like(x_video), torch.empty_like(x_audio))
+    w = _weights_struct(weights)
+    st = lib().dit_block_forward_noalloc(ctypes.byref(dims), _ptr(x_text), _ptr(x_video), _ptr(x_audio),
+                                         ctypes.byref(w), int(compress), _ptr(keep), _ptr(nk), _ptr(out[0]),
+                                         _ptr(out[1]), _ptr(out[2]), _stream())
+    check(st, "dit_block_forward_noalloc")
     return out
 
 

@@ -39,6 +39,8 @@ SIGNATURES = {
     "dit_block_forward_ctrl": (c_i32, [ctypes.POINTER(Dims), c_vp, c_vp, c_vp, c_vp, c_i32, c_vp,
                                        ctypes.POINTER(BlockWeights), c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                        c_size, c_vp]),
+    "dit_block_forward_noalloc": (c_i32, [ctypes.POINTER(Dims), c_vp, c_vp, c_vp, ctypes.POINTER(BlockWeights), c_i32,
+                                          c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "dit_history_count": (c_i32, [c_i32, c_i32, c_i32, P_i32]),
     "dit_history_index": (c_i32, [c_i32, c_i32, c_i32, c_vp, c_vp]),
     "dit_stack_workspace_size": (c_i32, [ctypes.POINTER(Dims), c_vp, c_i32, ctypes.POINTER(c_size)]),
