@@ -436,9 +436,10 @@ __global__ __launch_bounds__(512) void broadcast_residual_kernel(const T* x, con
     }
 }
 
-// x += dt * v (4 elements per thread)
+// x += dt * v (4 elements per thread); v may be x itself (a stack without
+// layers: the velocity is the state), so neither pointer is restrict
 template <typename T>
-__global__ void euler_kernel(T* __restrict__ x, const T* __restrict__ v, size_t n4, float dt) {
+__global__ void euler_kernel(T* x, const T* v, size_t n4, float dt) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n4) return;
     float a[4], b[4];
