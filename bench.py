@@ -43,13 +43,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # reads per byte of a plain 1 GiB copy. Valid only for the kernel source it was
 # taken on (sha256 of the listed files); otherwise reported as null.
 TRAFFIC = {
-    "gemm_gate_up": {"files": ['video_diffusion_transformer_flash_amd/csrc/gemm_mfma.hip', 'video_diffusion_transformer_flash_amd/csrc/epilogue.h', 'video_diffusion_transformer_flash_amd/csrc/common.h'], "sha": "5be5d83378e9c797",
-                     "fetch_bytes": 2905696690, "write_bytes": 107118613,
-                     "copy_scale": {"FETCH_SIZE": 1.99992, "WRITE_SIZE": 1.0},
+    "gemm_gate_up": {"files": ['video_diffusion_transformer_flash_amd/csrc/gemm_mfma.hip', 'video_diffusion_transformer_flash_amd/csrc/epilogue.h', 'video_diffusion_transformer_flash_amd/csrc/common.h'], "sha": "638fd62886f54f77",
+                     "fetch_bytes": 2883282603, "write_bytes": 107118592,
+                     "copy_scale": {"FETCH_SIZE": 1.99994, "WRITE_SIZE": 1.0},
                      "source": "profiles/gemm_gate_up_540p_compressed_hbm_traffic.md"},
-    "broadcast_residual": {"files": ['video_diffusion_transformer_flash_amd/csrc/rowops.hip', 'video_diffusion_transformer_flash_amd/csrc/common.h'], "sha": "7f6d728a117b5b17",
-                           "fetch_bytes": 206407378, "write_bytes": 131604719,
-                           "copy_scale": {"FETCH_SIZE": 1.99992, "WRITE_SIZE": 1.0},
+    "broadcast_residual": {"files": ['video_diffusion_transformer_flash_amd/csrc/rowops.hip', 'video_diffusion_transformer_flash_amd/csrc/common.h'], "sha": "a6cf603b052467ec",
+                           "fetch_bytes": 206408021, "write_bytes": 131604480,
+                           "copy_scale": {"FETCH_SIZE": 1.99994, "WRITE_SIZE": 1.0},
                            "source": "profiles/broadcast_residual_540p_compressed_hbm_traffic.md"},
 }
 
@@ -476,10 +476,11 @@ def cpu_info():
             for line in f:
                 k, _, v = line.partition(":")
                 k, v = k.strip(), v.strip()
+                key = {"cpu family": "cpu_family", "model": "cpu_model_number", "stepping": "cpu_stepping"}.get(k)
                 if k == "model name" and info["cpu_model"] == "unknown":
                     info["cpu_model"] = v
-                elif k in ("cpu family", "model", "stepping") and f"cpu_{k.replace(' ', '_')}" not in info:
-                    info[f"cpu_{k.replace(' ', '_')}"] = v
+                elif key and key not in info:
+                    info[key] = v
                 elif not line.strip() and info["cpu_model"] != "unknown":
                     break
     except OSError:
