@@ -239,10 +239,12 @@ int32_t dit_gather_kept(int32_t n_kept, int32_t D, int32_t dtype, const void* x_
 
 /* Nearest-kept update broadcast with the full-resolution residual [PD-2],
  * [TDH-training]: out[p] = x_video[p] + delta[nk[p]] for p < n_video, rows of
- * D elements; x_video / out have dtype (F32 or BF16), delta is fp32
- * [n_kept][D]. out may alias x_video. Bandwidth bound. */
+ * D elements (the add in fp32, then the store's rounding); x_video / out have
+ * dtype (F32 or BF16), delta [n_kept][D] has delta_dtype (F32 or BF16).
+ * out may alias x_video. Bandwidth bound. (Inside dit_block_forward the MFMA
+ * path adds the fp32 update in the down projection's epilogue instead.) */
 int32_t dit_broadcast_residual(int32_t n_video, int32_t n_kept, int32_t D, int32_t dtype, const void* x_video,
-                               const float* delta, const int32_t* nk, void* out, void* stream);
+                               const void* delta, int32_t delta_dtype, const int32_t* nk, void* out, void* stream);
 
 /* Multi-head attention over a joint sequence, the block's attention step on
  * its own [TDH-backbone]: o = softmax(q k^T * scale) v per head, unmasked.

@@ -99,8 +99,10 @@ def test_other_entry_points_reject():
     assert lib.dit_quantize_fp8(None, 0, 16, None, None, None) == _lib.DIT_EINVAL
     assert lib.dit_quantize_fp8(ctypes.c_void_p(1 << 20), 2, 16, ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 20),
                                 None) == _lib.DIT_EUNSUPPORTED
-    assert lib.dit_broadcast_residual(4, 0, 64, 1, ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 20),
+    assert lib.dit_broadcast_residual(4, 0, 64, 1, ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 20), 0,
                                       ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 20), None) == _lib.DIT_EINVAL
+    assert lib.dit_broadcast_residual(4, 2, 64, 1, ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 20), 2,
+                                      ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 20), None) == _lib.DIT_EUNSUPPORTED
     n = ctypes.c_size_t()
     assert lib.dit_attention_workspace_size(10, 2, 96, 1, ctypes.byref(n)) == _lib.DIT_EUNSUPPORTED
     d = _dims()

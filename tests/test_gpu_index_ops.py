@@ -59,8 +59,9 @@ def test_gather_kept_bit_exact(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("ddtype", ["f32", "bf16"])
 @pytest.mark.parametrize("grid", [(2, 9, 15), (6, 34, 60), (1, 1, 1), (2, 2, 5)])
-def test_broadcast_residual_bit_exact(dtype, grid):
+def test_broadcast_residual_bit_exact(dtype, ddtype, grid):
     T, H, W = grid
     D = 256
     g = np.random.default_rng(2)
@@ -69,16 +70,20 @@ def test_broadcast_residual_bit_exact(dtype, grid):
         x = round_bf16(x)
     nkept = len(O.keep_index(T, H, W))
     delta = (0.5 * g.standard_normal((nkept, D))).astype(np.float32)
+    if ddtype == "bf16":
+        delta = round_bf16(delta)
     nk = O.nearest_kept_map(T, H, W)
     ref = (x + delta[nk]).astype(np.float32)      # fp32 add, then the storage rounding
     if dtype == "bf16":
         ref = round_bf16(ref)
     tx = torch.from_numpy(x).cuda()
     tx = tx.to(torch.bfloat16) if dtype == "bf16" else tx
-    out = V.broadcast_residual(tx, torch.from_numpy(delta).cuda(), V.nearest_kept_map(T, H, W, 2))
+    td = torch.from_numpy(delta).cuda()
+    td = td.to(torch.bfloat16) if ddtype == "bf16" else td
+    out = V.broadcast_residual(tx, td, V.nearest_kept_map(T, H, W, 2))
     assert np.array_equal(out.float().cpu().numpy(), ref)
     # in place
-    V.broadcast_residual(tx, torch.from_numpy(delta).cuda(), V.nearest_kept_map(T, H, W, 2), out=tx)
+    V.broadcast_residual(tx, td, V.nearest_kept_map(T, H, W, 2), out=tx)
     assert np.array_equal(tx.float().cpu().numpy(), ref)
 
 

@@ -227,11 +227,13 @@ def gather_kept(x_video, keep, out=None):
 
 
 def broadcast_residual(x_video, delta, nk, out=None):
+    """out[p] = x_video[p] + delta[nk[p]] (delta fp32 or bf16 rows)."""
     D = x_video.shape[-1]
     dt = {torch.float32: DIT_F32, torch.bfloat16: DIT_BF16}[x_video.dtype]
+    ddt = {torch.float32: DIT_F32, torch.bfloat16: DIT_BF16}[delta.dtype]
     if out is None:
         out = torch.empty_like(x_video)
-    check(lib().dit_broadcast_residual(nk.numel(), delta.shape[0], D, dt, _ptr(x_video), _ptr(delta), _ptr(nk),
+    check(lib().dit_broadcast_residual(nk.numel(), delta.shape[0], D, dt, _ptr(x_video), _ptr(delta), ddt, _ptr(nk),
                                        _ptr(out), _stream()), "dit_broadcast_residual")
     return out
 

@@ -50,7 +50,7 @@ SIGNATURES = {
                                       c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "dit_quantize_fp8": (c_i32, [c_vp, c_i32, c_i64, c_vp, c_vp, c_vp]),
     "dit_gather_kept": (c_i32, [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]),
-    "dit_broadcast_residual": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "dit_broadcast_residual": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp]),
     "dit_attention_workspace_size": (c_i32, [c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_size)]),
     "dit_attention": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "dit_rmsnorm": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_f32, c_vp, c_vp, c_vp, c_vp]),

@@ -420,7 +420,7 @@ int block_forward_impl(const dit_dims* dims, const void* x_text, const void* x_v
     if (r) return r;
     if (compress_on && !fused) {
         TR("broadcast_residual");
-        HIPCHK(broadcast_residual_launch(false, x_video, (const float*)(w8 + P.delta), nk, y_video, nv, d.d_model, st));
+        HIPCHK(broadcast_residual_launch(false, x_video, w8 + P.delta, false, nk, y_video, nv, d.d_model, st));
     }
     TR("end");
     return DIT_OK;
@@ -554,7 +554,7 @@ int stack_impl(const dit_dims* dims, const dit_block_weights* layers_host, int32
             }
             if (!bf) {
                 TR("broadcast_residual");
-                HIPCHK(broadcast_residual_launch(false, cur.xv, delta, nk, Zv, nv, (int)D, st));
+                HIPCHK(broadcast_residual_launch(false, cur.xv, delta, false, nk, Zv, nv, (int)D, st));
             }
             cur = state;
             l = e;
@@ -626,12 +626,14 @@ int32_t dit_gather_kept(int32_t n_kept, int32_t D, int32_t dtype, const void* x_
 }
 
 int32_t dit_broadcast_residual(int32_t n_video, int32_t n_kept, int32_t D, int32_t dtype, const void* x_video,
-                               const float* delta, const int32_t* nk, void* out, void* stream) {
+                               const void* delta, int32_t delta_dtype, const int32_t* nk, void* out, void* stream) {
     if (n_video < 0 || n_kept < 1 || D <= 0 || D % 8 || !x_video || !delta || !nk || !out) return DIT_EINVAL;
     if (!aligned16(x_video) || !aligned16(delta) || !aligned16(out)) return DIT_EINVAL;
     if (dtype != DIT_F32 && dtype != DIT_BF16) return DIT_EUNSUPPORTED;
+    if (delta_dtype != DIT_F32 && delta_dtype != DIT_BF16) return DIT_EUNSUPPORTED;
     if (n_video == 0) return DIT_OK;
-    HIPCHK(broadcast_residual_launch(dtype == DIT_BF16, x_video, delta, nk, out, n_video, D, (hipStream_t)stream));
+    HIPCHK(broadcast_residual_launch(dtype == DIT_BF16, x_video, delta, delta_dtype == DIT_BF16, nk, out, n_video, D,
+                                     (hipStream_t)stream));
     return DIT_OK;
 }
 

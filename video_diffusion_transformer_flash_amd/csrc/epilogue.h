@@ -208,6 +208,24 @@ template <> DIT_DEV void load8<bf16_t>(const bf16_t* p, float v[8]) {
     }
 }
 
+// load8 of rows read once (the full-resolution rows of the broadcast)
+template <typename T> DIT_DEV void load8_stream(const T* p, float v[8]);
+template <> DIT_DEV void load8_stream<float>(const float* p, float v[8]) {
+    const uint4 a = ld_stream(p), b = ld_stream(p + 4);
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
+}
+template <> DIT_DEV void load8_stream<bf16_t>(const bf16_t* p, float v[8]) {
+    const uint4 x = ld_stream(p);
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+
 // q or k (dst = p.q or p.k): rotary embedding with the row's (cos, sin) pairs
 // (32 contiguous bytes per lane), head-major row; rows [M, Mpad) zero
 template <typename T>
@@ -276,7 +294,7 @@ DIT_DEV void bcast8(const EpiParams& p, int j, int n0, const float d[8]) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int h = h0 + (q >> 1), w = w0 + (q & 1);
-            if (h <= h1 && w <= w1) load8<T>(x + (base + (size_t)h * g.W + w) * p.D + n0, v[q]);
+            if (h <= h1 && w <= w1) load8_stream<T>(x + (base + (size_t)h * g.W + w) * p.D + n0, v[q]);
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -293,7 +311,7 @@ DIT_DEV void bcast8(const EpiParams& p, int j, int n0, const float d[8]) {
         for (int w = w0; w <= w1; ++w) {
             const size_t off = (base + (size_t)h * g.W + w) * p.D + n0;
             float v[8];
-            load8<T>(x + off, v);
+            load8_stream<T>(x + off, v);
 #pragma unroll
             for (int i = 0; i < 8; ++i) v[i] += d[i];
             store8<T>(out + off, v);

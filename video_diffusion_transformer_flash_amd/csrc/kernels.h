@@ -24,8 +24,8 @@ hipError_t quant_launch(bool bf16, const void* src, uint8_t* dst, const float* a
 hipError_t amax_launch(bool bf16, const void* src, size_t n, float* amax, hipStream_t st);
 hipError_t amax_to_scale_launch(float* p, hipStream_t st);
 hipError_t gather_rows_launch(const void* x, const int32_t* idx, void* out, int n, size_t rowbytes, hipStream_t st);
-hipError_t broadcast_residual_launch(bool bf16, const void* x, const float* delta, const int32_t* nk, void* out,
-                                     int n_video, int D, hipStream_t st);
+hipError_t broadcast_residual_launch(bool bf16, const void* x, const void* delta, bool delta_bf16, const int32_t* nk,
+                                     void* out, int n_video, int D, hipStream_t st);
 hipError_t euler_launch(bool bf16, void* x, const void* v, size_t n, float dt, hipStream_t st);
 
 hipError_t gemm_mfma(bool fp8, int mode, const void* A, const void* W0, const void* W1, int M, int N, int K,

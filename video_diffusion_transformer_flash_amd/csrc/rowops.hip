@@ -228,9 +228,10 @@ __global__ __launch_bounds__(256) void rmsnorm_reg_kernel(SeqIn seq, const float
         const TI* x = SEQ ? seq_row<TI>(seq, m, D) : (const TI*)(dense + (size_t)m * D);
         const int nch = D / EPC;
         uint4 r[NCM];
+        // the statistics pass keeps its rows cacheable: the quantise pass reads them again
 #pragma unroll
         for (int i = 0; i < NCM; ++i)
-            if (lane + 64 * i < nch) r[i] = ((const uint4*)x)[lane + 64 * i];
+            if (lane + 64 * i < nch) r[i] = MODE == 1 ? ((const uint4*)x)[lane + 64 * i] : ld_stream((const uint4*)x + lane + 64 * i);
         float rr;
         if constexpr (MODE == 2) {
             rr = rinv[m];
@@ -329,7 +330,7 @@ __global__ void amax_to_scale_kernel(float* p) {
 // out[j] = x[idx[j]], rows of `chunks` 16-byte chunks. A workgroup of 512
 // threads copies two consecutive output rows, 256 threads each (the source
 // row is then uniform per wave), up to four loads in flight per thread; the
-// copy is written non-temporally.
+// copy is written non-temporally (streaming loads were no faster here).
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_v;
 __global__ __launch_bounds__(512) void gather_rows_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__ idx,
                                                           uint8_t* __restrict__ out, int n, int chunks) {
@@ -354,7 +355,8 @@ __global__ __launch_bounds__(512) void gather_rows_kernel(const uint8_t* __restr
     }
 }
 
-// out[p] = x[p] + delta[nk[p]]. A workgroup of 512 threads takes two
+// out[p] = x[p] + delta[nk[p]] (delta fp32 or bf16, the add in fp32). A
+// workgroup of 512 threads takes two
 // consecutive video positions, 256 threads each (the kept slot nk[p] is then
 // uniform per wave), 8 elements per 16/32-byte access, up to four accesses in
 // flight per thread; the output is written non-temporally (it is not read
@@ -367,7 +369,7 @@ struct Chunk8;
 template <>
 struct Chunk8<bf16_t> {
     uint4 v;
-    DIT_DEV void load(const bf16_t* p) { v = *(const uint4*)p; }
+    DIT_DEV void load(const bf16_t* p) { v = ld_stream(p); }
     DIT_DEV void add_store(bf16_t* p, float4 d0, float4 d1) const {
         uint4 o;
         o.x = pack_bf2(__uint_as_float(v.x << 16) + d0.x, __uint_as_float(v.x & 0xFFFF0000u) + d0.y);
@@ -382,8 +384,9 @@ template <>
 struct Chunk8<float> {
     float4 a, b;
     DIT_DEV void load(const float* p) {
-        a = *(const float4*)p;
-        b = *(const float4*)(p + 4);
+        const uint4 u = ld_stream(p), w = ld_stream(p + 4);
+        a = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+        b = make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w));
     }
     DIT_DEV void add_store(float* p, float4 d0, float4 d1) const {
         const f32x4_v u = {a.x + d0.x, a.y + d0.y, a.z + d0.z, a.w + d0.w};
@@ -393,8 +396,22 @@ struct Chunk8<float> {
     }
 };
 
-template <typename T>
-__global__ __launch_bounds__(512) void broadcast_residual_kernel(const T* x, const float* __restrict__ delta,
+// eight update values from fp32 or bf16 rows
+template <typename TD> DIT_DEV void load_d8(const TD* p, float4& d0, float4& d1);
+template <> DIT_DEV void load_d8<float>(const float* p, float4& d0, float4& d1) {
+    d0 = *(const float4*)p;
+    d1 = *(const float4*)(p + 4);
+}
+template <> DIT_DEV void load_d8<bf16_t>(const bf16_t* p, float4& d0, float4& d1) {
+    const uint4 v = *(const uint4*)p;
+    d0 = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u), __uint_as_float(v.y << 16),
+                     __uint_as_float(v.y & 0xFFFF0000u));
+    d1 = make_float4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xFFFF0000u), __uint_as_float(v.w << 16),
+                     __uint_as_float(v.w & 0xFFFF0000u));
+}
+
+template <typename T, typename TD>
+__global__ __launch_bounds__(512) void broadcast_residual_kernel(const T* x, const TD* __restrict__ delta,
                                                                  const int32_t* __restrict__ nk, T* out, int n_video,
                                                                  int D) {
     // x and out may be the same buffer: every element is read, then written, by one thread
@@ -414,16 +431,13 @@ __global__ __launch_bounds__(512) void broadcast_residual_kernel(const T* x, con
     };
     int c0 = threadIdx.x & 255;
     load_x(c0);
-    const float* dr = delta + (size_t)nk[p] * D;
+    const TD* dr = delta + (size_t)nk[p] * D;
     for (;;) {
         float4 d0[U], d1[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int c = c0 + u * 256;
-            if (c < per_row) {
-                d0[u] = *(const float4*)(dr + 8 * c);
-                d1[u] = *(const float4*)(dr + 8 * c + 4);
-            }
+            if (c < per_row) load_d8<TD>(dr + 8 * c, d0[u], d1[u]);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -588,15 +602,22 @@ hipError_t gather_rows_launch(const void* x, const int32_t* idx, void* out, int 
     return hipGetLastError();
 }
 
-hipError_t broadcast_residual_launch(bool bf16, const void* x, const float* delta, const int32_t* nk, void* out,
-                                     int n_video, int D, hipStream_t st) {
+hipError_t broadcast_residual_launch(bool bf16, const void* x, const void* delta, bool delta_bf16, const int32_t* nk,
+                                     void* out, int n_video, int D, hipStream_t st) {
     if (n_video == 0) return hipSuccess;
-    if (bf16)
-        hipLaunchKernelGGL(broadcast_residual_kernel<bf16_t>, dim3((n_video + 1) / 2), dim3(512), 0, st,
-                           (const bf16_t*)x, delta, nk, (bf16_t*)out, n_video, D);
+    const dim3 grid((n_video + 1) / 2), block(512);
+    if (bf16 && delta_bf16)
+        hipLaunchKernelGGL((broadcast_residual_kernel<bf16_t, bf16_t>), grid, block, 0, st, (const bf16_t*)x,
+                           (const bf16_t*)delta, nk, (bf16_t*)out, n_video, D);
+    else if (bf16)
+        hipLaunchKernelGGL((broadcast_residual_kernel<bf16_t, float>), grid, block, 0, st, (const bf16_t*)x,
+                           (const float*)delta, nk, (bf16_t*)out, n_video, D);
+    else if (delta_bf16)
+        hipLaunchKernelGGL((broadcast_residual_kernel<float, bf16_t>), grid, block, 0, st, (const float*)x,
+                           (const bf16_t*)delta, nk, (float*)out, n_video, D);
     else
-        hipLaunchKernelGGL(broadcast_residual_kernel<float>, dim3((n_video + 1) / 2), dim3(512), 0, st,
-                           (const float*)x, delta, nk, (float*)out, n_video, D);
+        hipLaunchKernelGGL((broadcast_residual_kernel<float, float>), grid, block, 0, st, (const float*)x,
+                           (const float*)delta, nk, (float*)out, n_video, D);
     return hipGetLastError();
 }
 
