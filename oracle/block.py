@@ -80,10 +80,10 @@ def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
 
 # Precision each low-bit projection input is held in when its e4m3 codes are
 # decided (codes are integers decided by floating point, so the oracle decides
-# them in the precision the kernels quantise from): the normalised rows and
-# the SwiGLU product in fp32, the attention output in bf16 (the precision in
-# which the attention step hands it on).
-LOWBIT_PRECISION = {"n1": "f32", "o": "bf16", "n2": "f32", "u": "f32"}
+# them in the precision the kernels quantise from): the normalised rows in
+# fp32, the attention output and the SwiGLU product in bf16 (the precision in
+# which those steps hand them on).
+LOWBIT_PRECISION = {"n1": "f32", "o": "bf16", "n2": "f32", "u": "bf16"}
 
 
 def linear(a: np.ndarray, w: np.ndarray, lowbit: bool, precision: str = "f64") -> np.ndarray:

@@ -34,15 +34,14 @@ FLOOR_MARGIN = 1.5
 # stored; the value goes on in registers or straight into its quantiser).
 #   bf16 block: normalised rows, q / k / v, the attention weights P, the
 #     attention output, the SwiGLU product and the outputs in bf16; h in fp32.
-#   fp8 projections: the normalised rows go to the e4m3 quantiser from fp32,
-#     the SwiGLU product is kept in fp32 until its quantisation; the rest as
-#     for bf16.
+#   fp8 projections: the normalised rows go to the e4m3 quantiser from fp32;
+#     the rest as for bf16.
 #   stacks: the state between layers and evaluations in the activation dtype.
 GPU_STORE = {
     "bf16": {"n1": "bf16", "q": "bf16", "k": "bf16", "v": "bf16", "p": "bf16", "o": "bf16", "h": "f32",
              "n2": "bf16", "u": "bf16", "out": "bf16", "state": "bf16"},
     "fp8": {"n1": None, "q": "bf16", "k": "bf16", "v": "bf16", "p": "bf16", "o": "bf16", "h": "f32", "n2": None,
-            "u": "f32", "out": "bf16", "state": "bf16"},
+            "u": "bf16", "out": "bf16", "state": "bf16"},
     "f32": {k: "f32" for k in ("n1", "q", "k", "v", "p", "o", "h", "n2", "u", "out", "state")},
 }
 

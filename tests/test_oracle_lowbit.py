@@ -154,4 +154,4 @@ def test_attention_output_code_decided_in_bf16():
     vbf, sbf = O.fp8.quantize_act_fp8(a, "bf16")
     assert s64 == sbf == 7.0 / 448
     assert v64[0, 1] * s64 == 3.25 and vbf[0, 1] * sbf == 3.0
-    assert O.block.LOWBIT_PRECISION == {"n1": "f32", "o": "bf16", "n2": "f32", "u": "f32"}
+    assert O.block.LOWBIT_PRECISION == {"n1": "f32", "o": "bf16", "n2": "f32", "u": "bf16"}

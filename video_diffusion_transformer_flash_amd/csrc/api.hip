@@ -131,7 +131,7 @@ Plan make_plan(const dit_dims& d, int nv_seq, bool delta, int nc) {
     p.o = take((size_t)p.S * I * es);
     p.o8 = fp8 ? take((size_t)p.S * I) : 0;
     p.h = take((size_t)p.S * D * 4);
-    p.u = take((size_t)p.S * F * (fp8 ? 4 : es));   // fp8: fp32 u, quantised from full precision
+    p.u = take((size_t)p.S * F * es);
     p.u8 = fp8 ? take((size_t)p.S * F) : 0;
     p.delta = delta ? take((size_t)nv_seq * D * 4) : 0;
     // fp32 partial tiles of the O and down projections' K-split tails (a bound
@@ -256,7 +256,7 @@ int run_block(const dit_dims& d, const dit_block_weights& w, const SeqIn& in, co
     // 7. down projection + residual -> outputs / delta
     if (fp8) {
         TR("quant_u");
-        HIPCHK(quant_launch(false, u, u8, sc + 3, (size_t)S * F, st));
+        HIPCHK(quant_launch(true, u, u8, sc + 3, (size_t)S * F, st));
         ep.amax_a = sc + 3; ep.s_w = w.s_wdown; ep.s_w2 = nullptr;
         TR("gemm_down");
         HIPCHK(gemm_mfma(true, EPI_DOWN, u8, w.wdown, nullptr, S, D, F, ep, st));

@@ -9,8 +9,8 @@
 //   QKV   : rotary embedding on q and k (pairs (2i, 2i+1) of each band),
 //           written head-major: q, k [head][Sp][dh], v transposed [head][dh][Sp];
 //   RESID : h = X + acc in fp32 (attention output projection);
-//   SWIGLU: u = silu(gate) * up, with the running |u| max for fp8 (then u
-//           is kept in fp32 until its quantisation);
+//   SWIGLU: u = silu(gate) * up in the activation dtype, with the running
+//           max of the stored |u| for fp8 (quantised from there);
 //   DOWN  : y = h + acc to the text / video / audio outputs, or for kept video
 //           rows of a compressed block the update y - X_ref: in fp32 to a
 //           buffer, or (MFMA kernels) added straight onto every video

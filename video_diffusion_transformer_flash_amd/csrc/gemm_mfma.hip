@@ -632,7 +632,7 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
             }
         } else if constexpr (MODE == EPI_SWIGLU) {
             // columns 0..31 gate, 32..63 up of ffn features fw / 2 .. + 31; four lanes per token
-            using UT = std::conditional_t<FP8, float, TOUT>;   // fp8: u stays fp32 until its quantisation
+            using UT = TOUT;   // u in the activation dtype (bf16); fp8 quantises it from there
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int r = (lane >> 2) + 16 * i, j0 = (lane & 3) * 8;
