@@ -164,6 +164,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void attn_bf16_pipe_ker
         f32x16 sc[2];
         bf16x8_v kf[4][2];   // second half of K(t)'s fragments
         const uint8_t* bK = stK(KB);
+        // V^T(t - 1) landed before the barrier of the previous iteration, so
+        // the fragments phase B starts on are read in phase A's second half
+        const uint8_t* bV = stV(KB ^ 1);
+        bf16x8_v vf[4][4];
+        auto vread = [&](int ks, int d) { vf[ks][d] = *(const bf16x8_v*)(bV + vOff[ks] + d * 4096); };
         if constexpr (QK) {
 #pragma unroll
             for (int b = 0; b < 2; ++b)
@@ -182,18 +187,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void attn_bf16_pipe_ker
                 for (int r = 0; r < 4; ++r) o[i / 4][(i % 4) * 4 + r] *= alpha;
             }
             if constexpr (QK && s < 4) kf[s][b] = *(const bf16x8_v*)(bK + kOff[s + 4] + b * 8192);
+            if constexpr (PV && i >= 8) vread((i - 8) / 4, (i - 8) % 4);
             fence();
         });
         // ---- phase B: O^T += V^T(t - 1) P^T(t - 1) on the matrix core, softmax of S(t) on the VALU
-        const uint8_t* bV = stV(KB ^ 1);
-        bf16x8_v vf[4][4];
-        auto vread = [&](int ks, int d) { vf[ks][d] = *(const bf16x8_v*)(bV + vOff[ks] + d * 4096); };
-        if constexpr (PV) {
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int d = 0; d < 4; ++d) vread(ks, d);
-        }
         // fill bases of K(t + 2) (stage KB) and V^T(t + 1) (stage KB ^ 1), taken outside the slots
         LDSPTR lkN = nullptr, lvN = nullptr;
         if constexpr (QK) {
