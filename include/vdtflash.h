@@ -225,6 +225,30 @@ int32_t dit_stack_sample_ctrl(const dit_dims* dims, const dit_block_weights* lay
                               const int32_t* keep, const int32_t* nk,
                               void* ws, size_t ws_bytes, void* stream);
 
+/* Chunk-by-chunk long video [TDH-long] (tokendh.com article, long-video
+ * section), [PD-3] (PaperDaily review, section 3) on the chunk grid of dims
+ * (T frames; dims.n_ctrl, ctrl_offset and n_fixed must be 0). frames
+ * [T + (n_chunks - 1) (T - 1)][H][W][D] (act_dtype, device) holds on entry the
+ * first chunk's T noise frames, then for each later chunk c its T - 1 new noise
+ * frames; on return every frame is denoised. Chunk 0 is dit_stack_sample on
+ * frames [0, T). Chunk c >= 1 runs dit_stack_sample_ctrl on the window
+ * [n_hist, n_hist + T), n_hist = T + (c - 1)(T - 1) - 1: its first frame (the
+ * last frame made so far) is held fixed (n_fixed = 1) and the bounded history
+ * of frames [0, n_hist) (dit_history_index) joins as control tokens at time
+ * offset n_hist. x_audio [n_chunks][n_audio][D]: one audio segment per chunk,
+ * denoised in place. n_chunks >= 1; T >= 2 when n_chunks > 1. Layers,
+ * schedules, keep and nk as dit_stack_sample. ws: device workspace of at least
+ * dit_long_video_workspace_size bytes, 256-byte aligned (the history index list
+ * and the largest chunk's stack workspace, sized for its history tokens). */
+int32_t dit_long_video_workspace_size(const dit_dims* dims, const uint8_t* compressed_host, int32_t n_layers,
+                                      int32_t n_chunks, size_t* bytes);
+int32_t dit_long_video_sample(const dit_dims* dims, const dit_block_weights* layers_host, int32_t n_layers,
+                              const uint8_t* compressed_host, int32_t n_evals,
+                              const float* t_video_host, const float* t_audio_host,
+                              const void* x_text, int32_t n_chunks, void* frames, void* x_audio,
+                              const int32_t* keep, const int32_t* nk,
+                              void* ws, size_t ws_bytes, void* stream);
+
 /* Per-tensor e4m3 quantisation of a weight tensor [PD-2] (low-bit
  * projections): amax = max |src|, dst = e4m3(saturate(src * (448 / amax))) with
  * round-to-nearest-even, *scale = amax / 448 (fp32, device); amax 0 gives

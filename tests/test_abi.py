@@ -161,3 +161,46 @@ def test_history_count_matches_oracle():
             assert n.value == len(O.history_index(nh, H, W))
     assert lib.dit_history_count(-1, 4, 4, ctypes.byref(n)) == _lib.DIT_EINVAL
     assert lib.dit_history_index(3, 0, 4, None, None) == _lib.DIT_EINVAL
+
+
+def test_long_video_workspace_and_refusals():
+    """The long-video workspace covers the history index list and the largest
+    chunk's stack workspace sized for its history tokens (far below a stack
+    sized for every earlier position); bad arguments are refused on the host."""
+    lib = V.lib()
+    d = _dims(T=6)
+    fl = (ctypes.c_uint8 * 4)(0, 1, 1, 0)
+    flp = ctypes.cast(fl, ctypes.c_void_p)
+    n = ctypes.c_size_t()
+    assert lib.dit_long_video_workspace_size(ctypes.byref(d), flp, 4, 1, ctypes.byref(n)) == _lib.DIT_OK
+    one = n.value
+    s0 = ctypes.c_size_t()
+    assert lib.dit_stack_workspace_size(ctypes.byref(d), flp, 4, ctypes.byref(s0)) == _lib.DIT_OK
+    assert one == s0.value
+    assert lib.dit_long_video_workspace_size(ctypes.byref(d), flp, 4, 5, ctypes.byref(n)) == _lib.DIT_OK
+    five = n.value
+    # the last chunk has 6 + 3 * 5 - 1 = 20 earlier frames; its history keeps frame 0, two frames at
+    # stride 2 and eight at stride 4
+    cnt = ctypes.c_int32()
+    lib.dit_history_count(20, d.H, d.W, ctypes.byref(cnt))
+    assert cnt.value == len(O.history_index(20, d.H, d.W))
+    full = ctypes.c_size_t()
+    dl = _dims(T=6, n_ctrl=20, ctrl_offset=20, n_fixed=1)
+    lib.dit_stack_workspace_size(ctypes.byref(dl), flp, 4, ctypes.byref(full))
+    assert one < five < full.value
+    es = 2
+    grow_tokens = (five - one) / (d.d_model * es)
+    assert grow_tokens >= 2 * cnt.value    # the full-resolution and the packed state both hold the history rows
+    fake = ctypes.c_void_p(1 << 20)
+    ws = ctypes.c_void_p(1 << 24)
+    wf = (_lib.BlockWeights * 4)(*[_lib.BlockWeights(*([fake] * 7)) for _ in range(4)])
+    tv = (ctypes.c_float * 4)(1.0, 0.6, 0.3, 0.0)
+    tvp = ctypes.cast(tv, ctypes.c_void_p)
+    call = lambda dd, chunks, frames, wsb: lib.dit_long_video_sample(  # noqa: E731
+        ctypes.byref(dd), wf, 4, flp, 3, tvp, None, fake, chunks, frames, fake, fake, fake, ws, wsb, None)
+    assert call(d, 0, fake, 1 << 40) == _lib.DIT_EINVAL                        # no chunks
+    assert call(_dims(T=1), 2, fake, 1 << 40) == _lib.DIT_EINVAL               # a later chunk needs T >= 2
+    assert call(_dims(T=6, n_ctrl=1, ctrl_offset=1), 2, fake, 1 << 40) == _lib.DIT_EINVAL
+    assert call(_dims(T=6, n_fixed=1), 2, fake, 1 << 40) == _lib.DIT_EINVAL
+    assert call(d, 5, None, 1 << 40) == _lib.DIT_EINVAL                        # no frames
+    assert call(d, 5, fake, five - 256) == _lib.DIT_EWORKSPACE

@@ -170,3 +170,20 @@ def test_long_video_vs_oracle():
     ref_f, ref_a = O.long_video_sample(x["x_text"], first, new, audio, [oracle_weights(lw, "bf16") for lw in layers],
                                        flags, tv.astype(np.float32), ta.astype(np.float32), d)
     check_parity([to_numpy(frames)] + [to_numpy(a) for a in ga], [ref_f] + list(ref_a), "bf16", "long_video_bf16")
+    # the library's chunk loop equals the chunks composed from dit_stack_sample_ctrl calls, bit for bit
+    T = d.T
+    fr = torch.empty_like(frames)
+    fr[:T].copy_(torch_act(first, d.dtype))
+    for c, n in enumerate(new):
+        fr[T + c * (T - 1):T + (c + 1) * (T - 1)].copy_(torch_act(n, d.dtype))
+    ca = [torch_act(a, d.dtype) for a in audio]
+    V.stack_sample(dims, gl, flags, tv, ta, xt, fr[:T], ca[0], keep, nk)
+    for c in range(1, len(audio)):
+        n_hist = T + (c - 1) * (T - 1) - 1
+        dc = V.make_dims(d)
+        dc.n_ctrl, dc.ctrl_offset, dc.n_fixed = n_hist, n_hist, 1
+        V.stack_sample(dc, gl, flags, tv, ta, xt, fr[n_hist:n_hist + T], ca[c], keep, nk, x_ctrl=fr[:n_hist],
+                       ctrl_idx=V.history_index(n_hist, d.H, d.W))
+    torch.cuda.synchronize()
+    assert torch.equal(fr, frames)
+    assert all(torch.equal(a, b) for a, b in zip(ca, ga))

@@ -17,7 +17,7 @@ from ._lib import DIT_BF16, DIT_F32, DIT_FP8_E4M3, BlockWeights, Dims, DitError,
 __all__ = ["Dims", "make_dims", "keep_dims", "keep_index", "nearest_kept_map", "block_workspace_size",
            "block_forward", "block_forward_noalloc", "stack_workspace_size", "stack_sample", "quantize_fp8",
            "gather_kept", "broadcast_residual", "attention", "rmsnorm", "project_residual", "history_index",
-           "long_video_sample", "trace_enable", "trace_records", "DitError"]
+           "long_video_workspace_size", "long_video_sample", "trace_enable", "trace_records", "DitError"]
 
 _ACT = {"f32": DIT_F32, "bf16": DIT_BF16, "fp8": DIT_BF16}
 _WT = {"f32": DIT_F32, "bf16": DIT_BF16, "fp8": DIT_FP8_E4M3}
@@ -176,32 +176,47 @@ def stack_sample(dims: Dims, layers: list, flags, t_video, t_audio, x_text, x_vi
     return x_video, x_audio
 
 
-def long_video_sample(dims: Dims, layers: list, flags, t_video, t_audio, x_text, first_video, new_video, audio,
-                      keep=None, nk=None):
-    """Chunk-by-chunk long video on the chunk grid of `dims` (T frames).
+def long_video_workspace_size(dims: Dims, flags, n_chunks: int) -> int:
+    fl = (ctypes.c_uint8 * max(len(flags), 1))(*[int(f) for f in flags])
+    n = ctypes.c_size_t()
+    check(lib().dit_long_video_workspace_size(ctypes.byref(dims), ctypes.cast(fl, ctypes.c_void_p), len(flags),
+                                              n_chunks, ctypes.byref(n)), "dit_long_video_workspace_size")
+    return n.value
 
-    The first chunk denoises first_video [T, H, W, D]. Each later chunk is
-    [the last frame made so far, held fixed (n_fixed = 1) | T - 1 new frames
-    from its block of new_video], with every earlier frame as control frames
-    at the time offset n_hist, of which the block reads the bounded history
-    selection (dit_history_index). audio: one [n_audio, D] tensor per chunk,
-    denoised in place. Returns the frames [T + (chunks - 1)(T - 1), H, W, D]."""
-    T = dims.T
+
+def long_video_sample(dims: Dims, layers: list, flags, t_video, t_audio, x_text, first_video, new_video, audio,
+                      keep=None, nk=None, ws=None):
+    """Chunk-by-chunk long video on the chunk grid of `dims` (T frames), one
+    dit_long_video_sample call: the first chunk denoises first_video
+    [T, H, W, D]; each later chunk denoises its block of new_video [T - 1, H,
+    W, D] after the last frame made so far (held fixed), with the bounded
+    history of every earlier frame as control tokens. audio: one [n_audio, D]
+    tensor per chunk, denoised in place. Returns the frames
+    [T + (chunks - 1)(T - 1), H, W, D]."""
+    T, n_chunks = dims.T, 1 + len(new_video)
+    assert len(audio) == n_chunks
     frames = torch.empty((T + len(new_video) * (T - 1),) + tuple(first_video.shape[1:]), dtype=first_video.dtype,
                          device=first_video.device)
     frames[:T].copy_(first_video)
-    d = Dims.from_buffer_copy(dims)
-    d.n_ctrl, d.ctrl_offset, d.n_fixed = 0, 0, 0
-    stack_sample(d, layers, flags, t_video, t_audio, x_text, frames[:T], audio[0], keep, nk)
-    made = T
-    for noise, a in zip(new_video, audio[1:]):
-        n_hist = made - 1                       # frames before the boundary
-        frames[made:made + T - 1].copy_(noise)
-        d = Dims.from_buffer_copy(dims)
-        d.n_ctrl, d.ctrl_offset, d.n_fixed = n_hist, n_hist, 1
-        stack_sample(d, layers, flags, t_video, t_audio, x_text, frames[n_hist:n_hist + T], a, keep, nk,
-                     x_ctrl=frames[:n_hist], ctrl_idx=history_index(n_hist, dims.H, dims.W))
-        made += T - 1
+    for c, noise in enumerate(new_video):
+        frames[T + c * (T - 1):T + (c + 1) * (T - 1)].copy_(noise)
+    aud = torch.stack(list(audio)) if dims.n_audio > 0 else None
+    n = len(layers)
+    arr = (BlockWeights * max(n, 1))(*[_weights_struct(w) for w in layers])
+    fl = (ctypes.c_uint8 * max(n, 1))(*[int(f) for f in flags])
+    tv = (ctypes.c_float * len(t_video))(*[float(t) for t in t_video])
+    ta = None if t_audio is None else (ctypes.c_float * len(t_audio))(*[float(t) for t in t_audio])
+    if ws is None:
+        ws = workspace(long_video_workspace_size(dims, flags, n_chunks))
+    st = lib().dit_long_video_sample(ctypes.byref(dims), arr, n, ctypes.cast(fl, ctypes.c_void_p), len(t_video) - 1,
+                                     ctypes.cast(tv, ctypes.c_void_p),
+                                     None if ta is None else ctypes.cast(ta, ctypes.c_void_p), _ptr(x_text),
+                                     n_chunks, _ptr(frames), _ptr(aud), _ptr(keep), _ptr(nk), _ptr(ws), ws.numel(),
+                                     _stream())
+    check(st, "dit_long_video_sample")
+    if aud is not None:
+        for a, out in zip(audio, aud):
+            a.copy_(out)
     return frames
 
 

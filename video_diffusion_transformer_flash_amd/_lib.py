@@ -48,6 +48,9 @@ SIGNATURES = {
                                  c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "dit_stack_sample_ctrl": (c_i32, [ctypes.POINTER(Dims), ctypes.POINTER(BlockWeights), c_i32, c_vp, c_i32, c_vp,
                                       c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "dit_long_video_workspace_size": (c_i32, [ctypes.POINTER(Dims), c_vp, c_i32, c_i32, ctypes.POINTER(c_size)]),
+    "dit_long_video_sample": (c_i32, [ctypes.POINTER(Dims), ctypes.POINTER(BlockWeights), c_i32, c_vp, c_i32, c_vp,
+                                      c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "dit_quantize_fp8": (c_i32, [c_vp, c_i32, c_i64, c_vp, c_vp, c_vp]),
     "dit_gather_kept": (c_i32, [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "dit_broadcast_residual": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp]),

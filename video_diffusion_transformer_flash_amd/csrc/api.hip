@@ -453,19 +453,28 @@ int32_t dit_block_forward_ctrl(const dit_dims* dims, const void* x_text, const v
                               nk, y_text, y_video, y_ctrl, y_audio, ws, ws_bytes, stream);
 }
 
+namespace {
+
+// stack workspace with nc control tokens in the sequence: the full-resolution
+// and the packed compressed state, then the larger of the two block plans
+size_t stack_bytes(const dit_dims& d, int nc) {
+    const size_t es = esize(d.act_dtype);
+    const int nv = d.T * d.H * d.W;
+    const int nkept = d.T * keep_count(d.H, d.stride) * keep_count(d.W, d.stride);
+    const size_t Soff = (size_t)d.n_text + nv + nc + d.n_audio, Son = (size_t)d.n_text + nkept + nc + d.n_audio;
+    const Plan Pf = make_plan(d, nv, false, nc), Pc = make_plan(d, nkept, true, nc);
+    return align256(Soff * d.d_model * es) + align256(Son * d.d_model * es) + std::max(Pf.total, Pc.total);
+}
+
+}  // namespace
+
 int32_t dit_stack_workspace_size(const dit_dims* dims, const uint8_t* compressed_host, int32_t n_layers,
                                  size_t* bytes) {
     int r = validate_dims(dims);
     if (r) return r;
     if (!bytes || n_layers < 0 || (n_layers > 0 && !compressed_host)) return DIT_EINVAL;
-    const dit_dims& d = *dims;
-    const size_t es = esize(d.act_dtype);
-    const int nv = d.T * d.H * d.W;
-    const int nc = d.n_ctrl * d.H * d.W;   // every control position (a listed subset needs no more)
-    const int nkept = d.T * keep_count(d.H, d.stride) * keep_count(d.W, d.stride);
-    const size_t Soff = (size_t)d.n_text + nv + nc + d.n_audio, Son = (size_t)d.n_text + nkept + nc + d.n_audio;
-    const Plan Pf = make_plan(d, nv, false, nc), Pc = make_plan(d, nkept, true, nc);
-    *bytes = align256(Soff * d.d_model * es) + align256(Son * d.d_model * es) + std::max(Pf.total, Pc.total);
+    // every control position (a listed subset needs no more)
+    *bytes = stack_bytes(*dims, dims->n_ctrl * dims->H * dims->W);
     return DIT_OK;
 }
 
@@ -492,9 +501,9 @@ int stack_impl(const dit_dims* dims, const dit_block_weights* layers_host, int32
     if (d.n_ctrl > 0 && (!x_ctrl || !aligned16(x_ctrl))) return DIT_EINVAL;
     if (ctrl_idx && (n_ctrl_tok < 1 || n_ctrl_tok > d.n_ctrl * d.H * d.W)) return DIT_EINVAL;
     if (!ws || ((uintptr_t)ws & 255)) return DIT_EINVAL;
-    size_t need = 0;
-    dit_stack_workspace_size(dims, compressed_host, n_layers, &need);
-    if (ws_bytes < need) return DIT_EWORKSPACE;
+    // the workspace this call carves: its control tokens are the listed ones
+    // when ctrl_idx is given (dit_stack_workspace_size covers every position)
+    if (ws_bytes < stack_bytes(d, ctrl_idx ? n_ctrl_tok : d.n_ctrl * d.H * d.W)) return DIT_EWORKSPACE;
     if (n_evals == 0) return DIT_OK;
 
     hipStream_t st = (hipStream_t)stream;
@@ -600,6 +609,94 @@ int32_t dit_stack_sample_ctrl(const dit_dims* dims, const dit_block_weights* lay
     if (dims->n_ctrl < 1) return DIT_EINVAL;
     return stack_impl(dims, layers_host, n_layers, compressed_host, n_evals, t_video_host, t_audio_host, x_text,
                       x_video, x_ctrl, ctrl_idx, n_ctrl_tok, x_audio, keep, nk, ws, ws_bytes, stream);
+}
+
+namespace {
+
+// dims of chunk c >= 1 of a long video: the boundary frame held fixed, every
+// earlier frame as control frames at the time offset n_hist
+int chunk_hist(const dit_dims& d, int c) { return d.T + (c - 1) * (d.T - 1) - 1; }
+
+dit_dims chunk_dims(const dit_dims& d, int c) {
+    dit_dims e = d;
+    if (c > 0) {
+        e.n_ctrl = e.ctrl_offset = chunk_hist(d, c);
+        e.n_fixed = 1;
+    }
+    return e;
+}
+
+int long_video_plan(const dit_dims* dims, const uint8_t* compressed_host, int32_t n_layers, int32_t n_chunks,
+                    size_t* idx_bytes, size_t* stack_max) {
+    int r = validate_dims(dims);
+    if (r) return r;
+    const dit_dims& d = *dims;
+    if (d.n_ctrl != 0 || d.ctrl_offset != 0 || d.n_fixed != 0) return DIT_EINVAL;
+    if (n_chunks < 1 || n_layers < 0 || (n_layers > 0 && !compressed_host)) return DIT_EINVAL;
+    if (n_chunks > 1 && d.T < 2) return DIT_EINVAL;
+    if ((long long)d.T + (long long)(n_chunks - 1) * (d.T - 1) > (1 << 20)) return DIT_EINVAL;
+    size_t ib = 0, sm = stack_bytes(d, 0);
+    for (int c = 1; c < n_chunks; ++c) {
+        const dit_dims e = chunk_dims(d, c);
+        if ((r = validate_dims(&e))) return r;
+        int32_t cnt = 0;
+        if ((r = dit_history_count(e.n_ctrl, d.H, d.W, &cnt))) return r;
+        ib = std::max(ib, align256((size_t)cnt * sizeof(int32_t)));
+        sm = std::max(sm, stack_bytes(e, cnt));
+    }
+    *idx_bytes = ib;
+    *stack_max = sm;
+    return DIT_OK;
+}
+
+}  // namespace
+
+int32_t dit_long_video_workspace_size(const dit_dims* dims, const uint8_t* compressed_host, int32_t n_layers,
+                                      int32_t n_chunks, size_t* bytes) {
+    if (!bytes) return DIT_EINVAL;
+    size_t ib = 0, sm = 0;
+    int r = long_video_plan(dims, compressed_host, n_layers, n_chunks, &ib, &sm);
+    if (r) return r;
+    *bytes = ib + sm;
+    return DIT_OK;
+}
+
+int32_t dit_long_video_sample(const dit_dims* dims, const dit_block_weights* layers_host, int32_t n_layers,
+                              const uint8_t* compressed_host, int32_t n_evals, const float* t_video_host,
+                              const float* t_audio_host, const void* x_text, int32_t n_chunks, void* frames,
+                              void* x_audio, const int32_t* keep, const int32_t* nk, void* ws, size_t ws_bytes,
+                              void* stream) {
+    size_t ib = 0, sm = 0;
+    int r = long_video_plan(dims, compressed_host, n_layers, n_chunks, &ib, &sm);
+    if (r) return r;
+    if (!frames || !aligned16(frames) || !ws || ((uintptr_t)ws & 255)) return DIT_EINVAL;
+    if (dims->n_audio > 0 && (!x_audio || !aligned16(x_audio))) return DIT_EINVAL;
+    if (ws_bytes < ib + sm) return DIT_EWORKSPACE;
+    const dit_dims& d = *dims;
+    const size_t es = esize(d.act_dtype);
+    const size_t frame = (size_t)d.H * d.W * d.d_model * es;
+    const size_t aud = (size_t)d.n_audio * d.d_model * es;
+    int32_t* idx = (int32_t*)ws;
+    uint8_t* sws = (uint8_t*)ws + ib;
+    uint8_t* f8 = (uint8_t*)frames;
+    uint8_t* a8 = (uint8_t*)x_audio;
+    // chunk 0: the first T frames on their own
+    if ((r = stack_impl(dims, layers_host, n_layers, compressed_host, n_evals, t_video_host, t_audio_host, x_text,
+                        f8, nullptr, nullptr, 0, a8, keep, nk, sws, sm, stream)))
+        return r;
+    for (int c = 1; c < n_chunks; ++c) {
+        const dit_dims e = chunk_dims(d, c);
+        const int n_hist = e.n_ctrl;
+        int32_t cnt = 0;
+        if ((r = dit_history_count(n_hist, d.H, d.W, &cnt))) return r;
+        if ((r = dit_history_index(n_hist, d.H, d.W, idx, stream))) return r;
+        // window [n_hist, n_hist + T): the last frame made so far, then the T - 1 new ones
+        if ((r = stack_impl(&e, layers_host, n_layers, compressed_host, n_evals, t_video_host, t_audio_host, x_text,
+                            f8 + (size_t)n_hist * frame, f8, idx, cnt, a8 ? a8 + (size_t)c * aud : nullptr, keep, nk,
+                            sws, sm, stream)))
+            return r;
+    }
+    return DIT_OK;
 }
 
 int32_t dit_quantize_fp8(const void* src, int32_t src_dtype, int64_t n, uint8_t* dst, float* scale, void* stream) {

@@ -25,7 +25,7 @@ namespace dit {
 
 namespace detail {
 
-constexpr int KT = 64;   // keys per tile
+[[maybe_unused]] constexpr int KT = 64;   // keys per tile (device code only)
 constexpr int QW = 32;   // queries per wave
 typedef __attribute__((address_space(3))) uint8_t* LDSPTR;
 
