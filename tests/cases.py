@@ -53,3 +53,9 @@ HIST = CTRL_BF16.with_(name="hist_bf16", n_ctrl=12, ctrl_offset=12, seed=15)
 HIST_STACK = HIST.with_(name="hist_stack", d_model=256, n_heads=2, d_ffn=512, n_ctrl=5, ctrl_offset=5, seed=16)
 LONG_VIDEO = CTRL_BF16.with_(name="long_video", d_model=256, n_heads=2, d_ffn=512, T=3, H=8, W=12, n_ctrl=0,
                              ctrl_offset=0, seed=17)
+
+
+# fp8 blocks on degenerate grids: (T, H, W, n_text, n_audio); a single token,
+# text only beside a 2 x 2 grid, audio beside a one-column grid
+DEG_FP8 = [SMALL_FP8.with_(name=f"deg_fp8_{T}x{H}x{W}", T=T, H=H, W=W, n_text=nt, n_audio=na)
+           for T, H, W, nt, na in [(1, 1, 1, 0, 0), (1, 2, 2, 3, 0), (2, 3, 1, 0, 5)]]

@@ -76,6 +76,61 @@ def stack_floor(d, x, layers, flags, tv, ta):
     return errors(mod, ref)
 
 
+# how close (relative) to a code boundary a quantiser input must lie for the
+# other code to be admissible: one bf16 unit for inputs held in bf16 (one
+# rounding of a value whose accumulation differed can move it by that much),
+# 2^-12 for inputs held in fp32 (accumulation-order differences of the
+# projections and norms feeding them, fp8 products included)
+FLIP_REACH = {"bf16": 2.0 ** -8, "f32": 2.0 ** -12}
+
+
+def admissible_flips(d, x, ow, compress: bool):
+    """Oracle outputs under each admissible single code decision: an e4m3
+    code is an integer decided by floating point, and where the value at a
+    quantiser input (n1, o, n2, u; in the precision the codes are decided in)
+    lies within FLIP_REACH (relative) of the rounding boundary between two codes,
+    an implementation whose accumulation differs from the oracle's by rounding
+    may take the other code, which is as correct. Yields the oracle's outputs
+    with one such element moved to the code across its boundary (the tensor's
+    amax kept). For small cases: one oracle block per candidate."""
+    from oracle.fp8 import e4m3_decode, e4m3_encode
+
+    grid = np.sort(np.unique(np.abs(e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8)))))
+    mids = (grid[1:] + grid[:-1]) / 2
+    args = (x["x_text"], x["x_video"], x["x_audio"], ow, d, compress)
+    vals = {}
+
+    def probe(name, a):
+        if name in O.block.LOWBIT_PRECISION:
+            vals[name] = np.array(a, dtype=np.float64).reshape(-1)
+        return a
+    O.block_forward(*args, store=probe)
+    for site, v in vals.items():
+        prec = O.block.LOWBIT_PRECISION[site]
+        rel = FLIP_REACH[prec]
+        r = round_to(v, prec)
+        amax = float(np.max(np.abs(r)))
+        if amax == 0.0:
+            continue
+        z = np.abs(r) / (amax / 448.0)
+        j = np.clip(np.searchsorted(mids, z), 1, len(mids) - 1)
+        for jj in (j - 1, j):
+            near = np.abs(z - mids[jj]) <= rel * z
+            for i in np.nonzero(near & (np.abs(r) < amax))[0]:
+                lo, hi = grid[jj[i]], grid[jj[i] + 1]
+                c = int(e4m3_encode(np.array([r[i] / (amax / 448.0)]))[0])
+                other = hi if float(e4m3_decode(np.array([c], dtype=np.uint8))[0]) == np.copysign(lo, r[i]) else lo
+                target = np.copysign(other, r[i]) * (amax / 448.0)
+
+                def flip(name, a, site=site, i=i, target=target):
+                    if name != site:
+                        return a
+                    flat = np.array(a, dtype=np.float64).reshape(-1)
+                    flat[i] = target
+                    return flat.reshape(np.shape(a))
+                yield (site, int(i)), O.block_forward(*args, store=flip)
+
+
 def load():
     with open(GOLDEN) as f:
         return json.load(f)

@@ -93,6 +93,9 @@ def all_cases():
         for on in (False, True):
             cs[f"{d.name}_{'on' if on else 'off'}"] = block_case(d, on)
     cs["long_fp8_off"] = block_case(C.LONG_FP8, False)
+    for d in C.DEG_FP8:
+        for on in (False, True):
+            cs[f"{d.name}_{'on' if on else 'off'}"] = block_case(d, on)
     for on in (False, True):
         cs[f"hist_fp8_{'on' if on else 'off'}"] = block_case(C.HIST.with_(name="hist_fp8", dtype="fp8"), on, hist=True)
     cs["c5_block_on"] = block_case(C.C5_BLOCK, True)

@@ -34,9 +34,12 @@ def test_every_gpu_case_has_a_floor():
 
 def test_lowbit_floors_sit_above_the_fixed_bar():
     """The e4m3 code flips put every low-bit block's floor above 6e-2 on
-    max|err|/RMS, while its RMS floor stays near 1-2 %."""
+    max|err|/RMS, while its RMS floor stays near 1-2 %. (Degenerate grids
+    aside: a single token has no flip in the rounding model and nothing to
+    spread one to.)"""
     fl = FL.load()
-    blocks = [k for k in fl if k.endswith(("_on", "_off")) and ("fp8" in k or k.startswith("c5_block"))]
+    blocks = [k for k in fl if k.endswith(("_on", "_off")) and ("fp8" in k or k.startswith("c5_block"))
+              and not k.startswith("deg_")]
     assert len(blocks) >= 11
     for k in blocks:
         assert fl[k]["max"] > 6e-2 and fl[k]["rms"] < 3e-2, (k, fl[k])
@@ -60,3 +63,35 @@ def test_bf16_storage_floor_within_the_bf16_bar():
     ow = oracle_weights(w, "bf16")
     mx, rm = FL.block_floor(d, x, ow, True)
     assert 1e-3 < mx < 2e-2 and np.isfinite(rm)
+
+
+def test_admissible_flips_sit_at_code_boundaries():
+    """Each admissible single decision moves exactly one element of one
+    quantiser input to the neighbouring code, and only elements within the
+    reach of a boundary qualify: on the single-token case there are some, and
+    each changes the oracle's outputs."""
+    from cases import DEG_FP8
+    from oracle.fp8 import e4m3_encode
+    d = DEG_FP8[0]
+    x, w = inputs(d)
+    ow = oracle_weights(w, d.dtype)
+    ref = O.block_forward(x["x_text"], x["x_video"], x["x_audio"], ow, d, False)
+    vals = {}
+
+    def probe(name, a):
+        vals[name] = np.array(a, dtype=np.float64).reshape(-1)
+        return a
+    O.block_forward(x["x_text"], x["x_video"], x["x_audio"], ow, d, False, store=probe)
+    n = 0
+    for (site, i), out in FL.admissible_flips(d, x, ow, False):
+        n += 1
+        prec = O.block.LOWBIT_PRECISION[site]
+        r = FL.round_to(vals[site], prec)
+        s = np.max(np.abs(r)) / 448.0
+        z = r[i] / s
+        zs = z * (1 + FL.FLIP_REACH[prec] * np.array([-1.0, 1.0]))
+        codes = e4m3_encode(zs)
+        assert codes[0] != codes[1], (site, i)        # a boundary lies within reach
+        mx, _ = FL.errors(out, ref)
+        assert mx > 0
+    assert 0 < n < 0.1 * sum(v.size for k, v in vals.items() if k in O.block.LOWBIT_PRECISION)

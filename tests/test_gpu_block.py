@@ -10,9 +10,10 @@ one by one (keys and values still come from the whole sequence)."""
 import numpy as np
 import pytest
 
+import floors as FL
 import oracle as O
 from dit_synth import CONFIGS, SWEEP_FRAMES
-from cases import C5_BLOCK, LONG_BF16, LONG_FP8, SMALL_BF16, SMALL_FP8, SPLIT_BF16, SPLIT_FP8, WIDE_FP8
+from cases import DEG_FP8, C5_BLOCK, LONG_BF16, LONG_FP8, SMALL_BF16, SMALL_FP8, SPLIT_BF16, SPLIT_FP8, WIDE_FP8
 from helpers import check_parity, gpu_weights, inputs, oracle_weights, rel_err, to_numpy, torch_act
 
 pytestmark = pytest.mark.gpu
@@ -103,6 +104,53 @@ def test_degenerate_grids_bf16():
         d = SMALL_BF16.with_(name=f"deg{T}x{H}x{W}", T=T, H=H, W=W, n_text=nt, n_audio=na)
         for compress in (False, True):
             check_full(d, compress)
+
+
+@pytest.mark.parametrize("compress", [False, True])
+@pytest.mark.parametrize("d", DEG_FP8[1:], ids=lambda d: d.name)
+def test_degenerate_grids_fp8(d, compress):
+    """Low-bit projections on text beside a 2 x 2 grid and on audio beside a
+    one-column grid (tensors far smaller than a tile)."""
+    check_full(d, compress)
+
+
+@pytest.mark.parametrize("compress", [False, True])
+def test_single_token_fp8(compress):
+    """One token. Its rounding model flips no e4m3 code, so its floor is the
+    bf16 storage alone; the GPU's own accumulation can still put a value that
+    lies within rounding reach of a code boundary on the other side (that
+    code is as correct). The GPU must match the oracle within the floor bar,
+    either as is or under one such admissible decision."""
+    d = DEG_FP8[0]
+    print(f"block {d.name} compress={compress}", flush=True)
+    x, w = inputs(d)
+    got, _ = run_gpu(d, x, w, compress)
+    ow = oracle_weights(w, d.dtype)
+    case = f"{d.name}_{'on' if compress else 'off'}"
+    mb, rb = FL.bar(case)
+    cands = [("none", O.block_forward(x["x_text"], x["x_video"], x["x_audio"], ow, d, compress))]
+    cands += list(FL.admissible_flips(d, x, ow, compress))
+    errs = sorted((FL.errors(got, ref), key) for key, ref in cands)
+    (mx, rm), key = errs[0]
+    print(f"  {len(cands) - 1} admissible single code decisions; closest: {key}, max|err|/rms {mx:.3e} "
+          f"(bar {mb:.3e}), rms err {rm:.3e} (bar {rb:.3e})")
+    assert mx <= mb and rm <= rb
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_zero_inputs_give_zero_outputs(dtype):
+    """All-zero activations: the norms give zero rows, attention averages zero
+    values, and every e4m3 tensor has amax 0 (scale 1, zero codes), so every
+    output is exactly zero, as in the oracle."""
+    d = (SMALL_FP8 if dtype == "fp8" else SMALL_BF16).with_(name=f"zero_{dtype}")
+    x, w = inputs(d)
+    x = {k: np.zeros_like(v) for k, v in x.items()}
+    for compress in (False, True):
+        got, _ = run_gpu(d, x, w, compress)
+        ref = O.block_forward(x["x_text"], x["x_video"], x["x_audio"], oracle_weights(w, d.dtype), d, compress)
+        for g_, r_ in zip(got, ref):
+            assert not np.any(r_)
+            assert not np.any(g_) and np.all(np.isfinite(g_))
 
 
 def test_deterministic_and_in_place():
