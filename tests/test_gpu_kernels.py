@@ -161,3 +161,21 @@ def test_attention_at_540p_lengths(S, sharp):
     err = np.max(np.abs(out - ref)) / np.sqrt(np.mean(ref ** 2))
     print(f"attention S={S} sharp={sharp}: {err:.2e}")
     assert err <= 3e-2
+
+
+def test_attention_full_width_long_sequence():
+    """56 heads over 12628 tokens: the launcher takes its 8-wave workgroups
+    (256 queries sharing each key tile) here. Sampled query rows (the first,
+    the last, rows of the last partial 256-query block and random ones) over
+    every key, against the oracle, bar 3e-2 as above."""
+    S, nh, dh = 12628, 56, 128
+    g = np.random.default_rng(5)
+    q, k, v = (round_bf16(g.standard_normal((S, nh * dh)).astype(np.float32)) for _ in range(3))
+    tt = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)  # noqa: E731
+    out = V.attention(tt(q), tt(k), tt(v), nh, 1.0 / np.sqrt(dh)).float().cpu().numpy()
+    rows = np.unique(np.concatenate([[0, S - 1], np.arange(S - 84, S, 7), g.integers(0, S, 48)]))
+    ref = O.attention(q[rows].reshape(-1, nh, dh).astype(np.float64), k.reshape(S, nh, dh).astype(np.float64),
+                      v.reshape(S, nh, dh).astype(np.float64)).reshape(len(rows), nh * dh)
+    err = np.max(np.abs(out[rows] - ref)) / np.sqrt(np.mean(ref ** 2))
+    print(f"attention S={S} heads={nh}: {len(rows)} rows, {err:.2e}")
+    assert err <= 3e-2

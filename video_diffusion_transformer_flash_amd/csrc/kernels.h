@@ -34,6 +34,10 @@ hipError_t gemm_mfma(bool fp8, int mode, const void* A, const void* W0, const vo
 // tail of the RESID / DOWN modes (0: it never splits); it does not decrease
 // with M, and the current device's compute-unit count enters it
 size_t gemm_split_bytes_bound(int M, int N);
+namespace detail {
+// compute units of the current device (cached per device; 256 when it cannot be read)
+int device_cus();
+}  // namespace detail
 
 // Bounded long-video history: the kept frames and their strides (at most 11)
 struct HistPlan {
