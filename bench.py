@@ -71,6 +71,12 @@ def traffic_for(kernel):
             "write_bytes": t["write_bytes"], "copy_scale": t["copy_scale"], "source": t["source"]}
 
 
+def _traffic_bytes(kernel):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled), or None."""
+    t = traffic_for(kernel)
+    return None if t is None else t["bytes"]
+
+
 def block_flops(d, S):
     """Algorithmic FLOPs (2 per MAC) of one block on S tokens, per kernel."""
     D, I, F = d.d_model, d.inner, d.d_ffn
@@ -596,7 +602,8 @@ def main():
         "median_step_ms": round(med, 4),
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4),
-                     "flop_per_launch": flops[dom], "launch_ms": round(dom_ms, 4), "traffic": traffic_for(dom)},
+                     "flop_per_launch": flops[dom], "launch_ms": round(dom_ms, 4),
+                     "traffic": _traffic_bytes(dom), "traffic_detail": traffic_for(dom)},
         "kernels": table,
         "kernels_note": f"HIP events between kernel groups over a second run of {a.steps} steps "
                         f"({round(ms_tr, 4)} ms per step with the events)",
@@ -610,7 +617,8 @@ def main():
                             "peak": PEAK_HBM, "unit": "GB/s", "frac": bc["frac"], "bytes_per_launch": bc["bytes"],
                             "launch_ms": bc["ms"], "update_rows": "bf16",
                             "cache": "launches rotate over 4 disjoint buffer sets (1.2 GB), never cache-resident",
-                            "traffic": traffic_for("broadcast_residual")}
+                            "traffic": _traffic_bytes("broadcast_residual"),
+                            "traffic_detail": traffic_for("broadcast_residual")}
     line["bandwidth_kernels"] = bw
     torch.cuda.empty_cache()
     if not a.no_off:
