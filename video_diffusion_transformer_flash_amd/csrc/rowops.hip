@@ -301,6 +301,19 @@ __global__ void quant_kernel(const T* __restrict__ src, uint8_t* __restrict__ ds
     ((uint32_t*)dst)[i] = w;
 }
 
+// the same codes for a bf16 tensor, 8 elements (one 16-byte streaming read, one
+// 8-byte store) per thread
+__global__ void quant8_bf16_kernel(const bf16_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                   const float* __restrict__ amax, size_t n8) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n8) return;
+    const float a = *amax;
+    const float qs = a > 0.f ? __fdiv_rn(448.f, a) : 1.f;
+    float v[8];
+    unpack16<bf16_t>(ld_stream((const uint4*)src + i), v);
+    ((uint2*)dst)[i] = make_uint2(e4m3x4(v, qs), e4m3x4(v + 4, qs));
+}
+
 template <typename T>
 __global__ void amax_kernel(const T* __restrict__ src, size_t n4, float* amax) {
     float mx = 0.f;
@@ -572,7 +585,10 @@ hipError_t fill_launch(float* p, int n, float v, hipStream_t st) {
 
 hipError_t quant_launch(bool bf16, const void* src, uint8_t* dst, const float* amax, size_t n, hipStream_t st) {
     const size_t n4 = n / 4;
-    if (bf16)
+    if (bf16 && n % 8 == 0 && ((uintptr_t)src & 15) == 0 && ((uintptr_t)dst & 7) == 0) {
+        const size_t n8 = n / 8;
+        hipLaunchKernelGGL(quant8_bf16_kernel, dim3(nblk(n8)), dim3(256), 0, st, (const bf16_t*)src, dst, amax, n8);
+    } else if (bf16)
         hipLaunchKernelGGL(quant_kernel<bf16_t>, dim3(nblk(n4)), dim3(256), 0, st, (const bf16_t*)src, dst, amax, n4);
     else
         hipLaunchKernelGGL(quant_kernel<float>, dim3(nblk(n4)), dim3(256), 0, st, (const float*)src, dst, amax, n4);
