@@ -74,8 +74,15 @@ DIT_DEV float wave_max(float v) {
     return v;
 }
 
-// Non-negative float max through integer ordering (valid for x >= 0).
-DIT_DEV void atomic_max_nonneg(float* addr, float x) { atomicMax((unsigned int*)addr, __float_as_uint(x)); }
+// Running max of non-negative floats (x >= 0: their bit patterns order as
+// unsigned integers). The current value is read first and the atomic issued only when
+// x exceeds it: the value only grows, so a stale read can only be smaller and
+// costs a redundant atomic, never a lost maximum; thousands of workgroups
+// updating one address otherwise queue on it.
+DIT_DEV void atomic_max_nonneg(float* addr, float x) {
+    const unsigned cur = __hip_atomic_load((unsigned int*)addr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__float_as_uint(x) > cur) atomicMax((unsigned int*)addr, __float_as_uint(x));
+}
 
 // ----------------------------------------------------------------- sequence layout
 // The joint sequence is [text | video tokens | control | audio]. Video tokens
