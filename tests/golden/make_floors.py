@@ -106,6 +106,8 @@ def all_cases():
     cs["c3_bf16_on"] = block_case(CONFIGS["540p_on"], True)
     cs["c2_bf16_off"] = block_case(CONFIGS["540p_off"], False)
     cs["c4_bf16_on"] = block_case(CONFIGS["768p"], True)
+    for T, on in ((2, True), (2, False), (8, True)):
+        cs[f"t{T}_bf16_{'on' if on else 'off'}"] = block_case(CONFIGS["768p"].with_(name=f"768p_T{T}", T=T), on)
     for dt in ("fp8", "bf16"):
         cs[f"stack_small_{dt}"] = stack_case(C.STACK_SMALL.with_(dtype=dt), C.STACK_FLAGS, tv, ta)
     cs["stack_wide_fp8"] = stack_case(C.STACK_WIDE, C.STACK_WIDE_FLAGS, tv, None)

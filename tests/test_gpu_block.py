@@ -217,11 +217,24 @@ def test_fp8_block_at_stack_layer_sizes(compress):
     check_full(C5_BLOCK, compress, case=f"c5_block_{'on' if compress else 'off'}")
 
 
-@pytest.mark.parametrize("T", SWEEP_FRAMES)
-@pytest.mark.parametrize("compress", [True, False])
+# the 768p sequence-length sweep: every element up to 9244 tokens, sampled
+# rows beyond (32900 and 35044-129668 tokens)
+SWEEP_FULL = [(2, True), (2, False), (8, True)]
+SWEEP_SAMPLED = [(8, False), (32, True), (32, False)]
+assert sorted(SWEEP_FULL + SWEEP_SAMPLED) == sorted((T, c) for T in SWEEP_FRAMES for c in (True, False))
+
+
+@pytest.mark.parametrize("T,compress", SWEEP_FULL, ids=lambda v: str(v))
+def test_sweep_768p_every_element(T, compress):
+    """The 768p grid at 2 latent frames (2794 / 8708 tokens) and 8 frames
+    compressed (9244): every output element against the oracle."""
+    check_full(CONFIGS["768p"].with_(name=f"768p_T{T}", T=T), compress)
+
+
+@pytest.mark.parametrize("T,compress", SWEEP_SAMPLED, ids=lambda v: str(v))
 def test_sweep_768p_sampled(T, compress):
-    """The 768p grid at 2, 8 and 32 latent frames (sequence-length sweep;
-    2794 to 129668 tokens), sampled rows against the oracle."""
+    """The 768p grid at 8 frames uncompressed (32900 tokens) and 32 frames
+    (35044 / 129668), sampled rows against the oracle."""
     check_sampled(CONFIGS["768p"].with_(name=f"768p_T{T}", T=T), compress)
 
 
