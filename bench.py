@@ -636,16 +636,20 @@ def main():
                                 "kernels": kernel_table(kern2, f2, hbm_bytes(d2, S2, d2.n_video, 0))}
         line["on_off_speedup"] = round(ms2 / ms, 3)
         del host2
-    if not a.no_sweep:
-        line["sweep_768p"] = sweep()
-    if not a.no_stack:
-        line["stack"] = stack_timing()
-    if not a.no_decoder:
-        line["decoder_standin"] = decoder_timing()
-    if not a.no_long:
-        line["long_video"] = long_video_timing()
-    if not a.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(d, host, True)
+    # the secondary measurements: an error in one is recorded in its entry and
+    # the others and the headline line still come out
+    for flag, key, fn in ((a.no_sweep, "sweep_768p", sweep), (a.no_stack, "stack", stack_timing),
+                          (a.no_decoder, "decoder_standin", decoder_timing),
+                          (a.no_long, "long_video", long_video_timing),
+                          (a.no_cpu, "cpu_baseline", lambda: cpu_baseline(d, host, True))):
+        if flag:
+            continue
+        try:
+            line[key] = fn()
+        except Exception as e:  # noqa: BLE001
+            line[key] = {"error": f"{type(e).__name__}: {e}"[:400]}
+            print(f"bench.py: {key} failed: {e!r}", file=sys.stderr)
+        torch.cuda.empty_cache()
     print(json.dumps(line), flush=True)
 
 
