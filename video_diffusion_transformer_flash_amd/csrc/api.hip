@@ -147,9 +147,11 @@ Plan make_plan(const dit_dims& d, int nv_seq, bool delta, int nc) {
 // `in`: the joint sequence; `vpos`: flat positions of its video tokens
 // (nullptr: raster); `out`: output segments (or delta); `refin`: rows the
 // delta is taken against.
+// rope_ready: the rotary tables and rows of this plan are already in the
+// workspace (the previous block of a stack ran on the same plan)
 int run_block(const dit_dims& d, const dit_block_weights& w, const SeqIn& in, const int32_t* vpos, const int32_t* cpos,
               const SeqOut& out,
-              const SeqIn& refin, uint8_t* ws, const Plan& P, hipStream_t st) {
+              const SeqIn& refin, uint8_t* ws, const Plan& P, hipStream_t st, bool rope_ready = false) {
     const bool f32 = d.act_dtype == DIT_F32;
     const bool fp8 = d.w_dtype == DIT_FP8_E4M3;
     const int D = d.d_model, nh = d.n_heads, dh = d.head_dim, I = nh * dh, F = d.d_ffn;
@@ -157,8 +159,10 @@ int run_block(const dit_dims& d, const dit_block_weights& w, const SeqIn& in, co
 
     float2* tab = (float2*)(ws + P.tab);
     const int nt_pos = P.ntab_t;
-    TR("rope_tables");
-    HIPCHK(rope_tables_launch(tab, nt_pos, d.rope_t, d.H, d.rope_h, d.W, d.rope_w, (double)d.rope_base, st));
+    if (!rope_ready) {
+        TR("rope_tables");
+        HIPCHK(rope_tables_launch(tab, nt_pos, d.rope_t, d.H, d.rope_h, d.W, d.rope_w, (double)d.rope_base, st));
+    }
     Rope rope{};
     rope.tab_t = tab;
     rope.tab_h = tab + (size_t)nt_pos * (d.rope_t / 2);
@@ -170,8 +174,10 @@ int run_block(const dit_dims& d, const dit_block_weights& w, const SeqIn& in, co
     rope.nt = in.nt; rope.nv = in.nv; rope.nc = in.nc;
     rope.toff = d.ctrl_offset;
     if (d.act_dtype != DIT_F32) {
-        TR("rope_rows");
-        HIPCHK(rope_rows_launch(rope, (float2*)(ws + P.rrows), P.S, d.head_dim / 2, st));
+        if (!rope_ready) {
+            TR("rope_rows");
+            HIPCHK(rope_rows_launch(rope, (float2*)(ws + P.rrows), P.S, d.head_dim / 2, st));
+        }
         rope.rows = (const float2*)(ws + P.rrows);
     }
 
@@ -534,6 +540,10 @@ int stack_impl(const dit_dims* dims, const dit_block_weights* layers_host, int32
     void* Zca = Zc + ((size_t)nt + nkept + nc) * D * es;
     const SeqIn state{Zt, Zv, Zk, Za, nullptr, nullptr, nt, nv, nc, na};
 
+    // which plan's rotary tables and rows the block workspace holds (0: none,
+    // 1: the full-resolution plan, 2: the compressed one); the two plans share
+    // the workspace, so a change of plan rebuilds them
+    int rope_plan = 0;
     for (int ev = 0; ev < n_evals; ++ev) {
         // current full-resolution state: the inputs for the first layer, Z after
         // (listed control tokens are read through ctrl_idx by the first layer, packed after it)
@@ -542,7 +552,9 @@ int stack_impl(const dit_dims* dims, const dit_block_weights* layers_host, int32
         while (l < n_layers) {
             if (!compressed_host[l]) {
                 SeqOut out{Zt, Zv, Zk, Za, nullptr, nullptr, nullptr};
-                if ((r = run_block(d, layers_host[l], cur, nullptr, ctrl_idx, out, cur, bws, Pf, st))) return r;
+                if ((r = run_block(d, layers_host[l], cur, nullptr, ctrl_idx, out, cur, bws, Pf, st, rope_plan == 1)))
+                    return r;
+                rope_plan = 1;
                 cur = state;
                 ++l;
                 continue;
@@ -559,7 +571,9 @@ int stack_impl(const dit_dims* dims, const dit_block_weights* layers_host, int32
                 // the MFMA path, in a pass of its own for fp32)
                 SeqOut out = (i + 1 < e) ? SeqOut{Zct, Zcv, Zck, Zca, nullptr, nullptr, nullptr}
                                          : SeqOut{Zt, nullptr, Zk, Za, delta, bf ? cur.xv : nullptr, bf ? Zv : nullptr};
-                if ((r = run_block(d, layers_host[i], in, keep, ctrl_idx, out, start, bws, Pc, st))) return r;
+                if ((r = run_block(d, layers_host[i], in, keep, ctrl_idx, out, start, bws, Pc, st, rope_plan == 2)))
+                    return r;
+                rope_plan = 2;
             }
             if (!bf) {
                 TR("broadcast_residual");
