@@ -118,3 +118,21 @@ def test_project_residual_sentinels():
         assert bool((ws[need:] == fill).all().item())
         res.append(bits(h))
     assert np.array_equal(res[0], res[1])
+
+
+def test_weights_checked_against_dims():
+    """The binding refuses weights whose dtype or size does not match dims
+    (e4m3 codes under bf16 dims, a missing scale, a short tensor) before any
+    launch: the library takes plain pointers and would read past the end."""
+    d = SMALL_FP8
+    x, w = inputs(d)
+    xt, xv, xa = (torch_act(x[k], d.dtype) for k in ("x_text", "x_video", "x_audio"))
+    gw, _ = gpu_weights(w, d.dtype)
+    with pytest.raises(V.DitError, match="wqkv"):
+        V.block_forward(V.make_dims(d.with_(dtype="bf16")), xt, xv, xa, gw, False)
+    no_scale = {k: v for k, v in gw.items() if k != "s_wdown"}
+    with pytest.raises(V.DitError, match="s_wdown"):
+        V.block_forward(V.make_dims(d), xt, xv, xa, no_scale, False)
+    short = dict(gw, wo=gw["wo"][:-1])
+    with pytest.raises(V.DitError, match="wo"):
+        V.stack_sample(V.make_dims(d), [gw, short], [0, 0], [0.0, 1.0], None, xt, xv, xa)

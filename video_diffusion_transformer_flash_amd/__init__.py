@@ -84,10 +84,33 @@ def block_workspace_size(dims: Dims, compress: bool) -> int:
     return n.value
 
 
-def _weights_struct(w: dict) -> BlockWeights:
+def _weights_struct(w: dict, dims: Dims = None) -> BlockWeights:
+    if dims is not None:
+        _check_weights(w, dims)
     g = lambda k: _ptr(w.get(k))  # noqa: E731
     return BlockWeights(g("g1"), g("wqkv"), g("wo"), g("g2"), g("wgate"), g("wup"), g("wdown"), g("s_wqkv"),
                         g("s_wo"), g("s_wgate"), g("s_wup"), g("s_wdown"))
+
+
+def _check_weights(w: dict, dims: Dims):
+    """Host-side check of one block's weights against dims (the library takes
+    plain pointers and cannot see a buffer's size or type): every tensor on
+    the GPU, contiguous, of the dtype dims names and of its shape's size; e4m3
+    weights with their scales. A mismatch would make the kernels read past
+    the end of a buffer."""
+    D, I, F = dims.d_model, dims.n_heads * dims.head_dim, dims.d_ffn
+    wt = {DIT_F32: torch.float32, DIT_BF16: torch.bfloat16, DIT_FP8_E4M3: torch.uint8}[dims.w_dtype]
+    want = {"g1": (_TORCH[dims.act_dtype], D), "g2": (_TORCH[dims.act_dtype], D), "wqkv": (wt, 3 * I * D),
+            "wo": (wt, D * I), "wgate": (wt, F * D), "wup": (wt, F * D), "wdown": (wt, D * F)}
+    if dims.w_dtype == DIT_FP8_E4M3:
+        want.update({"s_" + k: (torch.float32, 1) for k in ("wqkv", "wo", "wgate", "wup", "wdown")})
+    for k, (dt, n) in want.items():
+        t = w.get(k)
+        if t is None:
+            raise DitError(f"block weights: {k} missing")
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != dt or t.numel() != n:
+            raise DitError(f"block weights: {k} must be a contiguous {dt} GPU tensor of {n} elements "
+                           f"(got {t.dtype}, {t.numel()} elements, {t.device})")
 
 
 def workspace(nbytes: int):
@@ -110,7 +133,7 @@ def block_forward(dims: Dims, x_text, x_video, x_audio, weights: dict, compress:
     need = block_workspace_size(dims, compress)
     if ws is None:
         ws = workspace(need)
-    w = _weights_struct(weights)
+    w = _weights_struct(weights, dims)
     if x_ctrl is None:
         st = lib().dit_block_forward(ctypes.byref(dims), _ptr(x_text), _ptr(x_video), _ptr(x_audio), ctypes.byref(w),
                                      int(compress), _ptr(keep), _ptr(nk), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]),
@@ -133,7 +156,7 @@ def block_forward_noalloc(dims: Dims, x_text, x_video, x_audio, weights: dict, c
     y_audio)."""
     if out is None:
         out = (torch.empty_like(x_text), torch.empty_like(x_video), torch.empty_like(x_audio))
-    w = _weights_struct(weights)
+    w = _weights_struct(weights, dims)
     st = lib().dit_block_forward_noalloc(ctypes.byref(dims), _ptr(x_text), _ptr(x_video), _ptr(x_audio),
                                          ctypes.byref(w), int(compress), _ptr(keep), _ptr(nk), _ptr(out[0]),
                                          _ptr(out[1]), _ptr(out[2]), _stream())
@@ -154,7 +177,7 @@ def stack_sample(dims: Dims, layers: list, flags, t_video, t_audio, x_text, x_vi
     """Flow-matching sampler; x_video and x_audio are updated in place
     (control frames x_ctrl, when given, are re-fed every evaluation)."""
     n = len(layers)
-    arr = (BlockWeights * max(n, 1))(*[_weights_struct(w) for w in layers])
+    arr = (BlockWeights * max(n, 1))(*[_weights_struct(w, dims) for w in layers])
     fl = (ctypes.c_uint8 * max(n, 1))(*[int(f) for f in flags])
     tv = (ctypes.c_float * len(t_video))(*[float(t) for t in t_video])
     ta = None if t_audio is None else (ctypes.c_float * len(t_audio))(*[float(t) for t in t_audio])
@@ -202,7 +225,7 @@ def long_video_sample(dims: Dims, layers: list, flags, t_video, t_audio, x_text,
         frames[T + c * (T - 1):T + (c + 1) * (T - 1)].copy_(noise)
     aud = torch.stack(list(audio)) if dims.n_audio > 0 else None
     n = len(layers)
-    arr = (BlockWeights * max(n, 1))(*[_weights_struct(w) for w in layers])
+    arr = (BlockWeights * max(n, 1))(*[_weights_struct(w, dims) for w in layers])
     fl = (ctypes.c_uint8 * max(n, 1))(*[int(f) for f in flags])
     tv = (ctypes.c_float * len(t_video))(*[float(t) for t in t_video])
     ta = None if t_audio is None else (ctypes.c_float * len(t_audio))(*[float(t) for t in t_audio])
