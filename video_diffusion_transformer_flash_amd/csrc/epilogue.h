@@ -226,29 +226,6 @@ template <> DIT_DEV void load8_stream<bf16_t>(const bf16_t* p, float v[8]) {
     }
 }
 
-// q or k (dst = p.q or p.k): rotary embedding with the row's (cos, sin) pairs
-// (32 contiguous bytes per lane), head-major row; rows [M, Mpad) zero
-template <typename T>
-DIT_DEV void epi8_qk(const EpiParams& p, void* dst, int head, int m, int d0, float v[8]) {
-    if (m >= p.Mpad) return;
-    if (m >= p.M) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = 0.f;
-    } else {
-        const float4* t = (const float4*)(p.rope.rows + (size_t)m * (p.dh >> 1) + (d0 >> 1));
-        const float4 c01 = t[0], c23 = t[1];
-        const float2 cs[4] = {make_float2(c01.x, c01.y), make_float2(c01.z, c01.w), make_float2(c23.x, c23.y),
-                              make_float2(c23.z, c23.w)};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float a = v[2 * j], b = v[2 * j + 1];
-            v[2 * j] = a * cs[j].x - b * cs[j].y;
-            v[2 * j + 1] = a * cs[j].y + b * cs[j].x;
-        }
-    }
-    store8<T>((T*)dst + ((size_t)head * p.Sp + m) * p.dh + d0, v);
-}
-
 template <typename T>
 DIT_DEV void epi8_resid(const EpiParams& p, int m, int n0, const float v[8]) {
     if (m >= p.M) return;
@@ -257,6 +234,29 @@ DIT_DEV void epi8_resid(const EpiParams& p, int m, int n0, const float v[8]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] += v[i];
     store8<float>(p.h + (size_t)m * p.D + n0, x);
+}
+
+// Source rows of N sequence rows m[i] (as seq_row) in two passes: every
+// index lookup (vidx / cidx, clamped into range so that each load is valid
+// whichever segment the row is in) is issued before any is used, so the
+// lookups of all N rows cost one memory latency instead of one each.
+template <typename T, int N>
+DIT_DEV void seq_rows(const SeqIn& s, const int (&m)[N], int D, const T* (&out)[N]) {
+    const int nt = s.nt, nv = s.nv, nc = s.nc;
+    int vi[N], ci[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        vi[i] = (s.vidx && nv > 0) ? s.vidx[min(max(m[i] - nt, 0), nv - 1)] : m[i] - nt;
+        ci[i] = (s.cidx && nc > 0) ? s.cidx[min(max(m[i] - nt - nv, 0), nc - 1)] : m[i] - nt - nv;
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int r = m[i];
+        out[i] = r < nt             ? (const T*)s.xt + (size_t)r * D
+                 : r < nt + nv      ? (const T*)s.xv + (size_t)vi[i] * D
+                 : r < nt + nv + nc ? (const T*)s.xc + (size_t)ci[i] * D
+                                    : (const T*)s.xa + (size_t)(r - nt - nv - nc) * D;
+    }
 }
 
 // u = silu(gate) * up for ffn features f0 .. f0 + 7; returns max |stored u|
@@ -345,6 +345,105 @@ DIT_DEV void epi8_down(const EpiParams& p, int m, int n0, const float v[8]) {
         store8<T>((T*)o.yc + (size_t)(m - nt - nv) * p.D + n0, y);
     } else {
         store8<T>((T*)o.ya + (size_t)(m - nt - nv - nc) * p.D + n0, y);
+    }
+}
+
+// The DOWN epilogue of one row in two parts, so that a round can issue the
+// loads of all its rows before its first store (stores may alias the
+// full-resolution rows, so the compiler keeps a later row's loads behind an
+// earlier row's stores): down_issue loads the residual row and, for a kept
+// video row with its update, the reference row and the full-resolution rows
+// of the slot's rectangle when it is at most 2 x 2; down_finish adds and
+// stores as epi8_down does (the same arithmetic, the same results). bf16 rows.
+// down_issue_h loads the residual row only, down_issue_rest the others.
+struct DownRow {
+    float h[8];
+    uint4 ref;
+    uint4 bx[4];
+};
+
+DIT_DEV void down_issue_h(const EpiParams& p, int m, int n0, DownRow& d) {
+    if (m < p.M) load8<float>(p.hres + (size_t)m * p.D + n0, d.h);
+}
+
+// the reference row and the rectangle's rows (after down_issue_h)
+DIT_DEV void down_issue_rest(const EpiParams& p, int m, int n0, DownRow& d) {
+    if (m >= p.M) return;
+    const int nt = p.xin.nt;
+    if (m < nt || m >= nt + p.xin.nv || !p.out.delta) return;
+    d.ref = *(const uint4*)(seq_row<bf16_t>(p.refin, m, p.D) + n0);
+    if (!p.out.bout) return;
+    const KeepGeom& g = p.kg;
+    const int j = m - nt, per = g.Hk * g.Wk;
+    const int t = j / per, r = j - t * per, a = r / g.Wk, b = r - a * g.Wk;
+    int h0, h1, w0, w1;
+    kept_preimage(a, g.H, g.s, g.Hk, h0, h1);
+    kept_preimage(b, g.W, g.s, g.Wk, w0, w1);
+    if (h1 - h0 > 1 || w1 - w0 > 1) return;
+    const bf16_t* x = (const bf16_t*)p.out.bx + n0;
+    const size_t base = (size_t)t * g.H * g.W;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int h = h0 + (q >> 1), w = w0 + (q & 1);
+        if (h <= h1 && w <= w1) d.bx[q] = ld_stream(x + (base + (size_t)h * g.W + w) * p.D);
+    }
+}
+
+DIT_DEV void down_finish(const EpiParams& p, int m, int n0, const float v[8], const DownRow& d) {
+    if (m >= p.M) return;
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = d.h[i] + v[i];
+    const SeqOut& o = p.out;
+    const int nt = p.xin.nt, nv = p.xin.nv, nc = p.xin.nc;
+    if (m < nt) {
+        store8<bf16_t>((bf16_t*)o.yt + (size_t)m * p.D + n0, y);
+    } else if (m < nt + nv) {
+        const int j = m - nt;
+        if (o.delta) {
+            const uint32_t rw[4] = {d.ref.x, d.ref.y, d.ref.z, d.ref.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                y[2 * i] -= __uint_as_float(rw[i] << 16);
+                y[2 * i + 1] -= __uint_as_float(rw[i] & 0xFFFF0000u);
+            }
+            if (!o.bout) {
+                store8<float>(o.delta + (size_t)j * p.D + n0, y);
+                return;
+            }
+            const KeepGeom& g = p.kg;
+            const int per = g.Hk * g.Wk;
+            const int t = j / per, r = j - t * per, a = r / g.Wk, b = r - a * g.Wk;
+            int h0, h1, w0, w1;
+            kept_preimage(a, g.H, g.s, g.Hk, h0, h1);
+            kept_preimage(b, g.W, g.s, g.Wk, w0, w1);
+            if (h1 - h0 > 1 || w1 - w0 > 1) {
+                bcast8<bf16_t>(p, j, n0, y);
+                return;
+            }
+            bf16_t* out = (bf16_t*)o.bout + n0;
+            const size_t base = (size_t)t * g.H * g.W;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int h = h0 + (q >> 1), w = w0 + (q & 1);
+                if (h <= h1 && w <= w1) {
+                    const uint32_t xw[4] = {d.bx[q].x, d.bx[q].y, d.bx[q].z, d.bx[q].w};
+                    float z[8];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        z[2 * i] = __uint_as_float(xw[i] << 16) + y[2 * i];
+                        z[2 * i + 1] = __uint_as_float(xw[i] & 0xFFFF0000u) + y[2 * i + 1];
+                    }
+                    store8<bf16_t>(out + (base + (size_t)h * g.W + w) * p.D, z);
+                }
+            }
+        } else {
+            store8<bf16_t>((bf16_t*)o.yv + (size_t)j * p.D + n0, y);
+        }
+    } else if (m < nt + nv + nc) {
+        store8<bf16_t>((bf16_t*)o.yc + (size_t)(m - nt - nv) * p.D + n0, y);
+    } else {
+        store8<bf16_t>((bf16_t*)o.ya + (size_t)(m - nt - nv - nc) * p.D + n0, y);
     }
 }
 

@@ -588,13 +588,43 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
     }
     const int fwave = f0 + wf * WF;       // first output (for SwiGLU: interleaved gate/up row) of the wave
     float mx = 0.f;
+    // RESID: every residual row the epilogue adds (16 bytes of bf16 per lane,
+    // row and round) is loaded here, before the first store. Vector memory
+    // loads and stores share one in-order counter, so a load issued after a
+    // store cannot be waited for without waiting for that store too. The
+    // loads are unconditional (rows past M read row M - 1) and the h stores
+    // go through a buffer descriptor that drops rows past M, so the rounds
+    // are straight-line code in which the compiler can count exactly which
+    // loads have landed; with a branch per row it waited for every earlier
+    // store before each row.
+    constexpr int NROUND = NBT * NH;   // rounds
+    uint4 xres[MODE == EPI_RESID ? NROUND : 1][4];
+    __amdgpu_buffer_rsrc_t rsH;
+    if constexpr (MODE == EPI_RESID) {
+        static_assert(std::is_same<TOUT, bf16_t>::value, "bf16 residual rows");
+        int mr[NROUND * 4];
+        const TOUT* rp[NROUND * 4];
+#pragma unroll
+        for (int k = 0; k < NROUND; ++k)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                mr[4 * k + i] = min(t0 + wt * WT + (k / NH) * 32 + (lane >> 3) + 8 * i, ep.M - 1);
+        seq_rows<TOUT>(ep.xin, mr, ep.D, rp);
+#pragma unroll
+        for (int k = 0; k < NROUND; ++k)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                xres[k][i] = *(const uint4*)(rp[4 * k + i] + fwave + 64 * (k % NH) + (lane & 7) * 8);
+        rsH = make_rsrc(ep.h + (size_t)t0 * ep.D, (min(ep.M, t0 + BT) - t0) * ep.D * 4);
+    }
     auto row8 = [&](int r, int c0, float v[8]) {
         const float4 x = *(const float4*)(wl + r * RS + c0 * 4), y = *(const float4*)(wl + r * RS + c0 * 4 + 16);
         v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w; v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
     };
-    static_for<NBT * NH>([&](auto ah) {
-        constexpr int a = decltype(ah)::value / NH, hb = 2 * (decltype(ah)::value % NH);   // token block, first feature block of the half
-        // accumulator layout -> LDS rows: lane (token lrow) holds outputs b 32 + 8 g + 4 h .. + 3
+    // accumulator layout -> LDS rows of round ah: lane (token lrow) holds
+    // outputs b 32 + 8 g + 4 h .. + 3
+    auto stage = [&](auto ah) {
+        constexpr int a = decltype(ah)::value / NH, hb = 2 * (decltype(ah)::value % NH);
         static_for<2>([&](auto b) {
             static_for<4>([&](auto g) {
                 *(float4*)(wl + lrow * RS + (b * 32 + 8 * g + 4 * lhalf) * 4) =
@@ -602,23 +632,72 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
                                 acc[a][hb + b][4 * g + 2] * scb[hb + b], acc[a][hb + b][4 * g + 3] * scb[hb + b]);
             });
         });
-        const int fw = fwave + 32 * hb;         // first output of the half
-        const int mb = t0 + wt * WT + a * 32;   // first token of the round
-        if constexpr (MODE == EPI_QKV) {
-            const int which = fw / ep.I;
-            const int rem = fw - which * ep.I;
-            const int head = rem / ep.dh;
-            const int dw = rem - head * ep.dh;  // head-local feature of output column 0
-            if (which < 2) {
+    };
+    if constexpr (MODE == EPI_QKV) {
+        // A wave's 64 outputs lie in one of q, k, v and one head (I and dh are
+        // multiples of 64), so the choice is made once per wave.
+        static_assert(NH == 1, "one 64-output half per wave");
+        static_assert(std::is_same<TOUT, bf16_t>::value, "bf16 q, k, v");
+        const int which = fwave / ep.I;
+        const int rem = fwave - which * ep.I;
+        const int head = rem / ep.dh;
+        const int dw = rem - head * ep.dh;   // head-local feature of output column 0
+        if (which < 2) {
+            // q, k: rotary embedding with the row's (cos, sin) pairs, head-major
+            // rows; rows [M, Mpad) zero. The rotary rows of round k + 1 (32
+            // bytes a lane and row; rows past M read row M - 1) are loaded
+            // before round k's stores, and the stores go through a descriptor
+            // bounded at Mpad rows: the rounds are straight-line code, so no
+            // load waits for an earlier store (loads and stores share one
+            // in-order counter).
+            const __amdgpu_buffer_rsrc_t rsQK =
+                make_rsrc((const TOUT*)(which ? ep.k : ep.q) + (size_t)head * ep.Sp * ep.dh, ep.Mpad * ep.dh * 2);
+            const int c0 = (lane & 7) * 8;
+            float4 rcs[2][4][2];
+            auto rope_load = [&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                if constexpr (k < NROUND) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int m = min(t0 + wt * WT + k * 32 + (lane >> 3) + 8 * i, ep.M - 1);
+                        const float4* t = (const float4*)(ep.rope.rows + (size_t)m * (ep.dh >> 1) + ((dw + c0) >> 1));
+                        rcs[k & 1][i][0] = t[0];
+                        rcs[k & 1][i][1] = t[1];
+                    }
+                }
+            };
+            rope_load(I0{});
+            static_for<NROUND>([&](auto ah) {
+                constexpr int k = decltype(ah)::value;
+                stage(ah);
+                rope_load(std::integral_constant<int, k + 1>{});
+                const int mb = t0 + wt * WT + k * 32;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = (lane >> 3) + 8 * i, c0 = (lane & 7) * 8;
+                    const int r = (lane >> 3) + 8 * i, m = mb + r;
                     float v[8];
                     row8(r, c0, v);
-                    epi8_qk<TOUT>(ep, which ? ep.k : ep.q, head, mb + r, dw + c0, v);
+                    const float4 c01 = rcs[k & 1][i][0], c23 = rcs[k & 1][i][1];
+                    const float2 cs[4] = {make_float2(c01.x, c01.y), make_float2(c01.z, c01.w),
+                                          make_float2(c23.x, c23.y), make_float2(c23.z, c23.w)};
+                    const bool live = m < ep.M;
+                    u32x4_t o;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float x = v[2 * j], y = v[2 * j + 1];
+                        // (x + i y)(c + i s), each part one product rounded, then a fused multiply-add
+                        const float re = __builtin_fmaf(x, cs[j].x, -(y * cs[j].y));
+                        const float im = __builtin_fmaf(x, cs[j].y, y * cs[j].x);
+                        o[j] = pack_bf2(live ? re : 0.f, live ? im : 0.f);
+                    }
+                    __builtin_amdgcn_raw_buffer_store_b128(o, rsQK, (m * ep.dh + dw + c0) * 2, 0, 0);
                 }
-            } else {
-                // v^T [head][dh][Sp]: lane = output column, eight consecutive tokens per store
+            });
+        } else {
+            // v^T [head][dh][Sp]: lane = output column, eight consecutive tokens per store
+            static_for<NROUND>([&](auto ah) {
+                stage(ah);
+                const int mb = t0 + wt * WT + decltype(ah)::value * 32;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int m0 = mb + 8 * i;
@@ -629,8 +708,15 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
                         store8<TOUT>((TOUT*)ep.vt + ((size_t)head * ep.dh + dw + lane) * ep.Sp + m0, v);
                     }
                 }
-            }
-        } else if constexpr (MODE == EPI_SWIGLU) {
+            });
+        }
+    }
+    if constexpr (MODE != EPI_QKV) static_for<NBT * NH>([&](auto ah) {
+        constexpr int a = decltype(ah)::value / NH, hb = 2 * (decltype(ah)::value % NH);   // token block, first feature block of the half
+        stage(ah);
+        const int fw = fwave + 32 * hb;         // first output of the half
+        const int mb = t0 + wt * WT + a * 32;   // first token of the round
+        if constexpr (MODE == EPI_SWIGLU) {
             // columns 0..31 gate, 32..63 up of ffn features fw / 2 .. + 31; four lanes per token
             using UT = TOUT;   // u in the activation dtype (bf16); fp8 quantises it from there
 #pragma unroll
@@ -641,15 +727,57 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
                 row8(r, 32 + j0, u);
                 mx = fmaxf(mx, epi8_swiglu<UT>(ep, mb + r, fw / 2 + j0, g, u));
             }
-        } else {
+        } else if constexpr (MODE == EPI_DOWN) {
+            // every load of the round's four rows before its first store; with
+            // fp8 (fewer free registers here) the residual rows of all four,
+            // then each row's reference and rectangle rows before its store
+            static_assert(std::is_same<TOUT, bf16_t>::value, "bf16 rows");
+            DownRow dr[4];
+            if (!pslot) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    down_issue_h(ep, mb + (lane >> 3) + 8 * i, fw + (lane & 7) * 8, dr[i]);
+                    if constexpr (!FP8) down_issue_rest(ep, mb + (lane >> 3) + 8 * i, fw + (lane & 7) * 8, dr[i]);
+                }
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = (lane >> 3) + 8 * i, c0 = (lane & 7) * 8;
                 float v[8];
                 row8(r, c0, v);
-                if (pslot) store8<float>(pslot + (size_t)(mb - t0 + r) * BF + (fw - f0 + c0), v);
-                else if constexpr (MODE == EPI_RESID) epi8_resid<TOUT>(ep, mb + r, fw + c0, v);
-                else epi8_down<TOUT>(ep, mb + r, fw + c0, v);
+                if (pslot) {
+                    store8<float>(pslot + (size_t)(mb - t0 + r) * BF + (fw - f0 + c0), v);
+                } else {
+                    if constexpr (FP8) down_issue_rest(ep, mb + r, fw + c0, dr[i]);
+                    down_finish(ep, mb + r, fw + c0, v, dr[i]);
+                }
+            }
+        } else if (pslot) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = (lane >> 3) + 8 * i, c0 = (lane & 7) * 8;
+                float v[8];
+                row8(r, c0, v);
+                store8<float>(pslot + (size_t)(mb - t0 + r) * BF + (fw - f0 + c0), v);
+            }
+        } else {
+            // h = X + acc (fp32), rows past M dropped by the descriptor's bound
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = (lane >> 3) + 8 * i, c0 = (lane & 7) * 8;
+                float v[8];
+                row8(r, c0, v);
+                const uint4 x = xres[decltype(ah)::value][i];
+                const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+                u32x4_t o[2];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    o[j >> 1][2 * (j & 1)] = __float_as_uint(__uint_as_float(xw[j] << 16) + v[2 * j]);
+                    o[j >> 1][2 * (j & 1) + 1] = __float_as_uint(__uint_as_float(xw[j] & 0xFFFF0000u) + v[2 * j + 1]);
+                }
+                const int off = ((mb - t0 + r) * ep.D + fw + c0) * 4;
+                __builtin_amdgcn_raw_buffer_store_b128(o[0], rsH, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(o[1], rsH, off + 16, 0, 0);
             }
         }
     });
