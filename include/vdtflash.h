@@ -65,8 +65,10 @@ typedef enum {
  * (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
  * Constraints: d_model % 64 == 0; d_ffn % 64 == 0; head_dim in {64, 128};
  * rope_t + rope_h + rope_w == head_dim, each even; T, H, W >= 1;
- * n_text, n_audio >= 0; stride >= 1. The bf16 / fp8 paths also need
- * d_model, n_heads * head_dim and d_ffn multiples of 128. */
+ * n_text, n_audio >= 0; stride >= 1; at most 2^30 tokens in the joint
+ * sequence. The bf16 / fp8 paths also need d_model, n_heads * head_dim and
+ * d_ffn multiples of 128, head_dim 128 and at most 2^23 tokens (their kernels
+ * address one head's rows with 32-bit byte offsets), else DIT_EUNSUPPORTED. */
 typedef struct {
     int32_t T, H, W;              /* latent video grid */
     int32_t n_text, n_audio;      /* text / audio tokens (never compressed) */

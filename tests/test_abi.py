@@ -60,10 +60,22 @@ def _dims(**kw):
     (dict(ctrl_offset=-2), _lib.DIT_EINVAL),
     (dict(n_fixed=-1), _lib.DIT_EINVAL),
     (dict(n_fixed=7), _lib.DIT_EINVAL),                          # more fixed frames than T = 6
+    (dict(T=8, H=1024, W=1025), _lib.DIT_EUNSUPPORTED),         # past 2^23 tokens on the MFMA path
+    (dict(T=1024, H=1024, W=1025), _lib.DIT_EINVAL),            # past 2^30 tokens
 ])
 def test_dims_rejected(bad, code):
     n = ctypes.c_size_t()
     assert V.lib().dit_block_workspace_size(ctypes.byref(_dims(**bad)), 1, ctypes.byref(n)) == code
+
+
+def test_token_bound_is_the_mfma_paths_only():
+    """2^23 + tokens: refused on the bf16 path, accepted by the f32 path."""
+    n = ctypes.c_size_t()
+    big = dict(T=8, H=1024, W=1025)
+    assert V.lib().dit_block_workspace_size(ctypes.byref(_dims(**big)), 0, ctypes.byref(n)) == _lib.DIT_EUNSUPPORTED
+    f32 = _dims(act_dtype=_lib.DIT_F32, w_dtype=_lib.DIT_F32, **big)
+    assert V.lib().dit_block_workspace_size(ctypes.byref(f32), 0, ctypes.byref(n)) == _lib.DIT_OK
+    assert n.value > 0
 
 
 def test_block_forward_rejects_before_launch():

@@ -93,6 +93,10 @@ int validate_dims(const dit_dims* d) {
         if (d->head_dim != 128) return DIT_EUNSUPPORTED;
         if (d->d_model % 128 || I % 128 || d->d_ffn % 128) return DIT_EUNSUPPORTED;
         if (d->rope_t % 8 || d->rope_h % 8 || d->rope_w % 8) return DIT_EUNSUPPORTED;
+        // the MFMA epilogues address a head's q / k rows and a tile's rows
+        // through buffer descriptors with 32-bit byte offsets (a head holds
+        // S x 256 bytes); 2^23 tokens is far past what one GPU's memory holds
+        if (S > (1LL << 23)) return DIT_EUNSUPPORTED;
     }
     return DIT_OK;
 }
