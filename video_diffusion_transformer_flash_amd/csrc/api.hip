@@ -142,7 +142,7 @@ Plan make_plan(const dit_dims& d, int nv_seq, bool delta, int nc) {
     // that grows with S, so a workspace sized for more tokens always suffices)
     p.part_bytes = d.act_dtype == DIT_F32 ? 0 : gemm_split_bytes_bound(p.S, (int)D);
     p.part = p.part_bytes ? take(p.part_bytes) : 0;
-    p.sc = take(16 * sizeof(float));
+    p.sc = take(32 * sizeof(float));   // amax values [0..3], the down projection's sink [16..19]
     p.total = off;
     return p;
 }
@@ -195,7 +195,7 @@ int run_block(const dit_dims& d, const dit_block_weights& w, const SeqIn& in, co
     float* h = (float*)(ws + P.h);
     void* u = ws + P.u;
     uint8_t* u8 = fp8 ? ws + P.u8 : nullptr;
-    float* sc = (float*)(ws + P.sc);   // [0] n1 amax, [1] o amax, [2] n2 amax, [3] u amax
+    float* sc = (float*)(ws + P.sc);   // [0] n1 amax, [1] o amax, [2] n2 amax, [3] u amax; [16..19] the sink
 
     EpiParams ep{};
     ep.M = S; ep.Mpad = Sp; ep.D = D; ep.I = I; ep.F = F; ep.dh = dh;
@@ -211,6 +211,7 @@ int run_block(const dit_dims& d, const dit_block_weights& w, const SeqIn& in, co
     ep.kg = KeepGeom{d.H, d.W, keep_count(d.H, d.stride), keep_count(d.W, d.stride), d.stride};
     ep.part = P.part_bytes ? (float*)(ws + P.part) : nullptr;
     ep.part_bytes = P.part_bytes;
+    ep.sink = sc + 16;
 
     // 1-2. RMSNorm1 + QKV (+ rotary)
     if (fp8) {

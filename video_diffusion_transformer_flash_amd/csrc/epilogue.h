@@ -51,6 +51,9 @@ struct EpiParams {
     SeqOut out;
     SeqIn refin;            // reference rows for delta (video segment only)
     KeepGeom kg;            // the compression's grid (broadcast into out.bout)
+    // DOWN: 16 writable bytes that nothing reads; the rows past M store
+    // there, so the output stores need no branch (nullptr: they branch)
+    void* sink;
     // RESID / DOWN: fp32 partial tiles of K-split tail tiles (nullptr or too
     // small: no split)
     float* part;

@@ -711,7 +711,58 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
             });
         }
     }
-    if constexpr (MODE != EPI_QKV) static_for<NBT * NH>([&](auto ah) {
+    // DOWN without update rows (every row y = h + acc into its segment's
+    // output): the residual rows of round k + 1 (32 bytes of fp32 per lane
+    // and row; rows past M read row M - 1) are loaded before round k's
+    // stores, and the stores need no branch (rows past M write the sink), so
+    // no load waits for an earlier store (one in-order counter for both). A
+    // loop of its own, so that its registers and the update path's are not
+    // live together.
+    bool done = false;
+    if constexpr (MODE == EPI_DOWN) {
+        static_assert(NH == 1, "one 64-output half per wave");
+        static_assert(std::is_same<TOUT, bf16_t>::value, "bf16 rows");
+        if (!ep.out.delta && ep.sink && !pslot) {
+            done = true;
+            const int c0 = (lane & 7) * 8;
+            float hpf[2][4][8];
+            auto hload = [&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                if constexpr (k < NROUND) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int m = min(t0 + wt * WT + k * 32 + (lane >> 3) + 8 * i, ep.M - 1);
+                        load8<float>(ep.hres + (size_t)m * ep.D + fwave + c0, hpf[k & 1][i]);
+                    }
+                }
+            };
+            hload(I0{});
+            const SeqOut& o = ep.out;
+            const int nt = ep.xin.nt, nv = ep.xin.nv, nc = ep.xin.nc;
+            static_for<NROUND>([&](auto ah) {
+                constexpr int k = decltype(ah)::value;
+                stage(ah);
+                hload(std::integral_constant<int, k + 1>{});
+                const int mb = t0 + wt * WT + k * 32;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = (lane >> 3) + 8 * i, m = mb + r;
+                    float v[8];
+                    row8(r, c0, v);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) v[j] = hpf[k & 1][i][j] + v[j];
+                    const int n0 = fwave + c0;
+                    TOUT* dst = m >= ep.M          ? (TOUT*)ep.sink
+                                : m < nt           ? (TOUT*)o.yt + (size_t)m * ep.D + n0
+                                : m < nt + nv      ? (TOUT*)o.yv + (size_t)(m - nt) * ep.D + n0
+                                : m < nt + nv + nc ? (TOUT*)o.yc + (size_t)(m - nt - nv) * ep.D + n0
+                                                   : (TOUT*)o.ya + (size_t)(m - nt - nv - nc) * ep.D + n0;
+                    store8<TOUT>(dst, v);
+                }
+            });
+        }
+    }
+    if constexpr (MODE != EPI_QKV) if (!done) static_for<NBT * NH>([&](auto ah) {
         constexpr int a = decltype(ah)::value / NH, hb = 2 * (decltype(ah)::value % NH);   // token block, first feature block of the half
         stage(ah);
         const int fw = fwave + 32 * hb;         // first output of the half
