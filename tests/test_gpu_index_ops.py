@@ -44,10 +44,17 @@ def test_index_maps_random_grids():
         _idx(2, H, W, 2)
 
 
+# (T, H, W, D): one 16-byte chunk per row on a single position; fewer chunks
+# than threads; the 540p compressed block's rows (several chunks per thread);
+# the 768p grid at 8 frames (more chunks than one pass of the grid covers)
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_gather_kept_bit_exact(dtype):
-    T, H, W, D = 3, 34, 60, 384
-    x = np.random.default_rng(1).standard_normal((T, H, W, D)).astype(np.float32)
+@pytest.mark.parametrize("shape", [(1, 1, 1, 8), (3, 34, 60, 384), (6, 34, 60, 5376), (8, 48, 80, 5376)])
+def test_gather_kept_bit_exact(dtype, shape):
+    T, H, W, D = shape
+    if dtype == "f32" and D == 8:
+        D = 4
+    print(f"gather {dtype} T={T} H={H} W={W} D={D}", flush=True)
+    x = np.random.default_rng(1).standard_normal((T, H, W, D), dtype=np.float32)
     if dtype == "bf16":
         x = round_bf16(x)
     tx = torch.from_numpy(x).cuda()
