@@ -11,14 +11,20 @@ the timed region. The same block with compression off (all 12628 tokens) is
 timed as a second line item.
 
 The bandwidth-bound kernels (gather of the kept rows, nearest-kept broadcast
-plus residual) are also timed alone on the same shapes with the 256 MB
-Infinity Cache and the L2s flushed before every repetition, which is the number
-their HBM roofline fraction is quoted on. The flush reads a 1 GiB buffer: a
-write flush would leave up to ~290 MB of dirty lines whose write-back to HBM
-would then be charged to the kernel under test.
+plus residual, the first RMSNorm) are also timed alone on the same shapes:
+back-to-back launches that rotate over disjoint buffer sets several times the
+256 MB Infinity Cache (so no launch finds its data cached; the number their
+HBM roofline fraction is quoted on), and each once more after a 1 GiB read
+that flushes the caches (a write flush would leave up to ~290 MB of dirty
+lines whose write-back to HBM would then be charged to the kernel under test).
+
+Warm-up: after a short warm-up the first few timed steps run 3-14 % slower
+than the rest (measured: 3.19, 3.09, 2.92 ... ms, then 2.80 ms per step after
+3 warm-up steps; every step at 2.78-2.84 ms after 10), so 10 untimed steps
+come first by default.
 
 Prints one JSON line (see the repository's bench contract).
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu] [--no-off] [--copy-calib]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 10] [--no-cpu] [--no-off] [--copy-calib]
 
 --copy-calib adds three plain 1 GiB elementwise copies after the timed region:
 the reference dispatches that scale rocprofv3's FETCH_SIZE / WRITE_SIZE
@@ -567,7 +573,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)   # the first ~5 steps after a short warm-up run 3-14 % slow
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-off", action="store_true", help="skip the compression-off line item")
     ap.add_argument("--copy-calib", action="store_true", help="add 1 GiB reference copies (counter calibration)")
