@@ -39,6 +39,7 @@ namespace detail {
 
 typedef __attribute__((address_space(3))) uint8_t* LDSPTR;
 
+
 // Row r of a tile with RB-byte rows: a 256-byte bank window holds G = 256 / RB
 // rows, so 16 consecutive rows at one logical chunk must spread over the
 // CPR = RB / 16 chunk slots of each of the G row residues: physical chunk =
@@ -49,11 +50,21 @@ DIT_DEV int swz(int row, int chunk) {
     return chunk ^ ((row / G) & (CPR - 1));
 }
 
+// Token tiles per weight-tile group (tile_origin). With 32 workgroups in
+// flight per XCD, 16 token tiles per weight tile make the token rows the
+// operand that misses the XCD's L2 (each token K slice fetched for every pair
+// of weight tiles); the bf16 projections, held by the power limit, are
+// fastest so (smaller groups were slower uncompressed). The fp8 projections
+// run at a higher clock and wait on their fills; with 4 token tiles per weight
+// tile the misses move towards the weight rows, which have the deeper
+// pipeline (same box: fp8 stack 540.7 -> 533.3 ms; 1, 2 and 8: 548.5, 537.3,
+// 534.8).
+constexpr int tile_group(bool fp8) { return fp8 ? 4 : 16; }
+
 // First token and first output feature of tile `tile`: GM consecutive token
 // tiles share one weight tile, so neighbouring tiles on an XCD reuse it in L2.
-template <int BT, int BF>
+template <int BT, int BF, int GM>
 DIT_DEV void tile_origin(int tile, int M, int N, int& t0, int& f0) {
-    constexpr int GM = 16;
     const int ntt = (M + BT - 1) / BT;
     const int ntf = N / BF;
     const int group = tile / (GM * ntf);
@@ -137,7 +148,7 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
         pslot = ep.part + (size_t)(r * splits + slice) * BT * BF;
     }
     int t0, f0;
-    tile_origin<BT, BF>(tile, M, N, t0, f0);
+    tile_origin<BT, BF, tile_group(FP8)>(tile, M, N, t0, f0);
 
     const int rowbytes = K * ESZ;
     const int lrow = lane & 31, lhalf = lane >> 5;
@@ -855,7 +866,7 @@ __global__ __launch_bounds__(64 * WGT * WGF, OCC) void gemm_mfma_kernel(const ui
 // K-split tail, second pass: one thread per 8 consecutive outputs of a tail
 // tile row; the slices are added in slice order, then the RESID / DOWN
 // epilogue runs on the sum.
-template <int MODE, int BT, int BF>
+template <int MODE, int BT, int BF, bool FP8>
 __global__ __launch_bounds__(256) void split_reduce_kernel(int M, int N, int nfull, int splits, EpiParams ep) {
     constexpr int TPR = BF / 8, RPB = 256 / TPR;   // threads per row, rows per block
     static_assert(BT % RPB == 0, "rows");
@@ -863,7 +874,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(int M, int N, int nfu
     const int row = (blockIdx.x % (BT / RPB)) * RPB + threadIdx.x / TPR;
     const int c0 = (threadIdx.x % TPR) * 8;
     int t0, f0;
-    tile_origin<BT, BF>(nfull + r, M, N, t0, f0);
+    tile_origin<BT, BF, tile_group(FP8)>(nfull + r, M, N, t0, f0);
     if (t0 + row >= M) return;
     const float* p = ep.part + ((size_t)r * splits * BT + row) * BF + c0;
     float v[8], x[8];
@@ -932,7 +943,7 @@ hipError_t launch_t(const void* A, const void* W0, const void* W1, int M, int N,
         if (sp.splits > 1) {
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            hipLaunchKernelGGL((split_reduce_kernel<MODE, BT, BF>), dim3((tiles - nfull) * (BT / (256 / (BF / 8)))),
+            hipLaunchKernelGGL((split_reduce_kernel<MODE, BT, BF, FP8>), dim3((tiles - nfull) * (BT / (256 / (BF / 8)))),
                                dim3(256), 0, st, M, N, nfull, sp.splits, ep);
         }
     }
